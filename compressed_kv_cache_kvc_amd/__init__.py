@@ -1,0 +1,254 @@
+"""Compressed KV cache for autoregressive video on MI355X (gfx950).
+
+Thin Python binding of the kvc C ABI (include/kvc.h): it checks tensor shapes,
+dtypes and devices, allocates the outputs and the workspace through PyTorch and
+passes raw device pointers plus the current HIP stream.  Every step of the
+computation runs in the HIP kernels of libkvc.so; nothing here computes.
+
+Entry points (names follow the C ABI):
+  fit_assign(x, centroids, n_iter)          -> ids            (centroids fitted in place)
+  encode(x, centroids, bits, group, ...)    -> (codes, meta, ids)
+  attend(q, segments)                       -> (out, lse)
+  attend_lowdim(q, basis_k, basis_v, segs)  -> (out, lse)
+  lse_merge(outs, lses)                     -> (out, lse)
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import KvcSegment
+
+__all__ = ["KvcError", "Segment", "fit_assign", "encode", "attend", "attend_lowdim", "lse_merge",
+           "library", "version"]
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{_status_name(status)}: {message}")
+
+
+def library():
+    return _lib.load()
+
+
+def version() -> str:
+    return library().kvc_version().decode()
+
+
+def _status_name(status: int) -> str:
+    return library().kvc_status_string(status).decode()
+
+
+def _check(status: int):
+    if status != _lib.KVC_OK:
+        raise KvcError(status, library().kvc_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.KVC_BF16
+    if t.dtype == torch.float32:
+        return _lib.KVC_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use bfloat16 or float32")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, device=None, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------------------ fit / assign
+def fit_assign(x: torch.Tensor, centroids: torch.Tensor, n_iter: int = 2,
+               ids_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Lloyd k-means per head; ``centroids`` [H, C, d] is updated in place with the
+    fitted centres; returns the final ids [H, N] (uint8)."""
+    _need(x, "x")
+    H, N, d = x.shape
+    _need(centroids, "centroids", x.device, x.dtype)
+    C = centroids.shape[1]
+    if tuple(centroids.shape) != (H, C, d):
+        raise ValueError("centroids must be [H, C, d]")
+    ids = ids_out if ids_out is not None else torch.empty(H, N, dtype=torch.uint8, device=x.device)
+    _need(ids, "ids_out", x.device, torch.uint8, (H, N))
+    lib = library()
+    wsb = lib.kvc_fit_assign_workspace_bytes(H, N, d, C)
+    ws = _workspace(wsb, x.device)
+    _check(lib.kvc_fit_assign(H, N, d, _dtype_code(x), _ptr(x), C, _ptr(centroids), n_iter, _ptr(ids),
+                              _ptr(ws), wsb, _stream(x.device)))
+    return ids
+
+
+# ------------------------------------------------------------------------------ encode
+def encode(x: torch.Tensor, centroids: torch.Tensor, bits: int, group: int,
+           ids: Optional[torch.Tensor] = None, basis: Optional[torch.Tensor] = None,
+           codes_out: Optional[torch.Tensor] = None, meta_out: Optional[torch.Tensor] = None):
+    """Encode [H, N, d] tokens against [H, C, d] centres.  Returns (codes uint8
+    [H, N, code_dim*bits/8], meta uint16 [H, N, code_dim/group, 2] (fp16 bits of
+    scale, zero), ids uint8 [H, N]).  Without ``ids`` the assignment runs first."""
+    _need(x, "x")
+    H, N, d = x.shape
+    _need(centroids, "centroids", x.device, x.dtype)
+    C = centroids.shape[1]
+    if tuple(centroids.shape) != (H, C, d):
+        raise ValueError("centroids must be [H, C, d]")
+    rank = 0
+    if basis is not None:
+        _need(basis, "basis", x.device, torch.float32)
+        if basis.shape[0] != H or basis.shape[1] != d:
+            raise ValueError("basis must be [H, d, rank]")
+        rank = basis.shape[2]
+    code_dim = rank or d
+    codes = codes_out if codes_out is not None else torch.empty(
+        H, N, code_dim * bits // 8, dtype=torch.uint8, device=x.device)
+    meta = meta_out if meta_out is not None else torch.empty(
+        H, N, code_dim // group, 2, dtype=torch.uint16, device=x.device)
+    _need(codes, "codes_out", x.device, torch.uint8, (H, N, code_dim * bits // 8))
+    _need(meta, "meta_out", x.device, torch.uint16, (H, N, code_dim // group, 2))
+    lib = library()
+    if ids is None:
+        ids_out = torch.empty(H, N, dtype=torch.uint8, device=x.device)
+        wsb = lib.kvc_encode_workspace_bytes(H, N, d, C, 0)
+        ws = _workspace(wsb, x.device)
+        _check(lib.kvc_encode(H, N, d, _dtype_code(x), _ptr(x), C, _ptr(centroids), None, _ptr(ids_out),
+                              _ptr(basis), rank, bits, group, _ptr(codes), _ptr(meta), _ptr(ws), wsb,
+                              _stream(x.device)))
+        return codes, meta, ids_out
+    _need(ids, "ids", x.device, torch.uint8, (H, N))
+    _check(lib.kvc_encode(H, N, d, _dtype_code(x), _ptr(x), C, _ptr(centroids), _ptr(ids), None,
+                          _ptr(basis), rank, bits, group, _ptr(codes), _ptr(meta), None, 0,
+                          _stream(x.device)))
+    return codes, meta, ids
+
+
+# ------------------------------------------------------------------------------ segments
+@dataclass
+class Segment:
+    """One run of encoded history (all heads) with its own centre tables."""
+    k_codes: torch.Tensor     # [H, n, code_dim*k_bits/8] uint8
+    k_meta: torch.Tensor      # [H, n, code_dim/group, 2] uint16
+    k_ids: torch.Tensor       # [H, n] uint8
+    k_cent: torch.Tensor      # [H, C, d]
+    v_codes: torch.Tensor
+    v_meta: torch.Tensor
+    v_ids: torch.Tensor
+    v_cent: torch.Tensor
+    k_bits: int
+    v_bits: int
+    group: int
+    rank: int = 0
+
+    @property
+    def n_tokens(self) -> int:
+        return int(self.k_ids.shape[1])
+
+    def to_c(self) -> KvcSegment:
+        s = KvcSegment()
+        s.n_tokens = self.n_tokens
+        s.n_centroids = int(self.k_cent.shape[1])
+        if int(self.v_cent.shape[1]) != s.n_centroids:
+            raise ValueError("K and V centre tables of a segment must have the same number of centres")
+        s.rank = self.rank
+        s.k_bits, s.v_bits, s.group = self.k_bits, self.v_bits, self.group
+        s.cent_dtype = _dtype_code(self.k_cent)
+        for name in ("k_codes", "v_codes", "k_meta", "v_meta", "k_ids", "v_ids", "k_cent", "v_cent"):
+            t = getattr(self, name)
+            _need(t, name)
+            setattr(s, name, t.data_ptr())
+        return s
+
+
+def _seg_array(segments: Sequence[Segment]):
+    arr = (KvcSegment * max(1, len(segments)))()
+    for i, s in enumerate(segments):
+        arr[i] = s.to_c()
+    return arr
+
+
+# ------------------------------------------------------------------------------ attention
+def attend(q: torch.Tensor, segments: Sequence[Segment], out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None):
+    """Attention of q [H, n_q, d] over the concatenated segments.  Returns
+    (out fp32 [H, n_q, d], lse fp32 [H, n_q])."""
+    _need(q, "q")
+    H, n_q, d = q.shape
+    out = out if out is not None else torch.empty(H, n_q, d, dtype=torch.float32, device=q.device)
+    lse = lse if lse is not None else torch.empty(H, n_q, dtype=torch.float32, device=q.device)
+    _need(out, "out", q.device, torch.float32, (H, n_q, d))
+    _need(lse, "lse", q.device, torch.float32, (H, n_q))
+    arr = _seg_array(segments)
+    lib = library()
+    wsb = lib.kvc_attend_workspace_bytes(H, n_q, d, _dtype_code(q), arr, len(segments))
+    ws = _workspace(wsb, q.device)
+    _check(lib.kvc_attend(H, n_q, d, _dtype_code(q), _ptr(q), arr, len(segments), _ptr(out), _ptr(lse),
+                          _ptr(ws), wsb, _stream(q.device)))
+    return out, lse
+
+
+def attend_lowdim(q: torch.Tensor, basis_k: torch.Tensor, basis_v: torch.Tensor, segments: Sequence[Segment],
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Low-dimensional attention over coefficient-coded segments; returns
+    (out fp32 [H, n_q, d], lse fp32 [H, n_q])."""
+    _need(q, "q")
+    H, n_q, d = q.shape
+    _need(basis_k, "basis_k", q.device, torch.float32)
+    _need(basis_v, "basis_v", q.device, torch.float32, tuple(basis_k.shape))
+    rank = basis_k.shape[2]
+    out = out if out is not None else torch.empty(H, n_q, d, dtype=torch.float32, device=q.device)
+    lse = lse if lse is not None else torch.empty(H, n_q, dtype=torch.float32, device=q.device)
+    _need(out, "out", q.device, torch.float32, (H, n_q, d))
+    _need(lse, "lse", q.device, torch.float32, (H, n_q))
+    arr = _seg_array(segments)
+    lib = library()
+    wsb = lib.kvc_attend_lowdim_workspace_bytes(H, n_q, d, rank, arr, len(segments))
+    ws = _workspace(wsb, q.device)
+    _check(lib.kvc_attend_lowdim(H, n_q, d, _dtype_code(q), _ptr(q), _ptr(basis_k), _ptr(basis_v), rank, arr,
+                                 len(segments), _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream(q.device)))
+    return out, lse
+
+
+def lse_merge(outs: Sequence[torch.Tensor], lses: Sequence[torch.Tensor], out: Optional[torch.Tensor] = None,
+              lse: Optional[torch.Tensor] = None):
+    """Merge attention parts of the same queries by log-sum-exp."""
+    if len(outs) != len(lses) or not outs:
+        raise ValueError("need the same positive number of outputs and LSEs")
+    H, n_q, d = outs[0].shape
+    for i, (o, l) in enumerate(zip(outs, lses)):
+        _need(o, f"outs[{i}]", outs[0].device, torch.float32, (H, n_q, d))
+        _need(l, f"lses[{i}]", outs[0].device, torch.float32, (H, n_q))
+    dev = outs[0].device
+    out = out if out is not None else torch.empty(H, n_q, d, dtype=torch.float32, device=dev)
+    lse = lse if lse is not None else torch.empty(H, n_q, dtype=torch.float32, device=dev)
+    po = (ctypes.c_void_p * len(outs))(*[o.data_ptr() for o in outs])
+    pl = (ctypes.c_void_p * len(lses))(*[l.data_ptr() for l in lses])
+    _check(library().kvc_lse_merge(H, n_q, d, len(outs), po, pl, _ptr(out), _ptr(lse), _stream(dev)))
+    return out, lse

@@ -1,0 +1,433 @@
+// C ABI: argument validation, workspace planning and kernel dispatch.
+// Every check runs before any launch; no C++ exception leaves this file.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kvc_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvc_status fail(kvc_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+kvc_status ok() {
+  g_last_error.clear();
+  return KVC_OK;
+}
+
+kvc_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(KVC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define KVC_REQUIRE(cond, st, ...) \
+  do {                             \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+#define KVC_PTR(p, needed, name)                                                        \
+  do {                                                                                  \
+    if (needed) {                                                                       \
+      if ((p) == nullptr) return fail(KVC_ERR_INVALID_ARG, "%s is NULL", name);         \
+      if (!aligned16(p)) return fail(KVC_ERR_INVALID_ARG, "%s is not 16-byte aligned", name); \
+    }                                                                                   \
+  } while (0)
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+bool valid_dtype(kvc_dtype d) { return d == KVC_F32 || d == KVC_BF16; }
+size_t dtype_size(kvc_dtype d) { return d == KVC_F32 ? 4 : 2; }
+
+int64_t tiles_of(int64_t n) { return (n + kvc::kAttendTile - 1) / kvc::kAttendTile; }
+
+// Validate a segment list for attention; fills the device list.
+kvc_status check_segments(int32_t heads, int32_t dim, const kvc_segment* segs, int32_t n_segs,
+                          int32_t want_rank, kvc::SegList* out, int* kb, int* vb, int* g,
+                          kvc_dtype* cdt) {
+  KVC_REQUIRE(n_segs >= 0, KVC_ERR_INVALID_ARG, "n_segs < 0");
+  KVC_REQUIRE(n_segs == 0 || segs != nullptr, KVC_ERR_INVALID_ARG, "segs is NULL");
+  KVC_REQUIRE(n_segs <= kvc::kMaxSegs, KVC_ERR_UNSUPPORTED, "at most %d segments per call", kvc::kMaxSegs);
+  out->n = 0;
+  out->total_tiles = 0;
+  *kb = *vb = *g = 0;
+  *cdt = KVC_BF16;
+  bool first = true;
+  for (int i = 0; i < n_segs; ++i) {
+    const kvc_segment& s = segs[i];
+    KVC_REQUIRE(s.n_tokens >= 0, KVC_ERR_INVALID_ARG, "segment %d: n_tokens < 0", i);
+    KVC_REQUIRE(s.rank == want_rank, KVC_ERR_INVALID_ARG, "segment %d: rank %d, expected %d", i, s.rank,
+                want_rank);
+    const int code_dim = want_rank ? want_rank : dim;
+    KVC_REQUIRE(s.k_bits == 2 || s.k_bits == 4, KVC_ERR_INVALID_ARG, "segment %d: k_bits must be 2 or 4", i);
+    KVC_REQUIRE(s.v_bits == 2 || s.v_bits == 4, KVC_ERR_INVALID_ARG, "segment %d: v_bits must be 2 or 4", i);
+    KVC_REQUIRE(s.group > 0 && code_dim % s.group == 0, KVC_ERR_INVALID_ARG,
+                "segment %d: group %d does not divide %d", i, s.group, code_dim);
+    KVC_REQUIRE(s.n_centroids >= 1 && s.n_centroids <= 256, KVC_ERR_INVALID_ARG,
+                "segment %d: n_centroids must be in [1, 256]", i);
+    KVC_REQUIRE(valid_dtype(s.cent_dtype), KVC_ERR_INVALID_ARG, "segment %d: bad centre dtype", i);
+    if (s.n_tokens == 0) continue;
+    if (first) {
+      *kb = s.k_bits; *vb = s.v_bits; *g = s.group; *cdt = s.cent_dtype;
+      first = false;
+    } else {
+      KVC_REQUIRE(s.k_bits == *kb && s.v_bits == *vb && s.group == *g && s.cent_dtype == *cdt,
+                  KVC_ERR_UNSUPPORTED, "segment %d: all segments of a call must share bits, group and centre dtype", i);
+    }
+    KVC_PTR(s.k_codes, true, "segment k_codes");
+    KVC_PTR(s.v_codes, true, "segment v_codes");
+    KVC_PTR(s.k_meta, true, "segment k_meta");
+    KVC_PTR(s.v_meta, true, "segment v_meta");
+    KVC_PTR(s.k_ids, true, "segment k_ids");
+    KVC_PTR(s.v_ids, true, "segment v_ids");
+    KVC_PTR(s.k_cent, true, "segment k_cent");
+    KVC_PTR(s.v_cent, true, "segment v_cent");
+    kvc::SegDev& d = out->s[out->n++];
+    d.n_tokens = s.n_tokens;
+    d.tile_begin = out->total_tiles;
+    d.n_centroids = s.n_centroids;
+    d.k_codes = s.k_codes;
+    d.v_codes = s.v_codes;
+    d.k_meta = reinterpret_cast<const uint32_t*>(s.k_meta);
+    d.v_meta = reinterpret_cast<const uint32_t*>(s.v_meta);
+    d.k_ids = s.k_ids;
+    d.v_ids = s.v_ids;
+    d.k_cent = s.k_cent;
+    d.v_cent = s.v_cent;
+    d.k_cent_proj = nullptr;
+    d.v_cent_proj = nullptr;
+    out->total_tiles += tiles_of(s.n_tokens);
+  }
+  (void)heads;
+  return ok();
+}
+
+int64_t total_tokens(const kvc_segment* segs, int32_t n_segs) {
+  int64_t t = 0;
+  if (segs == nullptr) return 0;
+  for (int i = 0; i < n_segs; ++i) t += segs[i].n_tokens > 0 ? segs[i].n_tokens : 0;
+  return t;
+}
+
+int64_t total_tiles_of(const kvc_segment* segs, int32_t n_segs) {
+  int64_t t = 0;
+  if (segs == nullptr) return 0;
+  for (int i = 0; i < n_segs; ++i) t += segs[i].n_tokens > 0 ? tiles_of(segs[i].n_tokens) : 0;
+  return t;
+}
+
+size_t split_bytes(int32_t heads, int64_t n_q, int32_t dim, int n_split) {
+  if (n_split <= 1) return 0;
+  const size_t rows = size_t(heads) * size_t(n_q);
+  return align_up(size_t(n_split) * rows * dim * 4) + align_up(size_t(n_split) * rows * 4);
+}
+
+}  // namespace
+
+namespace kvc {
+
+// Split of the history across workgroups: enough workgroups to cover the chip
+// (256 compute units) about twice, each split keeping at least 16 tiles.
+int attend_split_plan(int heads, int64_t n_q, int64_t total_tiles, int rows_per_block) {
+  if (total_tiles <= 0 || n_q <= 0 || heads <= 0) return 1;
+  const int64_t blocks = int64_t(heads) * ((n_q + rows_per_block - 1) / rows_per_block);
+  const int64_t target = 2 * 256;
+  int s = 1;
+  while (s < 8 && blocks * s < target && total_tiles / (s + 1) >= 16) ++s;
+  return s;
+}
+
+}  // namespace kvc
+
+extern "C" {
+
+const char* kvc_status_string(kvc_status status) {
+  switch (status) {
+    case KVC_OK: return "KVC_OK";
+    case KVC_ERR_INVALID_ARG: return "KVC_ERR_INVALID_ARG";
+    case KVC_ERR_UNSUPPORTED: return "KVC_ERR_UNSUPPORTED";
+    case KVC_ERR_WORKSPACE: return "KVC_ERR_WORKSPACE";
+    case KVC_ERR_HIP: return "KVC_ERR_HIP";
+  }
+  return "unknown kvc_status";
+}
+
+const char* kvc_last_error(void) { return g_last_error.c_str(); }
+
+const char* kvc_version(void) { return "kvc 0.1.0 (gfx950)"; }
+
+// ------------------------------------------------------------------------------ fit / assign
+size_t kvc_fit_assign_workspace_bytes(int32_t heads, int64_t n_tokens, int32_t dim, int32_t n_centroids) {
+  (void)n_tokens; (void)dim;
+  if (heads <= 0 || n_centroids <= 0) return 0;
+  return align_up(size_t(heads) * size_t(n_centroids) * 4);  // centre norms
+}
+
+kvc_status kvc_fit_assign(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt, const void* x,
+                          int32_t n_centroids, void* centroids, int32_t n_iters, uint8_t* ids_out,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  try {
+    KVC_REQUIRE(heads >= 0 && n_tokens >= 0, KVC_ERR_INVALID_ARG, "heads and n_tokens must be >= 0");
+    KVC_REQUIRE(dim == 64 || dim == 128, KVC_ERR_INVALID_ARG, "dim must be 64 or 128");
+    KVC_REQUIRE(valid_dtype(dt), KVC_ERR_INVALID_ARG, "bad dtype");
+    KVC_REQUIRE(n_centroids >= 1 && n_centroids <= 256, KVC_ERR_INVALID_ARG, "n_centroids must be in [1, 256]");
+    KVC_REQUIRE(n_iters >= 0, KVC_ERR_INVALID_ARG, "n_iters must be >= 0");
+    const bool work = heads > 0 && n_tokens > 0;
+    KVC_PTR(x, work, "x");
+    KVC_PTR(centroids, heads > 0, "centroids");
+    KVC_PTR(ids_out, work, "ids_out");
+    if (!work) return ok();
+    const size_t need = kvc_fit_assign_workspace_bytes(heads, n_tokens, dim, n_centroids);
+    KVC_REQUIRE(ws_bytes >= need, KVC_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    KVC_PTR(ws, true, "ws");
+    float* norms = static_cast<float*>(ws);
+    for (int it = 0; it <= n_iters; ++it) {
+      hipError_t e = kvc::launch_centroid_norms(heads, n_centroids, dim, dt, centroids, norms, stream);
+      if (e != hipSuccess) return hip_status(e, "centroid norms");
+      e = kvc::launch_assign(heads, n_tokens, dim, dt, x, n_centroids, centroids, norms, ids_out, stream);
+      if (e != hipSuccess) return hip_status(e, "assign");
+      if (it == n_iters) break;
+      e = kvc::launch_kmeans_update(heads, n_tokens, dim, dt, x, n_centroids, centroids, ids_out, stream);
+      if (e != hipSuccess) return hip_status(e, "k-means update");
+    }
+    return ok();
+  } catch (...) {
+    return fail(KVC_ERR_HIP, "unexpected exception in kvc_fit_assign");
+  }
+}
+
+// ------------------------------------------------------------------------------ encode
+size_t kvc_encode_workspace_bytes(int32_t heads, int64_t n_tokens, int32_t dim, int32_t n_centroids,
+                                  int32_t ids_given) {
+  if (ids_given) return 0;
+  return kvc_fit_assign_workspace_bytes(heads, n_tokens, dim, n_centroids);
+}
+
+kvc_status kvc_encode(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt, const void* x,
+                      int32_t n_centroids, const void* centroids, const uint8_t* ids_in, uint8_t* ids_out,
+                      const float* basis, int32_t rank, int32_t bits, int32_t group, uint8_t* codes,
+                      uint16_t* meta, void* ws, size_t ws_bytes, hipStream_t stream) {
+  try {
+    KVC_REQUIRE(heads >= 0 && n_tokens >= 0, KVC_ERR_INVALID_ARG, "heads and n_tokens must be >= 0");
+    KVC_REQUIRE(dim == 64 || dim == 128, KVC_ERR_INVALID_ARG, "dim must be 64 or 128");
+    KVC_REQUIRE(valid_dtype(dt), KVC_ERR_INVALID_ARG, "bad dtype");
+    KVC_REQUIRE(n_centroids >= 1 && n_centroids <= 256, KVC_ERR_INVALID_ARG, "n_centroids must be in [1, 256]");
+    KVC_REQUIRE(bits == 2 || bits == 4, KVC_ERR_INVALID_ARG, "bits must be 2 or 4");
+    KVC_REQUIRE((basis == nullptr) == (rank == 0), KVC_ERR_INVALID_ARG, "rank must be 0 exactly when basis is NULL");
+    const int code_dim = rank ? rank : dim;
+    KVC_REQUIRE(rank == 0 || (rank >= group && rank <= dim), KVC_ERR_INVALID_ARG, "rank must be 0 or in [group, dim]");
+    KVC_REQUIRE(group > 0 && code_dim % group == 0, KVC_ERR_INVALID_ARG, "group must divide the coded dimension");
+    KVC_REQUIRE(group == 16 || group == 32, KVC_ERR_UNSUPPORTED, "group must be 16 or 32");
+    KVC_REQUIRE(rank == 0 || ((rank == 32 || rank == 64) && dim == 128), KVC_ERR_UNSUPPORTED,
+                "coefficient codes need dim 128 and rank 32 or 64");
+    KVC_REQUIRE(ids_out == nullptr || ids_out != ids_in, KVC_ERR_INVALID_ARG, "ids_out must not alias ids_in");
+    const bool work = heads > 0 && n_tokens > 0;
+    KVC_PTR(x, work, "x");
+    KVC_PTR(centroids, work, "centroids");
+    KVC_PTR(codes, work, "codes");
+    KVC_PTR(meta, work, "meta");
+    KVC_PTR(basis, work && rank > 0, "basis");
+    if (ids_in) KVC_PTR(ids_in, work, "ids_in");
+    if (ids_out) KVC_PTR(ids_out, work, "ids_out");
+    if (!work) return ok();
+    const uint8_t* ids = ids_in;
+    if (ids == nullptr) {
+      KVC_REQUIRE(ids_out != nullptr, KVC_ERR_INVALID_ARG, "ids_out is needed when ids_in is NULL");
+      const size_t need = kvc_encode_workspace_bytes(heads, n_tokens, dim, n_centroids, 0);
+      KVC_REQUIRE(ws_bytes >= need, KVC_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+      KVC_PTR(ws, true, "ws");
+      float* norms = static_cast<float*>(ws);
+      hipError_t e = kvc::launch_centroid_norms(heads, n_centroids, dim, dt, centroids, norms, stream);
+      if (e != hipSuccess) return hip_status(e, "centroid norms");
+      e = kvc::launch_assign(heads, n_tokens, dim, dt, x, n_centroids, centroids, norms, ids_out, stream);
+      if (e != hipSuccess) return hip_status(e, "assign");
+      ids = ids_out;
+    } else if (ids_out != nullptr) {
+      hipError_t e = hipMemcpyAsync(ids_out, ids_in, size_t(heads) * size_t(n_tokens), hipMemcpyDeviceToDevice,
+                                    stream);
+      if (e != hipSuccess) return hip_status(e, "copy ids");
+    }
+    hipError_t e = kvc::launch_encode(heads, n_tokens, dim, dt, x, n_centroids, centroids, ids, basis, rank, bits,
+                                      group, codes, meta, stream);
+    return hip_status(e, "encode");
+  } catch (...) {
+    return fail(KVC_ERR_HIP, "unexpected exception in kvc_encode");
+  }
+}
+
+// ------------------------------------------------------------------------------ attention
+size_t kvc_attend_workspace_bytes(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype,
+                                  const kvc_segment* segs, int32_t n_segs) {
+  if (heads <= 0 || n_q <= 0 || (dim != 64 && dim != 128)) return 0;
+  if (q_dtype == KVC_F32) return 0;  // the fp32 path does not split the history
+  const int s = kvc::attend_split_plan(heads, n_q, total_tiles_of(segs, n_segs), kvc::kAttendRows);
+  return split_bytes(heads, n_q, dim, s);
+}
+
+kvc_status kvc_attend(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype, const void* q,
+                      const kvc_segment* segs, int32_t n_segs, float* out, float* lse, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  try {
+    KVC_REQUIRE(heads >= 0 && n_q >= 0, KVC_ERR_INVALID_ARG, "heads and n_q must be >= 0");
+    KVC_REQUIRE(dim == 64 || dim == 128, KVC_ERR_INVALID_ARG, "dim must be 64 or 128");
+    KVC_REQUIRE(valid_dtype(q_dtype), KVC_ERR_INVALID_ARG, "bad q dtype");
+    kvc::SegList sl;
+    int kb, vb, g;
+    kvc_dtype cdt;
+    kvc_status st = check_segments(heads, dim, segs, n_segs, 0, &sl, &kb, &vb, &g, &cdt);
+    if (st != KVC_OK) return st;
+    const bool work = heads > 0 && n_q > 0;
+    KVC_PTR(q, work, "q");
+    KVC_PTR(out, work, "out");
+    KVC_PTR(lse, work, "lse");
+    if (!work) return ok();
+    if (sl.total_tiles > 0) {
+      KVC_REQUIRE(g == 16 || g == 32, KVC_ERR_UNSUPPORTED, "group must be 16 or 32");
+      KVC_REQUIRE(q_dtype == cdt, KVC_ERR_UNSUPPORTED, "queries and centres must share a dtype");
+    }
+    int n_split = 1;
+    if (q_dtype == KVC_BF16) n_split = kvc::attend_split_plan(heads, n_q, sl.total_tiles, kvc::kAttendRows);
+    const size_t need = split_bytes(heads, n_q, dim, n_split);
+    KVC_REQUIRE(ws_bytes >= need, KVC_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    if (need) KVC_PTR(ws, true, "ws");
+    float* part_out = n_split > 1 ? static_cast<float*>(ws) : out;
+    float* part_lse = n_split > 1
+        ? reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(size_t(n_split) * heads * n_q * dim * 4))
+        : lse;
+    hipError_t e = kvc::launch_attend(heads, n_q, dim, q_dtype, q, sl, kb, vb, g, cdt, n_split, part_out, part_lse,
+                                      stream);
+    if (e != hipSuccess) return hip_status(e, "attend");
+    if (n_split > 1) {
+      e = kvc::launch_lse_merge_strided(heads, n_q, dim, n_split, part_out, part_lse, out, lse, stream);
+      if (e != hipSuccess) return hip_status(e, "split merge");
+    }
+    return ok();
+  } catch (...) {
+    return fail(KVC_ERR_HIP, "unexpected exception in kvc_attend");
+  }
+}
+
+size_t kvc_attend_lowdim_workspace_bytes(int32_t heads, int64_t n_q, int32_t dim, int32_t rank,
+                                         const kvc_segment* segs, int32_t n_segs) {
+  if (heads <= 0 || n_q <= 0 || dim != 128 || (rank != 32 && rank != 64)) return 0;
+  size_t b = align_up(size_t(heads) * size_t(n_q) * rank * 2);   // projected queries (bf16)
+  for (int i = 0; segs != nullptr && i < n_segs; ++i) {
+    const int C = segs[i].n_centroids > 0 ? segs[i].n_centroids : 0;
+    b += 2 * align_up(size_t(heads) * C * rank * 4);              // projected centres (fp32)
+  }
+  const int s = kvc::attend_split_plan(heads, n_q, total_tiles_of(segs, n_segs), kvc::kLowdimRows);
+  return b + split_bytes(heads, n_q, dim, s);
+}
+
+kvc_status kvc_attend_lowdim(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype, const void* q,
+                             const float* basis_k, const float* basis_v, int32_t rank, const kvc_segment* segs,
+                             int32_t n_segs, float* out, float* lse, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  try {
+    KVC_REQUIRE(heads >= 0 && n_q >= 0, KVC_ERR_INVALID_ARG, "heads and n_q must be >= 0");
+    KVC_REQUIRE(dim == 64 || dim == 128, KVC_ERR_INVALID_ARG, "dim must be 64 or 128");
+    KVC_REQUIRE(valid_dtype(q_dtype), KVC_ERR_INVALID_ARG, "bad q dtype");
+    KVC_REQUIRE(rank > 0 && rank <= dim, KVC_ERR_INVALID_ARG, "rank must be in [1, dim]");
+    KVC_REQUIRE(dim == 128 && (rank == 32 || rank == 64), KVC_ERR_UNSUPPORTED, "low-dim path needs dim 128, rank 32 or 64");
+    KVC_REQUIRE(q_dtype == KVC_BF16, KVC_ERR_UNSUPPORTED, "low-dim path needs bf16 queries");
+    kvc::SegList sl;
+    int kb, vb, g;
+    kvc_dtype cdt;
+    kvc_status st = check_segments(heads, dim, segs, n_segs, rank, &sl, &kb, &vb, &g, &cdt);
+    if (st != KVC_OK) return st;
+    const bool work = heads > 0 && n_q > 0;
+    KVC_PTR(q, work, "q");
+    KVC_PTR(basis_k, work, "basis_k");
+    KVC_PTR(basis_v, work, "basis_v");
+    KVC_PTR(out, work, "out");
+    KVC_PTR(lse, work, "lse");
+    if (!work) return ok();
+    if (sl.total_tiles > 0) {
+      KVC_REQUIRE(g == 16 || g == 32, KVC_ERR_UNSUPPORTED, "group must be 16 or 32");
+      KVC_REQUIRE(cdt == KVC_BF16, KVC_ERR_UNSUPPORTED, "low-dim path needs bf16 centres");
+    }
+    const size_t need = kvc_attend_lowdim_workspace_bytes(heads, n_q, dim, rank, segs, n_segs);
+    KVC_REQUIRE(ws_bytes >= need, KVC_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    KVC_PTR(ws, true, "ws");
+    char* w = static_cast<char*>(ws);
+    auto* q_proj = reinterpret_cast<uint16_t*>(w);
+    w += align_up(size_t(heads) * size_t(n_q) * rank * 2);
+    hipError_t e = kvc::launch_project_queries(heads, n_q, dim, rank, q, basis_k, q_proj, stream);
+    if (e != hipSuccess) return hip_status(e, "project queries");
+    int di = 0;
+    for (int i = 0; i < n_segs; ++i) {
+      const int C = segs[i].n_centroids;
+      float* pk = reinterpret_cast<float*>(w);
+      w += align_up(size_t(heads) * C * rank * 4);
+      float* pv = reinterpret_cast<float*>(w);
+      w += align_up(size_t(heads) * C * rank * 4);
+      if (segs[i].n_tokens == 0) continue;
+      e = kvc::launch_project_centres(heads, C, dim, rank, cdt, segs[i].k_cent, basis_k, pk, stream);
+      if (e != hipSuccess) return hip_status(e, "project centres");
+      e = kvc::launch_project_centres(heads, C, dim, rank, cdt, segs[i].v_cent, basis_v, pv, stream);
+      if (e != hipSuccess) return hip_status(e, "project centres");
+      sl.s[di].k_cent_proj = pk;
+      sl.s[di].v_cent_proj = pv;
+      ++di;
+    }
+    const int n_split = kvc::attend_split_plan(heads, n_q, sl.total_tiles, kvc::kLowdimRows);
+    float* part_out = out;
+    float* part_lse = lse;
+    if (n_split > 1) {
+      part_out = reinterpret_cast<float*>(w);
+      w += align_up(size_t(n_split) * heads * n_q * dim * 4);
+      part_lse = reinterpret_cast<float*>(w);
+    }
+    e = kvc::launch_attend_lowdim(heads, n_q, dim, rank, q_proj, basis_v, sl, kb, vb, g, n_split, part_out, part_lse,
+                                  stream);
+    if (e != hipSuccess) return hip_status(e, "attend low-dim");
+    if (n_split > 1) {
+      e = kvc::launch_lse_merge_strided(heads, n_q, dim, n_split, part_out, part_lse, out, lse, stream);
+      if (e != hipSuccess) return hip_status(e, "split merge");
+    }
+    return ok();
+  } catch (...) {
+    return fail(KVC_ERR_HIP, "unexpected exception in kvc_attend_lowdim");
+  }
+}
+
+// ------------------------------------------------------------------------------ merge
+kvc_status kvc_lse_merge(int32_t heads, int64_t n_q, int32_t dim, int32_t n_parts, const float* const* outs,
+                         const float* const* lses, float* out, float* lse, hipStream_t stream) {
+  try {
+    KVC_REQUIRE(heads >= 0 && n_q >= 0, KVC_ERR_INVALID_ARG, "heads and n_q must be >= 0");
+    KVC_REQUIRE(dim > 0 && dim % 4 == 0 && 256 % (dim / 4) == 0, KVC_ERR_INVALID_ARG,
+                "dim must be a multiple of 4 dividing 1024");
+    KVC_REQUIRE(n_parts >= 1, KVC_ERR_INVALID_ARG, "n_parts must be >= 1");
+    const bool work = heads > 0 && n_q > 0;
+    KVC_REQUIRE(!work || (outs != nullptr && lses != nullptr), KVC_ERR_INVALID_ARG, "outs/lses is NULL");
+    KVC_PTR(out, work, "out");
+    KVC_PTR(lse, work, "lse");
+    if (!work) return ok();
+    for (int p = 0; p < n_parts; ++p) {
+      KVC_PTR(outs[p], true, "outs[p]");
+      KVC_PTR(lses[p], true, "lses[p]");
+      if (p > 0)
+        KVC_REQUIRE(outs[p] != out && lses[p] != lse, KVC_ERR_INVALID_ARG,
+                    "only part 0 may alias the output");
+    }
+    return hip_status(kvc::launch_lse_merge(heads, n_q, dim, n_parts, outs, lses, out, lse, stream), "lse merge");
+  } catch (...) {
+    return fail(KVC_ERR_HIP, "unexpected exception in kvc_lse_merge");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Internal declarations shared by the host dispatcher and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "../../include/kvc.h"
+
+namespace kvc {
+
+constexpr int kMaxSegs = 24;        // history segments walked by one attention launch (kernel-argument size)
+constexpr int kMaxMergeParts = 32;  // parts merged by one launch of the merge kernel
+
+// Device-side view of one segment (kernel argument).
+struct SegDev {
+  int64_t n_tokens;
+  int64_t tile_begin;               // first global tile index of this segment
+  int64_t n_centroids;              // C: head stride of the centre tables
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const uint32_t* k_meta;           // one 32-bit word (scale | zero << 16) per group
+  const uint32_t* v_meta;
+  const uint8_t* k_ids;
+  const uint8_t* v_ids;
+  const void* k_cent;
+  const void* v_cent;
+  const float* k_cent_proj;         // low-dim: projected centres [heads][C][rank] (workspace)
+  const float* v_cent_proj;
+};
+
+struct SegList {
+  SegDev s[kMaxSegs];
+  int n;
+  int64_t total_tiles;
+};
+
+// ---------------------------------------------------------------- launchers (return hipError_t)
+hipError_t launch_encode(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C,
+                         const void* cent, const uint8_t* ids, const float* basis, int rank,
+                         int bits, int group, uint8_t* codes, uint16_t* meta, hipStream_t st);
+
+hipError_t launch_centroid_norms(int heads, int C, int dim, kvc_dtype dt, const void* cent,
+                                 float* norms, hipStream_t st);
+hipError_t launch_assign(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C,
+                         const void* cent, const float* norms, uint8_t* ids, hipStream_t st);
+hipError_t launch_kmeans_update(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C,
+                                void* cent, const uint8_t* ids, hipStream_t st);
+
+hipError_t launch_lse_merge(int heads, int64_t n_q, int dim, int n_parts, const float* const* outs,
+                            const float* const* lses, float* out, float* lse, hipStream_t st);
+hipError_t launch_lse_merge_strided(int heads, int64_t n_q, int dim, int n_parts,
+                                    const float* outs, const float* lses, float* out, float* lse,
+                                    hipStream_t st);
+
+// Full-dim attention.  If n_split > 1, writes partial (out, lse) for split s at
+// part_out + s*heads*n_q*dim and part_lse + s*heads*n_q.
+hipError_t launch_attend(int heads, int64_t n_q, int dim, kvc_dtype q_dtype, const void* q,
+                         const SegList& segs, int k_bits, int v_bits, int group, kvc_dtype cdt,
+                         int n_split, float* out, float* lse, hipStream_t st);
+
+hipError_t launch_project_queries(int heads, int64_t n_q, int dim, int rank, const void* q,
+                                  const float* basis, uint16_t* q_proj, hipStream_t st);
+hipError_t launch_project_centres(int heads, int C, int dim, int rank, kvc_dtype cdt,
+                                  const void* cent, const float* basis, float* proj,
+                                  hipStream_t st);
+hipError_t launch_attend_lowdim(int heads, int64_t n_q, int dim, int rank,
+                                const uint16_t* q_proj, const float* basis_v,
+                                const SegList& segs, int k_bits, int v_bits, int group,
+                                int n_split, float* out, float* lse, hipStream_t st);
+
+// Split plan shared by the dispatcher and the workspace-size queries.
+int attend_split_plan(int heads, int64_t n_q, int64_t total_tiles, int rows_per_block);
+
+constexpr int kAttendTile = 64;        // history tokens per tile
+constexpr int kAttendRows = 256;       // queries per workgroup (full-dim path)
+constexpr int kLowdimRows = 256;       // queries per workgroup (low-dim path)
+
+}  // namespace kvc

@@ -1,0 +1,187 @@
+/*
+ * kvc.h -- C ABI of the compressed KV-cache hot path on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (sources: the text of web pages on compressed KV
+ * caches for autoregressive video generation):
+ *   - each head's cached key and value tokens are stored as the id of their
+ *     nearest centre plus a 2- or 4-bit residual (QuantWM, section 4.1, on the
+ *     centroid-residual scheme of QVG; NanoKV, Table 4: 256 centres per head
+ *     for K and V, two k-means iterations);
+ *   - the residual against the centre (TempoKV, section 3.3, Eq. 2) is
+ *     quantized per group of g channels by the affine min/max quantizer of
+ *     TempoKV, section 3.1, Eq. 1, with an fp16 scale and zero-point per group;
+ *   - the current chunk's queries attend over the history reconstructed on the
+ *     fly as centre + dequantized residual, returning the outputs and the
+ *     log-sum-exp (LSE) of each row so that parts of the history can be merged
+ *     (NanoKV, Figure 4d);
+ *   - far history can instead be held as quantized coefficients in a reduced
+ *     basis and read in low dimension (NanoKV, Figure 4a and 4d).
+ *
+ * Conventions shared by every call
+ *   - All data pointers are DEVICE pointers owned by the caller.  Pointer
+ *     arrays (kvc_segment lists, the per-part pointers of kvc_lse_merge) are
+ *     HOST arrays holding device pointers; they are read before the call
+ *     returns and may be released afterwards.
+ *   - Every call is asynchronous on `stream` (0 = the null stream).  The
+ *     library never allocates, frees or synchronizes; scratch memory comes from
+ *     the caller as a workspace whose size the matching *_workspace_bytes
+ *     function returns.
+ *   - Arrays are dense, row-major, with the head index outermost:
+ *       x, centroids ....... [heads][n][dim] in the storage dtype (fp32 or bf16)
+ *       ids ................ [heads][n] uint8 (C <= 256)
+ *       codes .............. [heads][n][code_dim * bits / 8] uint8; code_dim = dim,
+ *                            or rank for coefficient codes.  Channel c of a row
+ *                            sits in byte c / (8/bits) at bit offset
+ *                            bits * (c % (8/bits)), least significant first.
+ *       meta ............... [heads][n][code_dim / group][2] fp16 bit patterns
+ *                            (scale, zero-point) per group, scale first.
+ *       q, out ............. [heads][n_q][dim]; lse [heads][n_q] fp32, natural log.
+ *       basis .............. [heads][dim][rank] fp32, orthonormal columns.
+ *   - Every pointer must be 16-byte aligned.  Outputs must not alias inputs.
+ *   - Inputs are read only; outputs are fully overwritten (code padding = 0).
+ *   - Errors are returned before any launch: KVC_ERR_INVALID_ARG for malformed
+ *     arguments, KVC_ERR_UNSUPPORTED for valid combinations without a built
+ *     kernel, KVC_ERR_WORKSPACE when the workspace is too small, KVC_ERR_HIP
+ *     when the HIP runtime reports a launch error.  kvc_last_error() then holds
+ *     a thread-local message.  No C++ exception crosses this interface.
+ *   - Results are deterministic: assignment and encoding bit for bit, fitting
+ *     with fixed-order fp64 sums, attention for a given split plan.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_ERR_INVALID_ARG = 1,
+  KVC_ERR_UNSUPPORTED = 2,
+  KVC_ERR_WORKSPACE = 3,
+  KVC_ERR_HIP = 4
+} kvc_status;
+
+typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+
+/* One contiguous run of encoded history that shares one centre table per head
+ * and tensor (a cache block, compressed as a unit).  rank = 0 means full-dim
+ * codes; rank > 0 means coefficient codes in a rank-dimensional basis.  All
+ * arrays cover every head of the call, head-major, with n_tokens per head. */
+typedef struct {
+  int64_t n_tokens;
+  int32_t n_centroids;          /* C, 1..256 */
+  int32_t rank;                 /* 0 or the coefficient dimension */
+  int32_t k_bits, v_bits;       /* 2 or 4 each */
+  int32_t group;                /* channel-group size g of the quantizer */
+  kvc_dtype cent_dtype;         /* dtype of the centre tables */
+  const uint8_t *k_codes, *v_codes;
+  const uint16_t *k_meta, *v_meta;
+  const uint8_t *k_ids, *v_ids;
+  const void *k_cent, *v_cent;  /* [heads][C][dim], full dimension even when rank > 0 */
+} kvc_segment;
+
+/* Lloyd k-means per head (QuantWM, section 4.1; NanoKV, Table 4: two
+ * iterations), then a final assignment.
+ *   x          [heads][n_tokens][dim], dtype dt.
+ *   centroids  [heads][n_centroids][dim], dtype dt; in: initial centres, out:
+ *              fitted centres.  Each iteration moves a centre to the mean of its
+ *              members (fp64 sum in token order, one division, rounded to nearest
+ *              even in dt); a centre without members keeps its value.
+ *   n_iters    >= 0 (0 = assignment only).
+ *   ids_out    [heads][n_tokens]: argmin over centres of the squared L2 distance,
+ *              ties to the lowest index.
+ *   ws         workspace of at least kvc_fit_assign_workspace_bytes(...) bytes.
+ * dim must be 64 or 128; n_centroids 1..256; n_tokens >= n_centroids is not
+ * required. */
+kvc_status kvc_fit_assign(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt,
+                          const void* x, int32_t n_centroids, void* centroids,
+                          int32_t n_iters, uint8_t* ids_out,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+size_t kvc_fit_assign_workspace_bytes(int32_t heads, int64_t n_tokens, int32_t dim,
+                                      int32_t n_centroids);
+
+/* Encode tokens against their centres (TempoKV, section 3.1 Eq. 1 and section
+ * 3.3 Eq. 2).  Per token: r = fl32(x - c[id]); with a basis, r is replaced by
+ * its coefficients a_k = sum_i fl32(U[i][k] * r[i]) accumulated in fp32 over
+ * i ascending (multiply and add rounded separately).  Per group of `group`
+ * coded channels: z = fp16 round-down of the minimum, s = fp16 round-up of
+ * fl32((max - z) / (2^bits - 1)), zero values stored as +0; code q =
+ * clamp(round-half-even(fl32(fl32(r - z) * fl32(1/s))), 0, 2^bits - 1), q = 0
+ * when s = 0.
+ *   ids_in     [heads][n_tokens] or NULL; NULL runs the assignment first (then a
+ *              workspace of kvc_encode_workspace_bytes(..., 0) bytes is needed).
+ *   ids_out    NULL, or where the ids used are written (may equal ids_in only
+ *              when ids_in is NULL).
+ *   basis      NULL or [heads][dim][rank] fp32; rank = 0 without a basis.
+ *   bits       2 or 4; group divides the coded dimension (dim or rank).
+ *   codes, meta  outputs as laid out above.
+ * Supported: dim 64 or 128; group 16 or 32 (and group <= coded dimension);
+ * rank 0, or 32 or 64 with dim 128. */
+kvc_status kvc_encode(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt,
+                      const void* x, int32_t n_centroids, const void* centroids,
+                      const uint8_t* ids_in, uint8_t* ids_out,
+                      const float* basis, int32_t rank, int32_t bits, int32_t group,
+                      uint8_t* codes, uint16_t* meta,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+size_t kvc_encode_workspace_bytes(int32_t heads, int64_t n_tokens, int32_t dim,
+                                  int32_t n_centroids, int32_t ids_given);
+
+/* Attention of n_q queries per head over the concatenation of n_segs history
+ * segments (full-dimensional codes, rank = 0): S = q . k_hat / sqrt(dim),
+ * k_hat = c_K[id] + q*s + z, likewise v_hat; out = softmax(S) V_hat, lse =
+ * ln sum exp(S).  No mask.  An empty history gives out = 0, lse = -inf.
+ *   q          [heads][n_q][dim], dtype q_dtype (bf16; fp32 selects an fp32 path).
+ *   segs       host array of n_segs descriptors; every segment must share the
+ *              codec parameters (k_bits, v_bits, group, cent_dtype); each has its
+ *              own centre tables.
+ *   out, lse   fp32 outputs.
+ *   ws         at least kvc_attend_workspace_bytes(...) bytes (partial results of
+ *              the split over history, merged by LSE inside the call). */
+kvc_status kvc_attend(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype, const void* q,
+                      const kvc_segment* segs, int32_t n_segs, float* out, float* lse,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+size_t kvc_attend_workspace_bytes(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype,
+                                  const kvc_segment* segs, int32_t n_segs);
+
+/* Low-dimensional attention over coefficient-coded segments (NanoKV, Figure 4a
+ * and 4d): q' = U_K^T q; k' = U_K^T c_K[id] + a_hat_K; S = q'.k' / sqrt(dim);
+ * O' = softmax(S) (U_V^T c_V[id] + a_hat_V); out = U_V O'.  Returns lse as
+ * kvc_attend does, so that the result LSE-merges with a full-dim part.
+ *   basis_k, basis_v  [heads][dim][rank] fp32, the bases the segments were
+ *                     encoded with (every segment must have this rank).
+ * Supported: dim 128, rank 32 or 64, bf16 queries and centres. */
+kvc_status kvc_attend_lowdim(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype,
+                             const void* q, const float* basis_k, const float* basis_v,
+                             int32_t rank, const kvc_segment* segs, int32_t n_segs,
+                             float* out, float* lse, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+size_t kvc_attend_lowdim_workspace_bytes(int32_t heads, int64_t n_q, int32_t dim, int32_t rank,
+                                         const kvc_segment* segs, int32_t n_segs);
+
+/* Merge n_parts attention results of the same queries (NanoKV, Figure 4d):
+ * lse = ln sum_p exp(lse_p), out = sum_p exp(lse_p - lse) out_p.  Parts with
+ * lse = -inf contribute nothing; if every part is -inf the result is
+ * out = 0, lse = -inf.
+ *   outs, lses  HOST arrays of n_parts device pointers ([heads][n_q][dim] and
+ *               [heads][n_q] fp32).  out/lse may alias outs[0]/lses[0]. */
+kvc_status kvc_lse_merge(int32_t heads, int64_t n_q, int32_t dim, int32_t n_parts,
+                         const float* const* outs, const float* const* lses,
+                         float* out, float* lse, hipStream_t stream);
+
+const char* kvc_status_string(kvc_status status);
+/* Message of the last failed call on this thread ("" if none). */
+const char* kvc_last_error(void);
+/* Library version string. */
+const char* kvc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

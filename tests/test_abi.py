@@ -1,0 +1,141 @@
+"""Host-side tests of the C ABI: the library loads, exports every symbol the
+header declares, and rejects malformed arguments before any GPU work.  No call
+here launches a kernel (all inputs fail validation or describe empty work)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from compressed_kv_cache_kvc_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "kvc.h")
+
+INV, UNS, WS, OK = _lib.KVC_ERR_INVALID_ARG, _lib.KVC_ERR_UNSUPPORTED, _lib.KVC_ERR_WORKSPACE, _lib.KVC_OK
+P = ctypes.c_void_p(1 << 20)       # aligned fake device pointer: never dereferenced here
+MIS = ctypes.c_void_p((1 << 20) + 8)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_symbols_exported(lib):
+    text = open(HDR).read()
+    declared = set(re.findall(r"\b(kvc_[a-z_]+)\s*\(", text))
+    assert declared == set(_lib.EXPORTS), declared ^ set(_lib.EXPORTS)
+    for name in declared:
+        assert getattr(lib, name) is not None
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kvc_version().decode().startswith("kvc")
+    for s, name in [(0, "KVC_OK"), (1, "KVC_ERR_INVALID_ARG"), (2, "KVC_ERR_UNSUPPORTED"),
+                    (3, "KVC_ERR_WORKSPACE"), (4, "KVC_ERR_HIP")]:
+        assert lib.kvc_status_string(s).decode() == name
+
+
+def _encode(lib, **kw):
+    a = dict(heads=2, n=100, dim=128, dt=1, x=P, C=16, cent=P, ids_in=P, ids_out=None, basis=None, rank=0,
+             bits=2, group=16, codes=P, meta=P, ws=None, wsb=0)
+    a.update(kw)
+    return lib.kvc_encode(a["heads"], a["n"], a["dim"], a["dt"], a["x"], a["C"], a["cent"], a["ids_in"],
+                          a["ids_out"], a["basis"], a["rank"], a["bits"], a["group"], a["codes"], a["meta"],
+                          a["ws"], a["wsb"], None)
+
+
+def test_encode_validation(lib):
+    assert _encode(lib, dim=96) == INV
+    assert _encode(lib, bits=3) == INV
+    assert _encode(lib, group=12) == INV
+    assert _encode(lib, group=8) == UNS
+    assert _encode(lib, C=0) == INV and _encode(lib, C=257) == INV
+    assert _encode(lib, rank=32) == INV                       # rank without a basis
+    assert _encode(lib, basis=P, rank=48) == UNS              # valid, but no kernel for rank 48
+    assert _encode(lib, basis=P, rank=8) == INV               # rank below the group
+    assert _encode(lib, basis=P, rank=32, dim=64) == UNS
+    assert _encode(lib, x=None) == INV
+    assert _encode(lib, codes=MIS) == INV
+    assert "aligned" in lib.kvc_last_error().decode()
+    assert _encode(lib, ids_in=None, ids_out=P, ws=None, wsb=0) == WS
+    assert _encode(lib, ids_in=None, ids_out=None) == INV
+    assert _encode(lib, n=-1) == INV
+    assert _encode(lib, n=0, x=None, codes=None, meta=None) == OK   # empty work: no launch
+    assert lib.kvc_last_error().decode() == ""
+
+
+def test_fit_assign_validation(lib):
+    f = lib.kvc_fit_assign
+    assert f(1, 10, 128, 1, P, 4, P, 2, P, None, 0, None) == WS
+    need = lib.kvc_fit_assign_workspace_bytes(1, 10, 128, 4)
+    assert need >= 16
+    assert f(1, 10, 100, 1, P, 4, P, 2, P, P, need, None) == INV
+    assert f(1, 10, 128, 7, P, 4, P, 2, P, P, need, None) == INV
+    assert f(1, 10, 128, 1, P, 300, P, 2, P, P, need, None) == INV
+    assert f(1, 10, 128, 1, P, 4, P, -1, P, P, need, None) == INV
+    assert f(0, 10, 128, 1, None, 4, None, 2, None, None, 0, None) == OK
+
+
+def _seg(**kw):
+    s = _lib.KvcSegment()
+    s.n_tokens, s.n_centroids, s.rank, s.k_bits, s.v_bits, s.group, s.cent_dtype = 100, 16, 0, 2, 2, 16, 1
+    for n in ("k_codes", "v_codes", "k_meta", "v_meta", "k_ids", "v_ids", "k_cent", "v_cent"):
+        setattr(s, n, P.value)
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def _attend(lib, segs, **kw):
+    a = dict(heads=2, n_q=10, dim=128, qdt=1, q=P, out=P, lse=P, ws=P, wsb=1 << 30)
+    a.update(kw)
+    arr = (_lib.KvcSegment * max(1, len(segs)))(*segs)
+    return lib.kvc_attend(a["heads"], a["n_q"], a["dim"], a["qdt"], a["q"], arr, len(segs), a["out"], a["lse"],
+                          a["ws"], a["wsb"], None)
+
+
+def test_attend_validation(lib):
+    assert _attend(lib, [_seg(k_bits=3)]) == INV
+    assert _attend(lib, [_seg(group=24)]) == INV
+    assert _attend(lib, [_seg(rank=32)]) == INV
+    assert _attend(lib, [_seg(), _seg(v_bits=4)]) == UNS     # segments must share codec parameters
+    assert _attend(lib, [_seg(k_codes=None)]) == INV
+    assert _attend(lib, [_seg()] * 25) == UNS                 # more segments than one launch walks
+    assert _attend(lib, [_seg(cent_dtype=0)]) == UNS          # bf16 queries with fp32 centres
+    assert _attend(lib, [_seg()], heads=0) == OK
+    arr = (_lib.KvcSegment * 1)(_seg(n_tokens=9360))
+    need = lib.kvc_attend_workspace_bytes(1, 256, 128, 1, arr, 1)
+    assert need > 0                                           # one query block: the history is split
+    assert _attend(lib, [_seg(n_tokens=9360)], heads=1, n_q=256, ws=P, wsb=need - 1) == WS
+
+
+def test_split_plan_sizes(lib):
+    # self-forcing-like layer: 12 heads x 19 query blocks = 228 workgroups -> history split 3 ways
+    arr = (_lib.KvcSegment * 1)(_seg(n_tokens=9360))
+    need = lib.kvc_attend_workspace_bytes(12, 4680, 128, 1, arr, 1)
+    rows = 12 * 4680
+    assert need == pytest.approx(3 * rows * 128 * 4 + 3 * rows * 4, rel=1e-3)
+    # streaming: 720 heads fill the chip without a split
+    arr = (_lib.KvcSegment * 1)(_seg(n_tokens=46800))
+    assert lib.kvc_attend_workspace_bytes(720, 4680, 128, 1, arr, 1) == 0
+
+
+def test_lowdim_validation(lib):
+    arr = (_lib.KvcSegment * 1)(_seg(rank=32))
+    f = lib.kvc_attend_lowdim
+    assert f(2, 10, 128, 1, P, P, P, 48, arr, 1, P, P, P, 1 << 30, None) == UNS
+    assert f(2, 10, 128, 0, P, P, P, 32, arr, 1, P, P, P, 1 << 30, None) == UNS
+    assert f(2, 10, 128, 1, P, None, P, 32, arr, 1, P, P, P, 1 << 30, None) == INV
+    arr0 = (_lib.KvcSegment * 1)(_seg(rank=0))
+    assert f(2, 10, 128, 1, P, P, P, 32, arr0, 1, P, P, P, 1 << 30, None) == INV
+
+
+def test_merge_validation(lib):
+    po = (ctypes.c_void_p * 2)(P.value, P.value)
+    f = lib.kvc_lse_merge
+    assert f(1, 10, 128, 0, po, po, P, P, None) == INV
+    assert f(1, 10, 127, 2, po, po, P, P, None) == INV
+    assert f(1, 10, 128, 2, po, po, P, P, None) == INV        # part 1 aliases the output
+    assert f(0, 10, 128, 2, po, po, P, P, None) == OK

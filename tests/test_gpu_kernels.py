@@ -1,0 +1,281 @@
+"""GPU parity of each kernel against the oracle at sizes the oracle finishes in
+seconds, spanning several tiles with ragged tails, plus the edge cases.
+
+Codes and metadata must be bit-exact given the same ids and centres; ids must
+match except where the oracle's top-2 distance gap is below 1e-5 relative;
+attention must be within rel-L2 1e-2, max-abs 2e-2 and |dLSE| 2e-2 of the fp64
+oracle on the same (oracle-made) cache; the LSE merge within 1e-6 relative."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.helpers import Cache, check_attention, encode_heads, near_tie, np32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X: torch.cuda.is_available() is False")
+    import compressed_kv_cache_kvc_amd as kvc
+    kvc.library()
+    yield
+
+
+def kvc():
+    import compressed_kv_cache_kvc_amd as m
+    return m
+
+
+def _bf16_tokens(H, N, d, seed, scale=1.0, outliers=True):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(H, N, d, generator=g) * scale
+    if outliers:
+        x[:, :, :4] *= 8.0
+    return x.to(torch.bfloat16)
+
+
+# ------------------------------------------------------------------------------ encode
+@pytest.mark.parametrize("d,bits,group,dtype", [
+    (128, 2, 16, torch.bfloat16), (128, 4, 32, torch.bfloat16), (128, 2, 32, torch.bfloat16),
+    (128, 4, 16, torch.bfloat16), (64, 2, 16, torch.bfloat16), (64, 4, 32, torch.bfloat16),
+    (64, 4, 32, torch.float32), (128, 2, 16, torch.float32)])
+def test_encode_bit_exact(d, bits, group, dtype):
+    H, N, C = 3, 1037, 37
+    x = _bf16_tokens(H, N, d, 1).to(dtype)
+    if dtype == torch.float32:
+        x = x + 1e-3 * torch.randn(H, N, d, generator=torch.Generator().manual_seed(2))
+    cent = synth.forgy_init(x, C, 3)
+    cent[:, 0] = 0                                  # an all-zero centre for the edge cases
+    xn, cn = np32(x), np32(cent)
+    ids = np.stack([oracle.assign(xn[h], cn[h])[0] for h in range(H)])
+    # edge cases (ids are inputs of encode, so they may point anywhere): a token
+    # equal to its centre, tiny residuals (subnormal fp16 scales), a constant
+    # group, a large-magnitude token
+    x2 = x.clone()
+    g = torch.Generator().manual_seed(12)
+    for h in range(H):
+        x2[h, 5] = cent[h, ids[h, 5]]
+        ids[h, 6:9] = 0
+        x2[h, 6] = (1e-6 * torch.randn(d, generator=g)).to(dtype)
+        x2[h, 7, :group] = 0.5
+        x2[h, 8] = (torch.linspace(-300, 300, d)).to(dtype)
+    xn = np32(x2)
+    ref_codes, ref_meta = encode_heads(xn, cn, ids, bits, group)
+    codes, meta, _ = kvc().encode(x2.to(DEV), cent.to(DEV), bits, group,
+                                  ids=torch.from_numpy(ids.astype(np.uint8)).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), ref_codes)
+    assert np.array_equal(meta.cpu().numpy(), ref_meta)
+
+
+@pytest.mark.parametrize("rank,bits,group", [(32, 2, 16), (32, 4, 16), (64, 4, 32), (64, 2, 32)])
+def test_encode_lowdim_bit_exact(rank, bits, group):
+    H, N, C, d = 2, 777, 20, 128
+    x = _bf16_tokens(H, N, d, 4)
+    cent = synth.forgy_init(x, C, 5)
+    U = synth.orthonormal_basis(H, d, rank, 6)
+    xn, cn = np32(x), np32(cent)
+    ids = np.stack([oracle.assign(xn[h], cn[h])[0] for h in range(H)])
+    ref_codes, ref_meta = encode_heads(xn, cn, ids, bits, group, U.numpy())
+    codes, meta, _ = kvc().encode(x.to(DEV), cent.to(DEV), bits, group,
+                                  ids=torch.from_numpy(ids.astype(np.uint8)).to(DEV), basis=U.to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), ref_codes)
+    assert np.array_equal(meta.cpu().numpy(), ref_meta)
+
+
+# ------------------------------------------------------------------------------ assign / fit
+def _check_ids(ids_gpu, x, cent):
+    """ids equal except near-ties; exact ties (D1 == D2) must go to the lowest
+    index like the oracle's.  Returns the number of excluded near-ties."""
+    excluded = 0
+    for h in range(x.shape[0]):
+        ids, d1, d2 = oracle.assign(x[h], cent[h])
+        exact = d1 == d2
+        tie = near_tie(d1, d2) & ~exact
+        bad = (ids_gpu[h] != ids) & ~tie
+        assert not bad.any(), f"head {h}: {int(bad.sum())} ids differ outside near-ties"
+        excluded += int(tie.sum())
+    return excluded
+
+
+@pytest.mark.parametrize("d,C,N", [(128, 256, 1300), (128, 100, 999), (64, 16, 700), (64, 256, 513)])
+def test_assign_bf16(d, C, N):
+    cfg = synth.get_config("self_forcing_layer")
+    H = 2
+    x = synth.AR1Stream(cfg, "k", heads=H).tokens(1560)[:, :N, :d].contiguous() if d == 128 else \
+        _bf16_tokens(H, N, d, 7)
+    cent = synth.forgy_init(x, C, 8)
+    cent[:, C - 1] = cent[:, 0]                    # exact duplicate: ties go to the lower index
+    ids = kvc().fit_assign(x.to(DEV), cent.to(DEV).clone(), n_iter=0)
+    torch.cuda.synchronize()
+    excl = _check_ids(ids.cpu().numpy().astype(np.int64), np32(x), np32(cent))
+    assert excl <= max(2, 0.001 * H * N)
+
+
+def test_assign_fp32_tiny():
+    cfg = synth.get_config("tiny")
+    x, _ = synth.tiny_kv(cfg, "k")
+    cent = synth.forgy_init(x, cfg.n_centroids, 9)
+    ids = kvc().fit_assign(x.to(DEV), cent.to(DEV).clone(), n_iter=0)
+    torch.cuda.synchronize()
+    _check_ids(ids.cpu().numpy().astype(np.int64), np32(x), np32(cent))
+
+
+@pytest.mark.parametrize("dtype,storage", [(torch.bfloat16, "bf16"), (torch.float32, "f32")])
+def test_fit_matches_oracle_per_iteration(dtype, storage):
+    cfg = synth.get_config("self_forcing_layer")
+    H, N, C = 2, 1560, 64
+    x = synth.AR1Stream(cfg, "v", heads=H).tokens(1560).to(dtype)
+    init = synth.forgy_init(x, C, 10)
+    xn = np32(x)
+    cent_o = np32(init).copy()
+    for it in range(2):
+        # one GPU iteration from the oracle's current centres
+        cg = torch.from_numpy(cent_o).to(dtype).to(DEV)
+        ids_g = kvc().fit_assign(x.to(DEV), cg, n_iter=1)
+        torch.cuda.synchronize()
+        for h in range(H):
+            ids0, d1, d2 = oracle.assign(xn[h], cent_o[h])
+            assert not near_tie(d1, d2).any(), "near-tie in the update test input"
+            c1, ids1 = oracle.fit(xn[h], cent_o[h], n_iter=1, storage=storage)
+            assert np.array_equal(np32(cg)[h].view(np.uint32), c1.view(np.uint32)), f"iteration {it} head {h}"
+            assert np.array_equal(ids_g.cpu().numpy()[h].astype(np.int64), ids1)
+            cent_o[h] = c1
+
+
+# ------------------------------------------------------------------------------ attention
+def _cache(H, N, d, C, kb, vb, g, seed, dtype=torch.bfloat16):
+    x_k = _bf16_tokens(H, N, d, seed).to(dtype)
+    x_v = _bf16_tokens(H, N, d, seed + 1).to(dtype)
+    kc = synth.forgy_init(x_k, C, seed + 2)
+    vc = synth.forgy_init(x_v, C, seed + 3)
+    kn, vn, kcn, vcn = np32(x_k), np32(x_v), np32(kc), np32(vc)
+    kid = np.stack([oracle.assign(kn[h], kcn[h])[0] for h in range(H)])
+    vid = np.stack([oracle.assign(vn[h], vcn[h])[0] for h in range(H)])
+    return Cache(kn, vn, kcn, vcn, kid, vid, kb, vb, g)
+
+
+def _attend_check(q, caches, cent_dtype=torch.bfloat16, what=""):
+    segs = [c.gpu_segment(cent_dtype) for c in caches]
+    out, lse = kvc().attend(q.to(DEV), segs)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    qn = np32(q)
+    res = []
+    for h in range(q.shape[0]):
+        o_ref, l_ref = oracle.attend(qn[h], [c.oracle_segment(h) for c in caches])
+        res.append(check_attention(out[h], lse[h], o_ref, l_ref, f"{what} head {h}"))
+    return res
+
+
+@pytest.mark.parametrize("d,kb,vb,g", [(128, 2, 2, 16), (128, 4, 4, 32), (128, 2, 4, 16), (128, 4, 2, 32),
+                                       (64, 4, 4, 32), (64, 2, 2, 16)])
+def test_attend_single_segment(d, kb, vb, g):
+    H, N, n_q = 2, 1000, 300
+    cache = _cache(H, N, d, 32, kb, vb, g, 20)
+    q = _bf16_tokens(H, n_q, d, 21, outliers=False)
+    _attend_check(q, [cache], what=f"d{d} k{kb}v{vb}g{g}")
+
+
+def test_attend_many_ragged_segments():
+    H, d, n_q = 3, 128, 517
+    caches = [_cache(H, n, d, min(16, n), 2, 4, 16, 30 + i) for i, n in enumerate([130, 64, 1, 333, 700])]
+    q = _bf16_tokens(H, n_q, d, 39, outliers=False)
+    _attend_check(q, caches, what="5 segments")
+
+
+def test_attend_split_history():
+    # one query block and 80 tiles: the history is split across workgroups and merged
+    H, d, n_q, N = 1, 128, 200, 5100
+    cache = _cache(H, N, d, 64, 4, 4, 32, 40)
+    q = _bf16_tokens(H, n_q, d, 41, outliers=False)
+    _attend_check(q, [cache], what="split")
+
+
+def test_attend_empty_history():
+    q = _bf16_tokens(2, 70, 128, 42, outliers=False).to(DEV)
+    out, lse = kvc().attend(q, [])
+    torch.cuda.synchronize()
+    assert not out.cpu().numpy().any() and np.all(np.isneginf(lse.cpu().numpy()))
+
+
+def test_attend_fp32_tiny():
+    cfg = synth.get_config("tiny")
+    k, _ = synth.tiny_kv(cfg, "k")
+    v, _ = synth.tiny_kv(cfg, "v")
+    q = synth.queries(cfg)
+    kc = synth.forgy_init(k, 16, 43)
+    vc = synth.forgy_init(v, 16, 44)
+    kn, vn, kcn, vcn = np32(k), np32(v), np32(kc), np32(vc)
+    kid = np.stack([oracle.assign(kn[0], kcn[0])[0]])
+    vid = np.stack([oracle.assign(vn[0], vcn[0])[0]])
+    cache = Cache(kn, vn, kcn, vcn, kid, vid, 4, 4, 32)
+    _attend_check(q, [cache], cent_dtype=torch.float32, what="tiny fp32")
+
+
+# ------------------------------------------------------------------------------ low-dim attention
+@pytest.mark.parametrize("rank,kb,vb,g", [(32, 2, 4, 16), (64, 4, 4, 32), (32, 4, 2, 32)])
+def test_attend_lowdim(rank, kb, vb, g):
+    H, N, d, n_q, C = 2, 900, 128, 270, 24
+    x_k = _bf16_tokens(H, N, d, 50)
+    x_v = _bf16_tokens(H, N, d, 51)
+    kc, vc = synth.forgy_init(x_k, C, 52), synth.forgy_init(x_v, C, 53)
+    Uk, Uv = synth.orthonormal_basis(H, d, rank, 54), synth.orthonormal_basis(H, d, rank, 55)
+    kn, vn, kcn, vcn = np32(x_k), np32(x_v), np32(kc), np32(vc)
+    kid = np.stack([oracle.assign(kn[h], kcn[h])[0] for h in range(H)])
+    vid = np.stack([oracle.assign(vn[h], vcn[h])[0] for h in range(H)])
+    caches = []
+    for part in (slice(0, 500), slice(500, N)):
+        caches.append(Cache(kn[:, part], vn[:, part], kcn, vcn, kid[:, part], vid[:, part], kb, vb, g,
+                            Uk.numpy(), Uv.numpy()))
+    q = _bf16_tokens(H, n_q, d, 56, outliers=False)
+    out, lse = kvc().attend_lowdim(q.to(DEV), Uk.to(DEV), Uv.to(DEV), [c.gpu_segment() for c in caches])
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    qn = np32(q)
+    for h in range(H):
+        o_ref, l_ref = oracle.attend_lowdim(qn[h], Uk.numpy()[h], Uv.numpy()[h], [c.oracle_segment(h) for c in caches])
+        check_attention(out[h], lse[h], o_ref, l_ref, f"lowdim r{rank} head {h}")
+
+
+# ------------------------------------------------------------------------------ merge
+@pytest.mark.parametrize("P", [1, 2, 5, 40])
+def test_lse_merge(P):
+    H, n_q, d = 3, 129, 128
+    g = torch.Generator().manual_seed(60 + P)
+    outs = [torch.randn(H, n_q, d, generator=g) for _ in range(P)]
+    lses = [torch.randn(H, n_q, generator=g) * 5 for _ in range(P)]
+    if P > 1:
+        lses[1][:, :10] = -float("inf")          # empty parts
+        for p in range(P):
+            lses[p][0, 20] = -float("inf")       # a row with no history at all
+    out, lse = kvc().lse_merge([o.to(DEV) for o in outs], [l.to(DEV) for l in lses])
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for h in range(H):
+        o_ref, l_ref = oracle.lse_merge([o[h].numpy() for o in outs], [l[h].numpy() for l in lses])
+        fin = np.isfinite(l_ref)
+        assert np.array_equal(fin, np.isfinite(lse[h]))
+        assert np.allclose(lse[h][fin], l_ref[fin], rtol=1e-6, atol=1e-6)
+        assert np.allclose(out[h], o_ref, rtol=1e-5, atol=1e-6)
+        assert not out[h][~fin].any()
+
+
+def test_lse_merge_in_place():
+    H, n_q, d = 2, 64, 64
+    g = torch.Generator().manual_seed(70)
+    o0, o1 = torch.randn(H, n_q, d, generator=g), torch.randn(H, n_q, d, generator=g)
+    l0, l1 = torch.randn(H, n_q, generator=g), torch.randn(H, n_q, generator=g)
+    ref = [oracle.lse_merge([o0[h].numpy(), o1[h].numpy()], [l0[h].numpy(), l1[h].numpy()]) for h in range(H)]
+    a, b = o0.to(DEV), l0.to(DEV)
+    kvc().lse_merge([a, o1.to(DEV)], [b, l1.to(DEV)], out=a, lse=b)
+    torch.cuda.synchronize()
+    for h in range(H):
+        assert np.allclose(a.cpu().numpy()[h], ref[h][0], rtol=1e-5, atol=1e-6)
+        assert np.allclose(b.cpu().numpy()[h], ref[h][1], rtol=1e-6, atol=1e-6)
