@@ -1,0 +1,402 @@
+"""Benchmark of the compressed-KV hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input that
+already sits in HBM: fit the K and V centres (two Lloyd iterations + final
+assignment), encode K and V, and attend the current chunk's queries over the
+compressed history (plus, for the larger-backbone workload, the low-dimensional
+far-history read and the LSE merge; for the streaming workload, ten chunks of
+fit + encode + attention over the growing history).
+
+Prints ONE JSON line.  `value` is the compressed-history attention throughput
+(TFLOP/s, 4*n_q*n_kv*d per head, multiply and add counted as 2) over the timed
+steps; the line also carries the encode rate (tokens/s, GB/s), the step time,
+the roofline of the attention kernel measured with HIP events on the launch
+stream, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense fp16/bf16 matrix peak
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="self_forcing_layer",
+                    choices=["self_forcing_layer", "long_history", "larger_backbone", "streaming", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------------------ workloads
+class Workload:
+    """Inputs resident on the GPU plus a step() that runs the whole hot path."""
+
+    def __init__(self, cfg, dev):
+        import torch
+        import synth
+        self.cfg, self.dev, self.torch = cfg, dev, torch
+        self.synth = synth
+        self.phase_ms = {}
+        self.events = []
+
+    def ev(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def mark(self, name, a, b):
+        self.events.append((name, a, b))
+
+    def collect(self):
+        acc = {}
+        for name, a, b in self.events:
+            acc[name] = acc.get(name, 0.0) + a.elapsed_time(b)
+        self.events = []
+        return acc
+
+
+def fit_encode(w, x, cent0, bits, basis=None, n_iter=2):
+    """Fit centres on x (from cent0) and encode: returns (codes, meta, ids, cent)."""
+    import compressed_kv_cache_kvc_amd as kvc
+    cent = cent0.clone()
+    e0 = w.ev()
+    ids = kvc.fit_assign(x, cent, n_iter=n_iter)
+    e1 = w.ev()
+    codes, meta, _ = kvc.encode(x, cent, bits, w.cfg.group, ids=ids)
+    e2 = w.ev()
+    w.mark("fit", e0, e1)
+    w.mark("encode", e1, e2)
+    out = [codes, meta, ids, cent]
+    if basis is not None:
+        lc, lm, _ = kvc.encode(x, cent, bits, w.cfg.group, ids=ids, basis=basis)
+        e3 = w.ev()
+        w.mark("encode", e2, e3)
+        out += [lc, lm]
+    return out
+
+
+class SingleLayer(Workload):
+    """self_forcing_layer, long_history, tiny: one history, fitted and encoded per step."""
+
+    def __init__(self, cfg, dev):
+        super().__init__(cfg, dev)
+        torch, synth = self.torch, self.synth
+        H, N = cfg.heads, cfg.hist
+        if cfg.dtype == "f32":
+            self.k, _ = synth.tiny_kv(cfg, "k")
+            self.v, _ = synth.tiny_kv(cfg, "v")
+            self.k, self.v = self.k.to(dev), self.v.to(dev)
+        else:
+            self.k = synth.AR1Stream(cfg, "k", device=dev).tokens(N)
+            self.v = synth.AR1Stream(cfg, "v", device=dev).tokens(N)
+        self.q = synth.queries(cfg, device=dev)
+        S = cfg.n_segments
+        self.bounds = [N * i // S for i in range(S + 1)]
+        self.k_parts = [self.k[:, a:b].contiguous() for a, b in zip(self.bounds[:-1], self.bounds[1:])]
+        self.v_parts = [self.v[:, a:b].contiguous() for a, b in zip(self.bounds[:-1], self.bounds[1:])]
+        # one centre table per head over the whole history; segments are attention splits
+        self.kc0 = synth.forgy_init(self.k, cfg.n_centroids, synth.seed_for(cfg.seed, 0, 0, 1)).to(dev)
+        self.vc0 = synth.forgy_init(self.v, cfg.n_centroids, synth.seed_for(cfg.seed, 0, 1, 1)).to(dev)
+        self.attn_flops = 4.0 * H * cfg.n_q * N * cfg.dim
+        self.enc_tokens = H * N
+        esz = 4 if cfg.dtype == "f32" else 2
+        self.enc_bytes = sum(H * N * (cfg.dim * esz + 1) + H * N * (cfg.dim * b // 8 + 4 * cfg.dim // cfg.group)
+                             for b in (cfg.k_bits, cfg.v_bits))
+
+    def step(self):
+        import compressed_kv_cache_kvc_amd as kvc
+        cfg = self.cfg
+        if len(self.bounds) == 2:
+            kcodes, kmeta, kid, kc = fit_encode(self, self.k, self.kc0, cfg.k_bits)
+            vcodes, vmeta, vid, vc = fit_encode(self, self.v, self.vc0, cfg.v_bits)
+            segs = [kvc.Segment(kcodes, kmeta, kid, kc, vcodes, vmeta, vid, vc, cfg.k_bits, cfg.v_bits, cfg.group)]
+        else:
+            # one centre table per head over the whole history; each history
+            # segment is encoded from its own slice (segments are attention splits)
+            kc, vc = self.kc0.clone(), self.vc0.clone()
+            e0 = self.ev()
+            kid = kvc.fit_assign(self.k, kc, n_iter=cfg.n_iter)
+            vid = kvc.fit_assign(self.v, vc, n_iter=cfg.n_iter)
+            e1 = self.ev()
+            segs = []
+            for (a, b), ks, vs in zip(zip(self.bounds[:-1], self.bounds[1:]), self.k_parts, self.v_parts):
+                ki, vi = kid[:, a:b].contiguous(), vid[:, a:b].contiguous()
+                kco, kme, _ = kvc.encode(ks, kc, cfg.k_bits, cfg.group, ids=ki)
+                vco, vme, _ = kvc.encode(vs, vc, cfg.v_bits, cfg.group, ids=vi)
+                segs.append(kvc.Segment(kco, kme, ki, kc, vco, vme, vi, vc, cfg.k_bits, cfg.v_bits, cfg.group))
+            e2 = self.ev()
+            self.mark("fit", e0, e1)
+            self.mark("encode", e1, e2)
+        e0 = self.ev()
+        out, lse = kvc.attend(self.q, segs)
+        e1 = self.ev()
+        self.mark("attend", e0, e1)
+        return out
+
+
+class LargerBackbone(Workload):
+    """Far history (rank-32 coefficients) + recent full-dim part, merged by LSE."""
+
+    def __init__(self, cfg, dev):
+        super().__init__(cfg, dev)
+        synth = self.synth
+        H, N, r = cfg.heads, cfg.hist, cfg.rank
+        self.k = synth.AR1Stream(cfg, "k", device=dev).tokens(N)
+        self.v = synth.AR1Stream(cfg, "v", device=dev).tokens(N)
+        self.q = synth.queries(cfg, device=dev)
+        self.kc0 = synth.forgy_init(self.k, cfg.n_centroids, synth.seed_for(cfg.seed, 0, 0, 1)).to(dev)
+        self.vc0 = synth.forgy_init(self.v, cfg.n_centroids, synth.seed_for(cfg.seed, 0, 1, 1)).to(dev)
+        self.Uk = synth.orthonormal_basis(H, cfg.dim, r, synth.seed_for(cfg.seed, 0, 0, 2)).to(dev)
+        self.Uv = synth.orthonormal_basis(H, cfg.dim, r, synth.seed_for(cfg.seed, 0, 1, 2)).to(dev)
+        F, R = cfg.far, cfg.recent
+        self.kf, self.kr = self.k[:, :F].contiguous(), self.k[:, F:].contiguous()
+        self.vf, self.vr = self.v[:, :F].contiguous(), self.v[:, F:].contiguous()
+        self.attn_flops = 4.0 * H * cfg.n_q * R * cfg.dim + 4.0 * H * cfg.n_q * F * r + 4.0 * H * cfg.n_q * cfg.dim * r
+        self.enc_tokens = H * N
+        self.enc_bytes = sum(H * N * (cfg.dim * 2 + 1) for _ in range(2)) + \
+            H * R * (cfg.dim * (cfg.k_bits + cfg.v_bits) // 8 + 8 * cfg.dim // cfg.group) + \
+            H * F * (r * (cfg.k_bits + cfg.v_bits) // 8 + 8 * r // cfg.group)
+
+    def step(self):
+        import compressed_kv_cache_kvc_amd as kvc
+        cfg = self.cfg
+        torch = self.torch
+        kc, vc = self.kc0.clone(), self.vc0.clone()
+        e0 = self.ev()
+        kid = kvc.fit_assign(self.k, kc, n_iter=cfg.n_iter)
+        vid = kvc.fit_assign(self.v, vc, n_iter=cfg.n_iter)
+        e1 = self.ev()
+        F = cfg.far
+        kidf, kidr = kid[:, :F].contiguous(), kid[:, F:].contiguous()
+        vidf, vidr = vid[:, :F].contiguous(), vid[:, F:].contiguous()
+        krc, krm, _ = kvc.encode(self.kr, kc, cfg.k_bits, cfg.group, ids=kidr)
+        vrc, vrm, _ = kvc.encode(self.vr, vc, cfg.v_bits, cfg.group, ids=vidr)
+        kfc, kfm, _ = kvc.encode(self.kf, kc, cfg.k_bits, cfg.group, ids=kidf, basis=self.Uk)
+        vfc, vfm, _ = kvc.encode(self.vf, vc, cfg.v_bits, cfg.group, ids=vidf, basis=self.Uv)
+        e2 = self.ev()
+        recent = kvc.Segment(krc, krm, kidr, kc, vrc, vrm, vidr, vc, cfg.k_bits, cfg.v_bits, cfg.group)
+        far = kvc.Segment(kfc, kfm, kidf, kc, vfc, vfm, vidf, vc, cfg.k_bits, cfg.v_bits, cfg.group, rank=cfg.rank)
+        o1, l1 = kvc.attend(self.q, [recent])
+        e3 = self.ev()
+        o2, l2 = kvc.attend_lowdim(self.q, self.Uk, self.Uv, [far])
+        e4 = self.ev()
+        out, lse = kvc.lse_merge([o1, o2], [l1, l2])
+        e5 = self.ev()
+        self.mark("fit", e0, e1)
+        self.mark("encode", e1, e2)
+        self.mark("attend", e2, e3)
+        self.mark("attend_lowdim", e3, e4)
+        self.mark("lse_merge", e4, e5)
+        return out
+
+
+class Streaming(Workload):
+    """Ten chunks: fit + encode each new chunk for all (layer, head) pairs, then
+    attend the chunk's queries over every segment so far."""
+
+    def __init__(self, cfg, dev):
+        super().__init__(cfg, dev)
+        synth = self.synth
+        H, T = cfg.heads, cfg.chunk
+        ks = synth.AR1Stream(cfg, "k", device=dev)
+        vs = synth.AR1Stream(cfg, "v", device=dev)
+        self.chunks = []
+        for i in range(cfg.steps):
+            k = ks.tokens(T)
+            v = vs.tokens(T)
+            q = synth.queries(cfg, device=dev, stream_id=i)
+            kc0 = synth.forgy_init(k, cfg.n_centroids, synth.seed_for(cfg.seed, i, 0, 1)).to(dev)
+            vc0 = synth.forgy_init(v, cfg.n_centroids, synth.seed_for(cfg.seed, i, 1, 1)).to(dev)
+            self.chunks.append((k, v, q, kc0, vc0))
+        self.attn_flops = sum(4.0 * H * cfg.n_q * T * (i + 1) * cfg.dim for i in range(cfg.steps))
+        self.enc_tokens = H * T * cfg.steps
+        self.enc_bytes = cfg.steps * sum(H * T * (cfg.dim * 2 + 1) + H * T * (cfg.dim * b // 8 + 4 * cfg.dim // cfg.group)
+                                         for b in (cfg.k_bits, cfg.v_bits))
+
+    def step(self):
+        import compressed_kv_cache_kvc_amd as kvc
+        cfg = self.cfg
+        segs = []
+        out = None
+        for (k, v, q, kc0, vc0) in self.chunks:
+            kcodes, kmeta, kid, kc = fit_encode(self, k, kc0, cfg.k_bits)
+            vcodes, vmeta, vid, vc = fit_encode(self, v, vc0, cfg.v_bits)
+            segs.append(kvc.Segment(kcodes, kmeta, kid, kc, vcodes, vmeta, vid, vc, cfg.k_bits, cfg.v_bits, cfg.group))
+            e0 = self.ev()
+            out, lse = kvc.attend(q, segs)
+            e1 = self.ev()
+            self.mark("attend", e0, e1)
+        return out
+
+
+def make_workload(cfg, dev):
+    if cfg.name == "larger_backbone":
+        return LargerBackbone(cfg, dev)
+    if cfg.name == "streaming":
+        return Streaming(cfg, dev)
+    return SingleLayer(cfg, dev)
+
+
+# ------------------------------------------------------------------------------ CPU oracle baseline
+def cpu_baseline(cfg, budget_s):
+    """Time the oracle (as it stands) on a bounded sample of the workload: one
+    head's attention over the full history for as many queries as fit the
+    budget, extrapolated to the workload's unit (TFLOP/s)."""
+    import numpy as np
+    import torch
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_info
+
+    H1 = 1
+    N = cfg.chunk if cfg.name == "streaming" else (cfg.recent if cfg.name == "larger_backbone" else cfg.hist)
+    if cfg.dtype == "f32":
+        k, _ = synth.tiny_kv(cfg, "k")
+        v, _ = synth.tiny_kv(cfg, "v")
+    else:
+        k = synth.AR1Stream(cfg, "k", heads=H1).tokens(N)
+        v = synth.AR1Stream(cfg, "v", heads=H1).tokens(N)
+    kn, vn = k[0].float().numpy(), v[0].float().numpy()
+    C = cfg.n_centroids
+    rng = np.random.default_rng(cfg.seed)
+    kc = kn[rng.choice(N, C, replace=False)]
+    vc = vn[rng.choice(N, C, replace=False)]
+    # the encode leg: ids from the expanded distance (input preparation), codes by the oracle
+    def ids_of(x, c):
+        xt, ct = torch.from_numpy(x.astype(np.float64)), torch.from_numpy(c.astype(np.float64))
+        return ((ct * ct).sum(1)[None] - 2 * xt @ ct.T).argmin(1).numpy()
+    kid, vid = ids_of(kn, kc), ids_of(vn, vc)
+    t0 = time.perf_counter()
+    n_enc = min(N, 4096)
+    kcodes, kmeta = oracle.encode(kn[:n_enc], kc, kid[:n_enc], cfg.k_bits, cfg.group)
+    vcodes, vmeta = oracle.encode(vn[:n_enc], vc, vid[:n_enc], cfg.v_bits, cfg.group)
+    t_enc = time.perf_counter() - t0
+    kcodes, kmeta = oracle.encode(kn, kc, kid, cfg.k_bits, cfg.group)
+    vcodes, vmeta = oracle.encode(vn, vc, vid, cfg.v_bits, cfg.group)
+    seg = oracle.Segment(kcodes, kmeta, kid, kc, vcodes, vmeta, vid, vc, cfg.k_bits, cfg.v_bits, cfg.group)
+    q = synth.queries(cfg, heads=1)[0].float().numpy()
+    # calibrate on 32 queries, then run as many as the budget allows
+    t0 = time.perf_counter()
+    oracle.attend(q[:32], [seg])
+    per_q = (time.perf_counter() - t0) / 32
+    nq = int(max(32, min(len(q), budget_s / max(per_q, 1e-9))))
+    t0 = time.perf_counter()
+    oracle.attend(q[:nq], [seg])
+    t_att = time.perf_counter() - t0
+    flops = 4.0 * nq * N * cfg.dim
+    threads = 1
+    for info in threadpool_info():
+        threads = max(threads, int(info.get("num_threads", 1)))
+    return {
+        "value": flops / t_att / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"fp64 attention of 1 head, {nq} queries x {N} history tokens (d={cfg.dim}); "
+                  f"encode of {n_enc} tokens x 2 tensors",
+        "encode_tokens_per_s": n_enc / t_enc,
+        "seconds": t_att + t_enc,
+        "cpu_count_affinity": len(os.sched_getaffinity(0)),
+    }
+
+
+# ------------------------------------------------------------------------------ main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported on this build "
+              "(the hot path has no multi-GPU sharding; see the design notes on how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import compressed_kv_cache_kvc_amd as kvc
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kvc.library()
+    cfg = synth.get_config(args.workload)
+    w = make_workload(cfg, dev)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        w.step()
+    torch.cuda.synchronize()
+    w.collect()
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        w.step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    phases = w.collect()
+    K = args.steps
+    ms_step = wall * 1e3 / K
+    attend_ms = phases.get("attend", 0.0) / K
+    lowdim_ms = phases.get("attend_lowdim", 0.0) / K
+    encode_ms = phases.get("encode", 0.0) / K
+    fit_ms = phases.get("fit", 0.0) / K
+    attn_ms_total = attend_ms + lowdim_ms + phases.get("lse_merge", 0.0) / K
+    value = w.attn_flops / (attn_ms_total * 1e-3) / 1e12
+
+    # roofline of the full-dim attention kernel (the dominant launch)
+    if cfg.name == "larger_backbone":
+        fl = 4.0 * cfg.heads * cfg.n_q * cfg.recent * cfg.dim
+        launches = 1
+    elif cfg.name == "streaming":
+        fl = w.attn_flops
+        launches = cfg.steps
+    else:
+        fl = w.attn_flops
+        launches = 1
+    achieved = fl / launches / (attend_ms / launches * 1e-3) / 1e12 if attend_ms > 0 else 0.0
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_MFMA_TFLOPS, 4), "traffic": None,
+                "kernel": "attend_kernel", "flops_per_launch": fl / launches,
+                "avg_launch_ms": attend_ms / launches}
+    enc_s = encode_ms * 1e-3
+    line = {
+        "metric": "compressed-history attention TFLOP/s (% bf16 MFMA peak); encode tokens/s, HBM GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 tiles (bf16 inputs), fp32 accumulate" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "heads": cfg.heads, "head_dim": cfg.dim, "history": cfg.hist,
+                   "queries": cfg.n_q, "centroids": cfg.n_centroids, "k_bits": cfg.k_bits, "v_bits": cfg.v_bits,
+                   "group": cfg.group, "segments": cfg.n_segments, "far": cfg.far, "rank": cfg.rank,
+                   "steps": cfg.steps},
+        "pct_mfma_peak": round(100.0 * value / PEAK_MFMA_TFLOPS, 2),
+        "encode_tokens_per_s": round(w.enc_tokens / enc_s, 1) if enc_s > 0 else None,
+        "encode_GBps": round(w.enc_bytes / enc_s / 1e9, 1) if enc_s > 0 else None,
+        "phase_ms": {"fit": round(fit_ms, 4), "encode": round(encode_ms, 4), "attend": round(attend_ms, 4),
+                     "attend_lowdim": round(lowdim_ms, 4),
+                     "lse_merge": round(phases.get("lse_merge", 0.0) / K, 4)},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

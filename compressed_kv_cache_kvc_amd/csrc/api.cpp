@@ -139,14 +139,17 @@ size_t split_bytes(int32_t heads, int64_t n_q, int32_t dim, int n_split) {
 
 namespace kvc {
 
-// Split of the history across workgroups: enough workgroups to cover the chip
-// (256 compute units) about twice, each split keeping at least 16 tiles.
+// Split of the history across workgroups.  One workgroup occupies one compute
+// unit (256 on the chip).  When the query blocks alone cover at least 192 of
+// them, splitting cannot raise the fraction of busy units by much and only adds
+// a merge pass, so the history stays whole; otherwise it is split (up to 8 ways,
+// at least 16 tiles per split) until about two workgroups per unit exist.
 int attend_split_plan(int heads, int64_t n_q, int64_t total_tiles, int rows_per_block) {
   if (total_tiles <= 0 || n_q <= 0 || heads <= 0) return 1;
   const int64_t blocks = int64_t(heads) * ((n_q + rows_per_block - 1) / rows_per_block);
-  const int64_t target = 2 * 256;
+  if (blocks >= 192) return 1;
   int s = 1;
-  while (s < 8 && blocks * s < target && total_tiles / (s + 1) >= 16) ++s;
+  while (s < 8 && blocks * (s + 1) <= 512 && total_tiles / (s + 1) >= 16) ++s;
   return s;
 }
 

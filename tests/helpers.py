@@ -64,16 +64,19 @@ class Cache:
                               self.k_bits, self.v_bits, self.group)
 
     def gpu_segment(self, cent_dtype=torch.bfloat16, head_map=None, device="cuda"):
-        """Upload as a GPU segment; head_map (list of source heads) tiles heads."""
+        """Upload as a GPU segment; head_map (source head of every GPU head) tiles
+        the oracle's heads over a larger head count on the device."""
         import compressed_kv_cache_kvc_amd as kvc
+        idx = None if head_map is None else torch.as_tensor(np.asarray(head_map), device=device)
 
         def up(a, dtype=None):
-            if head_map is not None:
-                a = a[np.asarray(head_map)]
             t = torch.from_numpy(np.ascontiguousarray(a))
             if dtype is not None:
                 t = t.to(dtype)
-            return t.to(device).contiguous()
+            t = t.to(device)
+            if idx is not None:
+                t = t.index_select(0, idx)
+            return t.contiguous()
 
         return kvc.Segment(
             k_codes=up(self.k_codes), k_meta=up(self.k_meta.view(np.int16)).view(torch.uint16),

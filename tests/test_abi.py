@@ -112,11 +112,13 @@ def test_attend_validation(lib):
 
 
 def test_split_plan_sizes(lib):
-    # self-forcing-like layer: 12 heads x 19 query blocks = 228 workgroups -> history split 3 ways
+    # self-forcing-like layer: 12 heads x 19 query blocks = 228 workgroups: no split
     arr = (_lib.KvcSegment * 1)(_seg(n_tokens=9360))
-    need = lib.kvc_attend_workspace_bytes(12, 4680, 128, 1, arr, 1)
-    rows = 12 * 4680
-    assert need == pytest.approx(3 * rows * 128 * 4 + 3 * rows * 4, rel=1e-3)
+    assert lib.kvc_attend_workspace_bytes(12, 4680, 128, 1, arr, 1) == 0
+    # 2 heads x 4 query blocks over 146 tiles: split 8 ways (64 workgroups)
+    rows = 2 * 1000
+    need = lib.kvc_attend_workspace_bytes(2, 1000, 128, 1, arr, 1)
+    assert need == pytest.approx(8 * rows * 128 * 4 + 8 * rows * 4, rel=1e-3)
     # streaming: 720 heads fill the chip without a split
     arr = (_lib.KvcSegment * 1)(_seg(n_tokens=46800))
     assert lib.kvc_attend_workspace_bytes(720, 4680, 128, 1, arr, 1) == 0
