@@ -242,69 +242,113 @@ __device__ __forceinline__ uint32_t f64_to_bits_rne(double d) {
   return (sign << SIGN_SHIFT) | bits;
 }
 
-// One wave per (head, centre): scan the ids in token order, add the member rows in
-// fp64 (fixed order, so the result is deterministic), then mean and round.
-template <typename T, int D>
+// One wavefront per (head, CPW consecutive centres).  The ids are scanned in
+// chunks of 1024 tokens (16 consecutive tokens per lane); the members of the
+// wave's centres are listed in token order in LDS through a prefix sum over the
+// lanes, then their rows are added in fp64, eight row loads in flight at a time.
+// The order of the additions is fixed, so the result is deterministic; each
+// centre becomes the mean (one fp64 division) rounded to nearest even in the
+// storage type, and a centre without members keeps its value.
+template <typename T, int D, int CPW>
 __global__ __launch_bounds__(256) void kmeans_update_kernel(const T* __restrict__ x, T* __restrict__ cent,
                                                             const uint8_t* __restrict__ ids, int C, int64_t n) {
   constexpr int PER = D / 64;                 // channels per lane
+  constexpr int BATCH = 8;
+  static_assert(CPW <= 16, "centre offsets are stored in 4 bits");
+  __shared__ uint32_t s_list[4][1024];        // per wave: (token in chunk << 4) | centre offset
   const int lane = threadIdx.x % 64;
-  const int c = blockIdx.x * 4 + threadIdx.x / 64;
+  const int wave = threadIdx.x / 64;
+  const int c0 = (blockIdx.x * 4 + wave) * CPW;
   const int h = blockIdx.y;
-  if (c >= C) return;
+  if (c0 >= C) return;                        // wave-uniform; the kernel has no block barrier
   const uint8_t* idh = ids + int64_t(h) * n;
   const T* xh = x + int64_t(h) * n * D;
-  double acc[PER];
+  double acc[CPW][PER];
+  int cnt[CPW];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.0;
-  int64_t count = 0;
-  for (int64_t j0 = 0; j0 < n; j0 += 64) {
-    const int64_t j = j0 + lane;
-    const bool mem = j < n && idh[j] == c;
-    uint64_t mask = __ballot(mem);
-    count += __popcll(mask);
-    while (mask) {
-      // up to four members per round: loads first, then adds in token order
-      int b[4];
-      int k = 0;
+  for (int k = 0; k < CPW; ++k) {
+    cnt[k] = 0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        b[u] = -1;
-        if (mask) { b[u] = __builtin_ctzll(mask); mask &= mask - 1; ++k; }
+    for (int i = 0; i < PER; ++i) acc[k][i] = 0.0;
+  }
+  uint32_t* list = s_list[wave];
+  for (int64_t j0 = 0; j0 < n; j0 += 1024) {
+    uint32_t m = 0;                           // members among this lane's 16 tokens
+    uint64_t sel = 0;                         // their centre offsets, 4 bits each
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int64_t j = j0 + 16 * lane + k;
+      const int d = j < n ? int(idh[j]) - c0 : -1;
+      if (d >= 0 && d < CPW) {
+        m |= 1u << k;
+        sel |= uint64_t(d) << (4 * k);
       }
-      float v[4][PER];
+    }
+    // exclusive prefix of the member counts over the lanes (token order is lane-major)
+    const int own = __popc(m);
+    int pre = own;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (b[u] >= 0) {
-          const T* row = xh + (j0 + b[u]) * D;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(pre, off, 64);
+      if (lane >= off) pre += t;
+    }
+    const int total = __shfl(pre, 63, 64);
+    int pos = pre - own;
+    uint32_t mm = m;
+    while (mm) {
+      const int k = __builtin_ctz(mm);
+      mm &= mm - 1;
+      list[pos++] = (uint32_t(16 * lane + k) << 4) | uint32_t((sel >> (4 * k)) & 15u);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int b0 = 0; b0 < total; b0 += BATCH) {
+      uint32_t e[BATCH];
+      float v[BATCH][PER];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        e[u] = __builtin_amdgcn_readfirstlane(b0 + u < total ? list[b0 + u] : 0u);
+        const T* row = xh + (j0 + (e[u] >> 4)) * D;
+        if (b0 + u < total) {
 #pragma unroll
           for (int i = 0; i < PER; ++i) {
-            if constexpr (sizeof(T) == 2) {
-              const uint16_t bits = reinterpret_cast<const uint16_t*>(row)[lane * PER + i];
-              v[u][i] = __uint_as_float(uint32_t(bits) << 16);
-            } else {
+            if constexpr (sizeof(T) == 2)
+              v[u][i] = __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(row)[lane * PER + i]) << 16);
+            else
               v[u][i] = reinterpret_cast<const float*>(row)[lane * PER + i];
-            }
           }
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (b[u] >= 0)
+      for (int u = 0; u < BATCH; ++u) {
+        if (b0 + u < total) {
+          const int ci = int(e[u] & 15u);
 #pragma unroll
-          for (int i = 0; i < PER; ++i) acc[i] = __dadd_rn(acc[i], double(v[u][i]));
-      (void)k;
+          for (int k = 0; k < CPW; ++k) {
+            if (k == ci) {
+              ++cnt[k];
+#pragma unroll
+              for (int i = 0; i < PER; ++i) acc[k][i] = __dadd_rn(acc[k][i], double(v[u][i]));
+            }
+          }
+        }
+      }
     }
+    __builtin_amdgcn_wave_barrier();          // the list is rewritten by the next chunk
   }
-  if (count == 0) return;                     // empty cluster keeps its centre
-  T* dst = cent + (int64_t(h) * C + c) * D;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const double mean = __ddiv_rn(acc[i], double(count));
-    if constexpr (sizeof(T) == 2) {
-      reinterpret_cast<uint16_t*>(dst)[lane * PER + i] = static_cast<uint16_t>(f64_to_bits_rne<8>(mean));
-    } else {
-      reinterpret_cast<uint32_t*>(dst)[lane * PER + i] = f64_to_bits_rne<24>(mean);
+  for (int k = 0; k < CPW; ++k) {
+    const int c = c0 + k;
+    if (c >= C || cnt[k] == 0) continue;      // empty cluster keeps its centre
+    T* dst = cent + (int64_t(h) * C + c) * D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const double mean = __ddiv_rn(acc[k][i], double(cnt[k]));
+      if constexpr (sizeof(T) == 2)
+        reinterpret_cast<uint16_t*>(dst)[lane * PER + i] = static_cast<uint16_t>(f64_to_bits_rne<8>(mean));
+      else
+        reinterpret_cast<uint32_t*>(dst)[lane * PER + i] = f64_to_bits_rne<24>(mean);
     }
   }
 }
@@ -360,25 +404,31 @@ hipError_t launch_assign(int heads, int64_t n, int dim, kvc_dtype dt, const void
   return hipGetLastError();
 }
 
+template <typename T, int D, int CPW>
+hipError_t run_kmeans_update(int heads, int64_t n, const void* x, int C, void* cent, const uint8_t* ids,
+                             hipStream_t st) {
+  const dim3 grid(unsigned((C + 4 * CPW - 1) / (4 * CPW)), unsigned(heads));
+  hipLaunchKernelGGL((kmeans_update_kernel<T, D, CPW>), grid, dim3(256), 0, st, static_cast<const T*>(x),
+                     static_cast<T*>(cent), ids, C, n);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t pick_cpw(int heads, int64_t n, const void* x, int C, void* cent, const uint8_t* ids, hipStream_t st) {
+  // one centre per wavefront while that gives at most ~16k wavefronts; beyond
+  // that, eight centres share a wavefront and its scan of the ids
+  if (int64_t(heads) * C <= 16384) return run_kmeans_update<T, D, 1>(heads, n, x, C, cent, ids, st);
+  return run_kmeans_update<T, D, 8>(heads, n, x, C, cent, ids, st);
+}
+
 hipError_t launch_kmeans_update(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C, void* cent,
                                 const uint8_t* ids, hipStream_t st) {
   if (heads == 0 || n == 0) return hipSuccess;
-  const dim3 grid(unsigned((C + 3) / 4), unsigned(heads));
-  if (dt == KVC_BF16 && dim == 128)
-    hipLaunchKernelGGL((kmeans_update_kernel<bf16_t, 128>), grid, dim3(256), 0, st, static_cast<const bf16_t*>(x),
-                       static_cast<bf16_t*>(cent), ids, C, n);
-  else if (dt == KVC_BF16 && dim == 64)
-    hipLaunchKernelGGL((kmeans_update_kernel<bf16_t, 64>), grid, dim3(256), 0, st, static_cast<const bf16_t*>(x),
-                       static_cast<bf16_t*>(cent), ids, C, n);
-  else if (dt == KVC_F32 && dim == 128)
-    hipLaunchKernelGGL((kmeans_update_kernel<float, 128>), grid, dim3(256), 0, st, static_cast<const float*>(x),
-                       static_cast<float*>(cent), ids, C, n);
-  else if (dt == KVC_F32 && dim == 64)
-    hipLaunchKernelGGL((kmeans_update_kernel<float, 64>), grid, dim3(256), 0, st, static_cast<const float*>(x),
-                       static_cast<float*>(cent), ids, C, n);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (dt == KVC_BF16 && dim == 128) return pick_cpw<bf16_t, 128>(heads, n, x, C, cent, ids, st);
+  if (dt == KVC_BF16 && dim == 64) return pick_cpw<bf16_t, 64>(heads, n, x, C, cent, ids, st);
+  if (dt == KVC_F32 && dim == 128) return pick_cpw<float, 128>(heads, n, x, C, cent, ids, st);
+  if (dt == KVC_F32 && dim == 64) return pick_cpw<float, 64>(heads, n, x, C, cent, ids, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kvc

@@ -23,11 +23,18 @@
 // bits, which keeps the logit error of keys with large outlier channels inside
 // the accuracy target.  Reconstructed keys, values and the queries must lie in the
 // fp16 range, the same range the codec's fp16 scale and zero-point already impose.
-// Tiles are double buffered: global loads of tile t+1 are in flight while tile t
-// is multiplied.
+//
+// Latency hiding: the centre ids of tile t+2 and the codes, metadata and centre
+// rows of tile t+1 are loaded (unconditionally, with clamped indices, so no load
+// result is needed before its use) while tile t is multiplied; tile t+1 is then
+// dequantized into the other LDS buffer.  The running maximum of a row is only
+// raised when a tile's maximum exceeds it by more than 8 (log2 units), so the
+// output accumulator is rarely rescaled; probabilities then stay below 2^8.
 #include "kvc_internal.h"
 #include "dev_common.h"
 #include "mfma.h"
+
+#include <type_traits>
 
 namespace kvc {
 namespace {
@@ -44,7 +51,10 @@ struct AttendParams {
 };
 
 template <int NB>
-__device__ __forceinline__ uint64_t load_code_bits(const uint8_t* p) {
+using code_t = typename std::conditional<(NB > 4), uint64_t, uint32_t>::type;
+
+template <int NB>
+__device__ __forceinline__ code_t<NB> load_code_bits(const uint8_t* p) {
   if constexpr (NB == 1) return *p;
   else if constexpr (NB == 2) return *reinterpret_cast<const uint16_t*>(p);
   else if constexpr (NB == 4) return *reinterpret_cast<const uint32_t*>(p);
@@ -62,14 +72,22 @@ __device__ __forceinline__ int vperm(int k) {
   return (k & ~15) | (o & 3) | ((o & 4) << 1) | ((o & 8) >> 1);
 }
 
-// Globally loaded inputs of one tile for one thread (token dk, channel group dg).
-template <int CH, int KB, int VB>
-struct TileRegs {
-  uint64_t kc, vc;        // packed codes of CH channels
-  uint32_t km, vm;        // (scale | zero << 16)
-  float kcent[CH], vcent[CH];
-  bool valid;
+// Where a tile lives: its segment's arrays and the tile's first token.
+struct TileLoc {
+  const SegDev* s;
+  int64_t j0;             // first token of the tile within the segment
+  int nvalid;             // valid tokens in the tile (1..64)
 };
+
+__device__ __forceinline__ TileLoc locate(const SegList& segs, int& si, int64_t t) {
+  while (si + 1 < segs.n && t >= segs.s[si + 1].tile_begin) ++si;
+  TileLoc L;
+  L.s = &segs.s[si];
+  L.j0 = (t - L.s->tile_begin) * 64;
+  const int64_t rem = L.s->n_tokens - L.j0;
+  L.nvalid = rem >= 64 ? 64 : int(rem);
+  return L;
+}
 
 template <int DQ, int KB, int VB, int G, typename CT, bool LOWDIM, int DOUT>
 __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList segs) {
@@ -113,48 +131,70 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
   const int dk = lane;            // dequant role: token within the tile
   const int dg = wave;            // channel group [dg*CH, dg*CH + CH)
 
-  auto seek = [&](int& si, int64_t t) {
-    while (si + 1 < segs.n && t >= segs.s[si + 1].tile_begin) ++si;
+  // token index of this thread's row in a tile, clamped into the segment so that
+  // every load is in bounds; rows past the end read real (finite) data and are
+  // masked out of the softmax
+  auto row_of = [&](const TileLoc& L) -> int64_t {
+    const int64_t j = L.j0 + (dk < L.nvalid ? dk : L.nvalid - 1);
+    return int64_t(h) * L.s->n_tokens + j;
   };
 
-  auto load_tile = [&](int si, int64_t t, TileRegs<CH, KB, VB>& r) {
-    const SegDev& s = segs.s[si];
-    const int64_t j = (t - s.tile_begin) * 64 + dk;
-    r.valid = j < s.n_tokens;
-    r.kc = r.vc = 0;
-    r.km = r.vm = 0;
+  // ---- register pipeline (raw loaded words; converted only at dequantization)
+  using cent_t = typename std::conditional<LOWDIM, float, CT>::type;
+  constexpr int CW = CH * int(sizeof(cent_t)) / 16;   // 16-byte words of one centre chunk
+  static_assert(CW >= 1, "centre chunk");
+  int kid_n = 0, vid_n = 0;       // ids of the tile to load next (t+1)
+  code_t<KNB> kc_r = 0;
+  code_t<VNB> vc_r = 0;
+  uint32_t km_r = 0, vm_r = 0;
+  uint4 kcw[CW], vcw[CW];
+
+  auto load_ids = [&](const TileLoc& L, int& ki, int& vi) {
+    const int64_t tok = row_of(L);
+    ki = L.s->k_ids[tok];
+    vi = L.s->v_ids[tok];
+  };
+  auto load_data = [&](const TileLoc& L, int ki, int vi) {
+    const int64_t tok = row_of(L);
+    kc_r = load_code_bits<KNB>(L.s->k_codes + tok * (DQ * KB / 8) + dg * KNB);
+    vc_r = load_code_bits<VNB>(L.s->v_codes + tok * (DQ * VB / 8) + dg * VNB);
+    km_r = L.s->k_meta[tok * (DQ / G) + (dg * CH) / G];
+    vm_r = L.s->v_meta[tok * (DQ / G) + (dg * CH) / G];
+    const int64_t C = L.s->n_centroids;
+    const cent_t* kb = LOWDIM ? reinterpret_cast<const cent_t*>(L.s->k_cent_proj)
+                              : static_cast<const cent_t*>(L.s->k_cent);
+    const cent_t* vb = LOWDIM ? reinterpret_cast<const cent_t*>(L.s->v_cent_proj)
+                              : static_cast<const cent_t*>(L.s->v_cent);
+    const uint4* kp = reinterpret_cast<const uint4*>(kb + (int64_t(h) * C + ki) * DQ + dg * CH);
+    const uint4* vp = reinterpret_cast<const uint4*>(vb + (int64_t(h) * C + vi) * DQ + dg * CH);
 #pragma unroll
-    for (int e = 0; e < CH; ++e) { r.kcent[e] = 0.f; r.vcent[e] = 0.f; }
-    if (!r.valid) return;
-    const int64_t tok = int64_t(h) * s.n_tokens + j;
-    const int kid = s.k_ids[tok];
-    const int vid = s.v_ids[tok];
-    r.kc = load_code_bits<KNB>(s.k_codes + tok * (DQ * KB / 8) + dg * KNB);
-    r.vc = load_code_bits<VNB>(s.v_codes + tok * (DQ * VB / 8) + dg * VNB);
-    r.km = s.k_meta[tok * (DQ / G) + (dg * CH) / G];
-    r.vm = s.v_meta[tok * (DQ / G) + (dg * CH) / G];
-    if constexpr (LOWDIM) {
-      load_row<CH>(s.k_cent_proj + (int64_t(h) * s.n_centroids + kid) * DQ + dg * CH, r.kcent);
-      load_row<CH>(s.v_cent_proj + (int64_t(h) * s.n_centroids + vid) * DQ + dg * CH, r.vcent);
+    for (int i = 0; i < CW; ++i) { kcw[i] = kp[i]; vcw[i] = vp[i]; }
+  };
+
+  // element e of a raw centre chunk as fp32
+  auto cent_at = [&](const uint4 (&w)[CW], int e) -> float {
+    if constexpr (sizeof(cent_t) == 2) {
+      const uint4 q = w[e / 8];
+      const int k = (e % 8) / 2;
+      const uint32_t x = k == 0 ? q.x : k == 1 ? q.y : k == 2 ? q.z : q.w;
+      return (e & 1) ? bf16_hi(x) : bf16_lo(x);
     } else {
-      const CT* kcb = static_cast<const CT*>(s.k_cent);
-      const CT* vcb = static_cast<const CT*>(s.v_cent);
-      load_row<CH>(kcb + (int64_t(h) * s.n_centroids + kid) * DQ + dg * CH, r.kcent);
-      load_row<CH>(vcb + (int64_t(h) * s.n_centroids + vid) * DQ + dg * CH, r.vcent);
+      const uint4 q = w[e / 4];
+      const int k = e % 4;
+      return __uint_as_float(k == 0 ? q.x : k == 1 ? q.y : k == 2 ? q.z : q.w);
     }
   };
 
-  auto store_tile = [&](const TileRegs<CH, KB, VB>& r, int buf) {
-    const float ks = f16_bits_to_f32(r.km & 0xffffu), kz = f16_bits_to_f32(r.km >> 16);
-    const float vs = f16_bits_to_f32(r.vm & 0xffffu), vz = f16_bits_to_f32(r.vm >> 16);
+  auto store_tile = [&](int buf) {
+    const float ks = f16_bits_to_f32(km_r & 0xffffu), kz = f16_bits_to_f32(km_r >> 16);
+    const float vs = f16_bits_to_f32(vm_r & 0xffffu), vz = f16_bits_to_f32(vm_r >> 16);
     uint32_t kw[CH / 2];
 #pragma unroll
     for (int e = 0; e < CH; e += 2) {
-      const float q0 = float(uint32_t(r.kc >> (KB * e)) & ((1u << KB) - 1));
-      const float q1 = float(uint32_t(r.kc >> (KB * (e + 1))) & ((1u << KB) - 1));
-      float k0 = r.kcent[e] + fmaf(q0, ks, kz);
-      float k1 = r.kcent[e + 1] + fmaf(q1, ks, kz);
-      if (!r.valid) { k0 = 0.f; k1 = 0.f; }
+      const float q0 = float(uint32_t(kc_r >> (KB * e)) & ((1u << KB) - 1));
+      const float q1 = float(uint32_t(kc_r >> (KB * (e + 1))) & ((1u << KB) - 1));
+      const float k0 = cent_at(kcw, e) + fmaf(q0, ks, kz);
+      const float k1 = cent_at(kcw, e + 1) + fmaf(q1, ks, kz);
       kw[e / 2] = pack_f16x2(k0, k1);
     }
     uint16_t* kdst = &sK[buf][dk * ROWK + dg * CH];
@@ -170,18 +210,17 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
     const int vp = vperm(dk);
 #pragma unroll
     for (int e = 0; e < CH; e += 2) {
-      const float q0 = float(uint32_t(r.vc >> (VB * e)) & ((1u << VB) - 1));
-      const float q1 = float(uint32_t(r.vc >> (VB * (e + 1))) & ((1u << VB) - 1));
-      float v0 = r.vcent[e] + fmaf(q0, vs, vz);
-      float v1 = r.vcent[e + 1] + fmaf(q1, vs, vz);
-      if (!r.valid) { v0 = 0.f; v1 = 0.f; }
+      const float q0 = float(uint32_t(vc_r >> (VB * e)) & ((1u << VB) - 1));
+      const float q1 = float(uint32_t(vc_r >> (VB * (e + 1))) & ((1u << VB) - 1));
+      const float v0 = cent_at(vcw, e) + fmaf(q0, vs, vz);
+      const float v1 = cent_at(vcw, e + 1) + fmaf(q1, vs, vz);
       const uint32_t w = pack_f16x2(v0, v1);
       sV[buf][(dg * CH + e) * ROWV + vp] = static_cast<uint16_t>(w & 0xffffu);
       sV[buf][(dg * CH + e + 1) * ROWV + vp] = static_cast<uint16_t>(w >> 16);
     }
   };
 
-  float m_run = -INFINITY;        // running maximum, log2 units
+  float m_run = -INFINITY;        // reference maximum of the row, log2 units
   float l_run = 0.f;              // this lane's share of the running sum
   f32x16 o[NDB];
 #pragma unroll
@@ -189,25 +228,32 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[b][v] = 0.f;
 
-  int si_load = 0, si_comp = 0;
-  TileRegs<CH, KB, VB> regs;
+  int si_ids = 0, si_data = 0, si_comp = 0;
   if (t_begin < t_end) {
-    seek(si_load, t_begin);
-    load_tile(si_load, t_begin, regs);
-    store_tile(regs, 0);
+    TileLoc L0 = locate(segs, si_data, t_begin);
+    int k0, v0;
+    load_ids(L0, k0, v0);
+    load_data(L0, k0, v0);
+    si_ids = si_data;
+    const TileLoc L1 = locate(segs, si_ids, t_begin + 1 < t_end ? t_begin + 1 : t_begin);
+    load_ids(L1, kid_n, vid_n);
+    store_tile(0);
   }
   __syncthreads();
 
   for (int64_t t = t_begin; t < t_end; ++t) {
     const int buf = int((t - t_begin) & 1);
     const bool has_next = t + 1 < t_end;
-    if (has_next) {
-      seek(si_load, t + 1);
-      load_tile(si_load, t + 1, regs);
+    // issue the loads of tile t+1 (data) and t+2 (ids), clamped to the last tile so
+    // that they are unconditional; they are consumed after the compute
+    {
+      const TileLoc L1 = locate(segs, si_data, has_next ? t + 1 : t);
+      load_data(L1, kid_n, vid_n);
+      const TileLoc L2 = locate(segs, si_ids, t + 2 < t_end ? t + 2 : t_end - 1);
+      load_ids(L2, kid_n, vid_n);
     }
-    seek(si_comp, t);
-    const int64_t nvalid64 = segs.s[si_comp].n_tokens - (t - segs.s[si_comp].tile_begin) * 64;
-    const int nvalid = nvalid64 >= 64 ? 64 : int(nvalid64);
+    const TileLoc Lc = locate(segs, si_comp, t);
+    const int nvalid = Lc.nvalid;
 
     // S^T = K_hat Q^T for keys [0, 32) and [32, 64)
     f32x16 sacc[2];
@@ -235,24 +281,29 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * p.scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * p.scale_log2;
+    // raise the reference maximum only when the tile exceeds it by more than 2^8
+    const bool raise = mx > m_run + 8.f;
+    if (__any(raise)) {
+      const float m_new = raise ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < NDB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[b][v] *= alpha;
+    }
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v], p.scale_log2, -m_new));
+        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v], p.scale_log2, -m_run));
         sacc[kb][v] = e;
         psum += e;
       }
-    l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-    for (int b = 0; b < NDB; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[b][v] *= alpha;
+    l_run += psum;
 
     f16x8 pf[4];
 #pragma unroll
@@ -271,7 +322,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
         o[b] = mfma32h(a, pf[c], o[b]);
       }
 
-    if (has_next) store_tile(regs, buf ^ 1);
+    store_tile(buf ^ 1);           // the last iteration writes a spare copy nobody reads
     __syncthreads();
   }
 

@@ -149,6 +149,30 @@ def test_fit_matches_oracle_per_iteration(dtype, storage):
             cent_o[h] = c1
 
 
+def test_fit_many_heads_eight_centres_per_wave():
+    # heads x centres above 16384 selects the update kernel that gives eight
+    # centres to one wavefront; C = 100 leaves a partial last group
+    H, N, C, d = 200, 300, 100, 64
+    x = _bf16_tokens(H, N, d, 13)
+    init = synth.forgy_init(x, C, 14)
+    cg = init.to(DEV).clone()
+    ids_g = kvc().fit_assign(x.to(DEV), cg, n_iter=1)
+    torch.cuda.synchronize()
+    xn, cn = np32(x), np32(init)
+    checked = 0
+    for h in (0, 1, 99, 199):
+        _, d1, d2 = oracle.assign(xn[h], cn[h])
+        if near_tie(d1, d2).any():
+            continue
+        c1, ids1 = oracle.fit(xn[h], cn[h], n_iter=1, storage="bf16")
+        assert np.array_equal(np32(cg)[h].view(np.uint32), c1.view(np.uint32)), f"head {h}"
+        _, e1, e2 = oracle.assign(xn[h], c1)
+        tie = near_tie(e1, e2) & (e1 != e2)
+        assert not ((ids_g.cpu().numpy()[h] != ids1) & ~tie).any()
+        checked += 1
+    assert checked >= 3
+
+
 # ------------------------------------------------------------------------------ attention
 def _cache(H, N, d, C, kb, vb, g, seed, dtype=torch.bfloat16):
     x_k = _bf16_tokens(H, N, d, seed).to(dtype)
