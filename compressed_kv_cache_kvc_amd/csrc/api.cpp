@@ -69,6 +69,9 @@ kvc_status check_segments(int32_t heads, int32_t dim, const kvc_segment* segs, i
   for (int i = 0; i < n_segs; ++i) {
     const kvc_segment& s = segs[i];
     KVC_REQUIRE(s.n_tokens >= 0, KVC_ERR_INVALID_ARG, "segment %d: n_tokens < 0", i);
+    // the attention kernel addresses a head's rows with 32-bit offsets
+    KVC_REQUIRE(s.n_tokens <= (int64_t(1) << 25), KVC_ERR_UNSUPPORTED,
+                "segment %d: at most 2^25 tokens per head and segment", i);
     KVC_REQUIRE(s.rank == want_rank, KVC_ERR_INVALID_ARG, "segment %d: rank %d, expected %d", i, s.rank,
                 want_rank);
     const int code_dim = want_rank ? want_rank : dim;

@@ -72,23 +72,6 @@ __device__ __forceinline__ int vperm(int k) {
   return (k & ~15) | (o & 3) | ((o & 4) << 1) | ((o & 8) >> 1);
 }
 
-// Where a tile lives: its segment's arrays and the tile's first token.
-struct TileLoc {
-  const SegDev* s;
-  int64_t j0;             // first token of the tile within the segment
-  int nvalid;             // valid tokens in the tile (1..64)
-};
-
-__device__ __forceinline__ TileLoc locate(const SegList& segs, int& si, int64_t t) {
-  while (si + 1 < segs.n && t >= segs.s[si + 1].tile_begin) ++si;
-  TileLoc L;
-  L.s = &segs.s[si];
-  L.j0 = (t - L.s->tile_begin) * 64;
-  const int64_t rem = L.s->n_tokens - L.j0;
-  L.nvalid = rem >= 64 ? 64 : int(rem);
-  return L;
-}
-
 template <int DQ, int KB, int VB, int G, typename CT, bool LOWDIM, int DOUT>
 __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList segs) {
   constexpr int KC = DQ / 16;     // k-chunks of the QK^T product
@@ -131,42 +114,76 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
   const int dk = lane;            // dequant role: token within the tile
   const int dg = wave;            // channel group [dg*CH, dg*CH + CH)
 
-  // token index of this thread's row in a tile, clamped into the segment so that
-  // every load is in bounds; rows past the end read real (finite) data and are
-  // masked out of the softmax
-  auto row_of = [&](const TileLoc& L) -> int64_t {
-    const int64_t j = L.j0 + (dk < L.nvalid ? dk : L.nvalid - 1);
-    return int64_t(h) * L.s->n_tokens + j;
-  };
-
-  // ---- register pipeline (raw loaded words; converted only at dequantization)
   using cent_t = typename std::conditional<LOWDIM, float, CT>::type;
   constexpr int CW = CH * int(sizeof(cent_t)) / 16;   // 16-byte words of one centre chunk
   static_assert(CW >= 1, "centre chunk");
+
+  // A cursor holds the segment of the tiles it walks over, with its arrays
+  // already offset to this workgroup's head; being wave-uniform its fields live
+  // in scalar registers, and are reloaded only when the cursor crosses into the
+  // next segment, so no scalar memory load sits in the tile loop otherwise.
+  struct Cursor {
+    int si;
+    int64_t tile_begin, tile_end;
+    int n_tokens;
+    const uint8_t *k_codes, *v_codes, *k_ids, *v_ids;
+    const uint32_t *k_meta, *v_meta;
+    const cent_t *k_cent, *v_cent;
+  };
+  auto cursor_load = [&](Cursor& c, int si) {
+    const SegDev& s = segs.s[si];
+    c.si = si;
+    c.tile_begin = s.tile_begin;
+    c.tile_end = si + 1 < segs.n ? segs.s[si + 1].tile_begin : segs.total_tiles;
+    c.n_tokens = int(s.n_tokens);
+    const int64_t hn = int64_t(h) * s.n_tokens;
+    c.k_codes = s.k_codes + hn * (DQ * KB / 8);
+    c.v_codes = s.v_codes + hn * (DQ * VB / 8);
+    c.k_ids = s.k_ids + hn;
+    c.v_ids = s.v_ids + hn;
+    c.k_meta = s.k_meta + hn * (DQ / G);
+    c.v_meta = s.v_meta + hn * (DQ / G);
+    const int64_t hc = int64_t(h) * s.n_centroids * DQ;
+    if constexpr (LOWDIM) {
+      c.k_cent = reinterpret_cast<const cent_t*>(s.k_cent_proj) + hc;
+      c.v_cent = reinterpret_cast<const cent_t*>(s.v_cent_proj) + hc;
+    } else {
+      c.k_cent = static_cast<const cent_t*>(s.k_cent) + hc;
+      c.v_cent = static_cast<const cent_t*>(s.v_cent) + hc;
+    }
+  };
+  auto cursor_seek = [&](Cursor& c, int64_t t) {
+    while (t >= c.tile_end) cursor_load(c, c.si + 1);
+  };
+  // token (within the head) of this thread's row in tile t, clamped into the
+  // segment so that every load is in bounds; rows past the end read real
+  // (finite) data and are masked out of the softmax
+  auto row_of = [&](const Cursor& c, int64_t t) -> uint32_t {
+    const int j0 = int(t - c.tile_begin) * 64;
+    const int last = c.n_tokens - 1;
+    return uint32_t(j0 + dk < last ? j0 + dk : last);
+  };
+
+  // ---- register pipeline (raw loaded words; converted only at dequantization)
   int kid_n = 0, vid_n = 0;       // ids of the tile to load next (t+1)
   code_t<KNB> kc_r = 0;
   code_t<VNB> vc_r = 0;
   uint32_t km_r = 0, vm_r = 0;
   uint4 kcw[CW], vcw[CW];
 
-  auto load_ids = [&](const TileLoc& L, int& ki, int& vi) {
-    const int64_t tok = row_of(L);
-    ki = L.s->k_ids[tok];
-    vi = L.s->v_ids[tok];
+  auto load_ids = [&](const Cursor& c, int64_t t, int& ki, int& vi) {
+    const uint32_t j = row_of(c, t);
+    ki = c.k_ids[j];
+    vi = c.v_ids[j];
   };
-  auto load_data = [&](const TileLoc& L, int ki, int vi) {
-    const int64_t tok = row_of(L);
-    kc_r = load_code_bits<KNB>(L.s->k_codes + tok * (DQ * KB / 8) + dg * KNB);
-    vc_r = load_code_bits<VNB>(L.s->v_codes + tok * (DQ * VB / 8) + dg * VNB);
-    km_r = L.s->k_meta[tok * (DQ / G) + (dg * CH) / G];
-    vm_r = L.s->v_meta[tok * (DQ / G) + (dg * CH) / G];
-    const int64_t C = L.s->n_centroids;
-    const cent_t* kb = LOWDIM ? reinterpret_cast<const cent_t*>(L.s->k_cent_proj)
-                              : static_cast<const cent_t*>(L.s->k_cent);
-    const cent_t* vb = LOWDIM ? reinterpret_cast<const cent_t*>(L.s->v_cent_proj)
-                              : static_cast<const cent_t*>(L.s->v_cent);
-    const uint4* kp = reinterpret_cast<const uint4*>(kb + (int64_t(h) * C + ki) * DQ + dg * CH);
-    const uint4* vp = reinterpret_cast<const uint4*>(vb + (int64_t(h) * C + vi) * DQ + dg * CH);
+  auto load_data = [&](const Cursor& c, int64_t t, int ki, int vi) {
+    const uint32_t j = row_of(c, t);
+    kc_r = load_code_bits<KNB>(c.k_codes + (j * uint32_t(DQ * KB / 8) + uint32_t(dg * KNB)));
+    vc_r = load_code_bits<VNB>(c.v_codes + (j * uint32_t(DQ * VB / 8) + uint32_t(dg * VNB)));
+    km_r = c.k_meta[j * uint32_t(DQ / G) + uint32_t((dg * CH) / G)];
+    vm_r = c.v_meta[j * uint32_t(DQ / G) + uint32_t((dg * CH) / G)];
+    const uint4* kp = reinterpret_cast<const uint4*>(c.k_cent + (uint32_t(ki) * DQ + dg * CH));
+    const uint4* vp = reinterpret_cast<const uint4*>(c.v_cent + (uint32_t(vi) * DQ + dg * CH));
 #pragma unroll
     for (int i = 0; i < CW; ++i) { kcw[i] = kp[i]; vcw[i] = vp[i]; }
   };
@@ -228,32 +245,36 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[b][v] = 0.f;
 
-  int si_ids = 0, si_data = 0, si_comp = 0;
+  auto clamp_t = [&](int64_t t) { return t < t_end ? t : t_end - 1; };
+  Cursor cur_ids, cur_data, cur_comp;
   if (t_begin < t_end) {
-    TileLoc L0 = locate(segs, si_data, t_begin);
+    cursor_load(cur_data, 0);
+    cursor_seek(cur_data, t_begin);
+    cur_ids = cur_data;
+    cur_comp = cur_data;
     int k0, v0;
-    load_ids(L0, k0, v0);
-    load_data(L0, k0, v0);
-    si_ids = si_data;
-    const TileLoc L1 = locate(segs, si_ids, t_begin + 1 < t_end ? t_begin + 1 : t_begin);
-    load_ids(L1, kid_n, vid_n);
+    load_ids(cur_data, t_begin, k0, v0);
+    load_data(cur_data, t_begin, k0, v0);
+    cursor_seek(cur_ids, clamp_t(t_begin + 1));
+    load_ids(cur_ids, clamp_t(t_begin + 1), kid_n, vid_n);
     store_tile(0);
   }
   __syncthreads();
 
   for (int64_t t = t_begin; t < t_end; ++t) {
     const int buf = int((t - t_begin) & 1);
-    const bool has_next = t + 1 < t_end;
     // issue the loads of tile t+1 (data) and t+2 (ids), clamped to the last tile so
     // that they are unconditional; they are consumed after the compute
     {
-      const TileLoc L1 = locate(segs, si_data, has_next ? t + 1 : t);
-      load_data(L1, kid_n, vid_n);
-      const TileLoc L2 = locate(segs, si_ids, t + 2 < t_end ? t + 2 : t_end - 1);
-      load_ids(L2, kid_n, vid_n);
+      const int64_t t1 = clamp_t(t + 1), t2 = clamp_t(t + 2);
+      cursor_seek(cur_data, t1);
+      load_data(cur_data, t1, kid_n, vid_n);
+      cursor_seek(cur_ids, t2);
+      load_ids(cur_ids, t2, kid_n, vid_n);
     }
-    const TileLoc Lc = locate(segs, si_comp, t);
-    const int nvalid = Lc.nvalid;
+    cursor_seek(cur_comp, t);
+    const int nvalid_left = cur_comp.n_tokens - int(t - cur_comp.tile_begin) * 64;
+    const int nvalid = nvalid_left >= 64 ? 64 : nvalid_left;
 
     // S^T = K_hat Q^T for keys [0, 32) and [32, 64)
     f32x16 sacc[2];
