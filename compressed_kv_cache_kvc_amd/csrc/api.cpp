@@ -110,8 +110,8 @@ kvc_status check_segments(int32_t heads, int32_t dim, const kvc_segment* segs, i
     d.v_ids = s.v_ids;
     d.k_cent = s.k_cent;
     d.v_cent = s.v_cent;
-    d.k_cent_proj = nullptr;
-    d.v_cent_proj = nullptr;
+    d.k_tab = nullptr;
+    d.v_tab = nullptr;
     out->total_tiles += tiles_of(s.n_tokens);
   }
   (void)heads;
@@ -130,6 +130,15 @@ int64_t total_tiles_of(const kvc_segment* segs, int32_t n_segs) {
   if (segs == nullptr) return 0;
   for (int i = 0; i < n_segs; ++i) t += segs[i].n_tokens > 0 ? tiles_of(segs[i].n_tokens) : 0;
   return t;
+}
+
+// fp16 centre tables (K and V) of every non-empty segment, code_dim channels a row
+size_t table_bytes(int32_t heads, int32_t code_dim, const kvc_segment* segs, int32_t n_segs) {
+  size_t b = 0;
+  for (int i = 0; segs != nullptr && i < n_segs; ++i)
+    if (segs[i].n_tokens > 0 && segs[i].n_centroids > 0)
+      b += 2 * align_up(size_t(heads) * size_t(segs[i].n_centroids) * code_dim * 2);
+  return b;
 }
 
 size_t split_bytes(int32_t heads, int64_t n_q, int32_t dim, int n_split) {
@@ -278,9 +287,9 @@ kvc_status kvc_encode(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt
 size_t kvc_attend_workspace_bytes(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype,
                                   const kvc_segment* segs, int32_t n_segs) {
   if (heads <= 0 || n_q <= 0 || (dim != 64 && dim != 128)) return 0;
-  if (q_dtype == KVC_F32) return 0;  // the fp32 path does not split the history
+  if (q_dtype == KVC_F32) return 0;  // the fp32 path reads the fp32 centres and does not split
   const int s = kvc::attend_split_plan(heads, n_q, total_tiles_of(segs, n_segs), kvc::kAttendRows);
-  return split_bytes(heads, n_q, dim, s);
+  return split_bytes(heads, n_q, dim, s) + table_bytes(heads, dim, segs, n_segs);
 }
 
 kvc_status kvc_attend(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype, const void* q,
@@ -305,14 +314,40 @@ kvc_status kvc_attend(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype
       KVC_REQUIRE(q_dtype == cdt, KVC_ERR_UNSUPPORTED, "queries and centres must share a dtype");
     }
     int n_split = 1;
-    if (q_dtype == KVC_BF16) n_split = kvc::attend_split_plan(heads, n_q, sl.total_tiles, kvc::kAttendRows);
-    const size_t need = split_bytes(heads, n_q, dim, n_split);
+    size_t need = 0;
+    if (q_dtype == KVC_BF16) {
+      n_split = kvc::attend_split_plan(heads, n_q, sl.total_tiles, kvc::kAttendRows);
+      need = split_bytes(heads, n_q, dim, n_split) + table_bytes(heads, dim, segs, n_segs);
+    }
     KVC_REQUIRE(ws_bytes >= need, KVC_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
     if (need) KVC_PTR(ws, true, "ws");
-    float* part_out = n_split > 1 ? static_cast<float*>(ws) : out;
-    float* part_lse = n_split > 1
-        ? reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(size_t(n_split) * heads * n_q * dim * 4))
-        : lse;
+    char* w = static_cast<char*>(ws);
+    float* part_out = out;
+    float* part_lse = lse;
+    if (n_split > 1) {
+      part_out = reinterpret_cast<float*>(w);
+      w += align_up(size_t(n_split) * heads * n_q * dim * 4);
+      part_lse = reinterpret_cast<float*>(w);
+      w += align_up(size_t(n_split) * heads * n_q * 4);
+    }
+    if (q_dtype == KVC_BF16) {
+      // fp16 centre tables in the attention tiles' channel order
+      int di = 0;
+      for (int i = 0; i < n_segs; ++i) {
+        if (segs[i].n_tokens == 0) continue;
+        const int C = segs[i].n_centroids;
+        const size_t tb = align_up(size_t(heads) * C * dim * 2);
+        auto* kt = reinterpret_cast<uint16_t*>(w);
+        auto* vt = reinterpret_cast<uint16_t*>(w + tb);
+        w += 2 * tb;
+        hipError_t e = kvc::launch_centre_table(heads, C, dim, cdt, segs[i].k_cent, kt, stream);
+        if (e == hipSuccess) e = kvc::launch_centre_table(heads, C, dim, cdt, segs[i].v_cent, vt, stream);
+        if (e != hipSuccess) return hip_status(e, "centre table");
+        sl.s[di].k_tab = kt;
+        sl.s[di].v_tab = vt;
+        ++di;
+      }
+    }
     hipError_t e = kvc::launch_attend(heads, n_q, dim, q_dtype, q, sl, kb, vb, g, cdt, n_split, part_out, part_lse,
                                       stream);
     if (e != hipSuccess) return hip_status(e, "attend");
@@ -329,11 +364,8 @@ kvc_status kvc_attend(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype
 size_t kvc_attend_lowdim_workspace_bytes(int32_t heads, int64_t n_q, int32_t dim, int32_t rank,
                                          const kvc_segment* segs, int32_t n_segs) {
   if (heads <= 0 || n_q <= 0 || dim != 128 || (rank != 32 && rank != 64)) return 0;
-  size_t b = align_up(size_t(heads) * size_t(n_q) * rank * 2);   // projected queries (bf16)
-  for (int i = 0; segs != nullptr && i < n_segs; ++i) {
-    const int C = segs[i].n_centroids > 0 ? segs[i].n_centroids : 0;
-    b += 2 * align_up(size_t(heads) * C * rank * 4);              // projected centres (fp32)
-  }
+  size_t b = align_up(size_t(heads) * size_t(n_q) * rank * 2);   // projected queries (fp16)
+  b += table_bytes(heads, rank, segs, n_segs);                      // projected centres (fp16)
   const int s = kvc::attend_split_plan(heads, n_q, total_tiles_of(segs, n_segs), kvc::kLowdimRows);
   return b + split_bytes(heads, n_q, dim, s);
 }
@@ -375,18 +407,18 @@ kvc_status kvc_attend_lowdim(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype 
     if (e != hipSuccess) return hip_status(e, "project queries");
     int di = 0;
     for (int i = 0; i < n_segs; ++i) {
-      const int C = segs[i].n_centroids;
-      float* pk = reinterpret_cast<float*>(w);
-      w += align_up(size_t(heads) * C * rank * 4);
-      float* pv = reinterpret_cast<float*>(w);
-      w += align_up(size_t(heads) * C * rank * 4);
       if (segs[i].n_tokens == 0) continue;
+      const int C = segs[i].n_centroids;
+      const size_t tb = align_up(size_t(heads) * C * rank * 2);
+      auto* pk = reinterpret_cast<uint16_t*>(w);
+      auto* pv = reinterpret_cast<uint16_t*>(w + tb);
+      w += 2 * tb;
       e = kvc::launch_project_centres(heads, C, dim, rank, cdt, segs[i].k_cent, basis_k, pk, stream);
       if (e != hipSuccess) return hip_status(e, "project centres");
       e = kvc::launch_project_centres(heads, C, dim, rank, cdt, segs[i].v_cent, basis_v, pv, stream);
       if (e != hipSuccess) return hip_status(e, "project centres");
-      sl.s[di].k_cent_proj = pk;
-      sl.s[di].v_cent_proj = pv;
+      sl.s[di].k_tab = pk;
+      sl.s[di].v_tab = pv;
       ++di;
     }
     const int n_split = kvc::attend_split_plan(heads, n_q, sl.total_tiles, kvc::kLowdimRows);

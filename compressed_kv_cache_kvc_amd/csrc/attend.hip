@@ -14,7 +14,14 @@
 //   1. every thread dequantizes one (token, channel group) of K and of V from the
 //      packed codes, the fp16 (scale, zero) pair and the centre row into fp16
 //      tiles in LDS (K row-major, V transposed with a key permutation that lets
-//      the probabilities feed the second product straight from registers);
+//      the probabilities feed the second product straight from registers).
+//      Dequantization runs two channels at a time in packed fp16: the hardware's
+//      fp4/fp8 conversions turn a pair of codes into exact small integers, one
+//      fused multiply-add applies (scale, zero) and one add the centre, read from
+//      an fp16 copy of the centre table.  The pairs are channels (c, c+2) of each
+//      block of four, so the tiles, the table and the queries all hold the
+//      channels of a block in the order 0, 2, 1, 3 (the contraction does not care;
+//      the output rows are put back in order when written);
 //   2. each wavefront computes S^T = K_hat Q^T on v_mfma_f32_32x32x16_f16, so a
 //      lane holds 32 scores of one query; the online softmax uses exp2 with the
 //      1/sqrt(d) log2(e) factor applied in fp32;
@@ -50,6 +57,70 @@ struct AttendParams {
   const float* basis_v;   // low-dim: [H][DOUT][DQ]
 };
 
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ h2 as_h2(uint32_t w) { return __builtin_bit_cast(h2, w); }
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// Channel held at position p of a tile row, centre-table row or query fragment:
+// the middle two channels of every block of four are swapped (an involution).
+__host__ __device__ constexpr int tile_channel(int p) { return (p & ~3) | ((p & 1) << 1) | ((p >> 1) & 1); }
+
+// Codes of the channel pairs of one thread's chunk, spread so that each pair
+// converts with one instruction.  Pair j (tile positions 2j, 2j+1) holds channels
+// 4*(j/2) + j%2 and that + 2.  2-bit codes go to nibbles and convert as fp4 e2m1,
+// whose codes 0..3 are 0, 0.5, 1, 1.5 (times the power-of-two scale 2); 4-bit
+// codes go to bytes and convert as fp8 e4m3, whose codes 0..15 are q * 2^-9 (times
+// the scale 2^9).  Either way the result is the integer code, exactly, in fp16.
+template <int NB, int CH>
+struct CodePairs;
+
+template <int CH>
+struct CodePairs<2, CH> {
+  static_assert(CH <= 16, "2-bit chunk fits one word");
+  uint32_t a, b;   // a: nibble n holds code 2n; b: code 2n+1
+  __device__ __forceinline__ explicit CodePairs(uint32_t w) : a(w & 0x33333333u), b((w >> 2) & 0x33333333u) {}
+  __device__ __forceinline__ h2 pair(int j) const {
+    const uint32_t src = (j & 1) ? b : a;
+    switch (j >> 1) {       // byte m = codes (4m, 4m+2) of a, (4m+1, 4m+3) of b
+      case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(src, 2.0f, 0);
+      case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(src, 2.0f, 1);
+      case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(src, 2.0f, 2);
+      default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(src, 2.0f, 3);
+    }
+  }
+};
+
+template <int CH>
+struct CodePairs<4, CH> {
+  static constexpr int NW = (CH * 4 + 31) / 32;
+  uint32_t a[NW], b[NW];   // byte k of a[i]: code 8i + 2k; of b[i]: code 8i + 2k + 1
+  template <typename W>
+  __device__ __forceinline__ explicit CodePairs(W w) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const uint32_t x = uint32_t(w >> (32 * i));
+      a[i] = x & 0x0F0F0F0Fu;
+      b[i] = (x >> 4) & 0x0F0F0F0Fu;
+    }
+  }
+  __device__ __forceinline__ h2 pair(int j) const {
+    const int m = j >> 1;   // word m/2 of the spread codes, 16-bit half m%2
+    const uint32_t src = (j & 1) ? b[m >> 1] : a[m >> 1];
+    if (m & 1) return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 512.0f, true);
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 512.0f, false);
+  }
+};
+
+// (fp16(t0 + c.lo), fp16(t1 + c.hi)) for fp32 t and a packed fp16 pair c, each with
+// a single rounding: v_fma_mix{lo,hi}_f16 with fp32 sources t and 1.0 and the fp16
+// source c, computed in fp32 and rounded once to the destination half.
+__device__ __forceinline__ uint32_t round_add_f16x2(float t0, float t1, uint32_t c) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, 1.0, %2 op_sel_hi:[0,0,1]" : "=&v"(r) : "v"(t0), "v"(c));
+  asm("v_fma_mixhi_f16 %0, %1, 1.0, %2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(r) : "v"(t1), "v"(c));
+  return r;
+}
+
 template <int NB>
 using code_t = typename std::conditional<(NB > 4), uint64_t, uint32_t>::type;
 
@@ -72,7 +143,7 @@ __device__ __forceinline__ int vperm(int k) {
   return (k & ~15) | (o & 3) | ((o & 4) << 1) | ((o & 8) >> 1);
 }
 
-template <int DQ, int KB, int VB, int G, typename CT, bool LOWDIM, int DOUT>
+template <int DQ, int KB, int VB, int G, bool LOWDIM, int DOUT>
 __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList segs) {
   constexpr int KC = DQ / 16;     // k-chunks of the QK^T product
   constexpr int NDB = DQ / 32;    // 32-row blocks of O^T
@@ -94,15 +165,16 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
   const int64_t qi = int64_t(blockIdx.x) * 256 + wave * 32 + col;
   const bool q_ok = qi < p.n_q;
 
-  // B operand Q^T in fp16: bf16 queries convert exactly inside the fp16 range
+  // B operand Q^T in fp16, channels in tile order: bf16 queries convert exactly
+  // inside the fp16 range; reduced queries arrive in fp16 and tile order already
   f16x8 qf[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
     uint4 w = make_uint4(0, 0, 0, 0);
     if (q_ok) w = *reinterpret_cast<const uint4*>(p.q + (int64_t(h) * p.n_q + qi) * DQ + kc * 16 + half * 8);
     if constexpr (!LOWDIM) {
-      w = make_uint4(pack_f16x2(bf16_lo(w.x), bf16_hi(w.x)), pack_f16x2(bf16_lo(w.y), bf16_hi(w.y)),
-                     pack_f16x2(bf16_lo(w.z), bf16_hi(w.z)), pack_f16x2(bf16_lo(w.w), bf16_hi(w.w)));
+      w = make_uint4(pack_f16x2(bf16_lo(w.x), bf16_lo(w.y)), pack_f16x2(bf16_hi(w.x), bf16_hi(w.y)),
+                     pack_f16x2(bf16_lo(w.z), bf16_lo(w.w)), pack_f16x2(bf16_hi(w.z), bf16_hi(w.w)));
     }
     qf[kc] = as_f16x8(w);
   }
@@ -114,9 +186,9 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
   const int dk = lane;            // dequant role: token within the tile
   const int dg = wave;            // channel group [dg*CH, dg*CH + CH)
 
-  using cent_t = typename std::conditional<LOWDIM, float, CT>::type;
-  constexpr int CW = CH * int(sizeof(cent_t)) / 16;   // 16-byte words of one centre chunk
-  static_assert(CW >= 1, "centre chunk");
+  // a thread's centre chunk: CH fp16 values from the table, as CH/2 channel pairs
+  constexpr int CWD = CH / 2;
+  static_assert(CWD == 2 || CWD % 4 == 0, "centre chunk");
 
   // A cursor holds the segment of the tiles it walks over, with its arrays
   // already offset to this workgroup's head; being wave-uniform its fields live
@@ -128,7 +200,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
     int n_tokens;
     const uint8_t *k_codes, *v_codes, *k_ids, *v_ids;
     const uint32_t *k_meta, *v_meta;
-    const cent_t *k_cent, *v_cent;
+    const uint16_t *k_tab, *v_tab;
   };
   auto cursor_load = [&](Cursor& c, int si) {
     const SegDev& s = segs.s[si];
@@ -144,13 +216,8 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
     c.k_meta = s.k_meta + hn * (DQ / G);
     c.v_meta = s.v_meta + hn * (DQ / G);
     const int64_t hc = int64_t(h) * s.n_centroids * DQ;
-    if constexpr (LOWDIM) {
-      c.k_cent = reinterpret_cast<const cent_t*>(s.k_cent_proj) + hc;
-      c.v_cent = reinterpret_cast<const cent_t*>(s.v_cent_proj) + hc;
-    } else {
-      c.k_cent = static_cast<const cent_t*>(s.k_cent) + hc;
-      c.v_cent = static_cast<const cent_t*>(s.v_cent) + hc;
-    }
+    c.k_tab = s.k_tab + hc;
+    c.v_tab = s.v_tab + hc;
   };
   auto cursor_seek = [&](Cursor& c, int64_t t) {
     while (t >= c.tile_end) cursor_load(c, c.si + 1);
@@ -169,7 +236,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
   code_t<KNB> kc_r = 0;
   code_t<VNB> vc_r = 0;
   uint32_t km_r = 0, vm_r = 0;
-  uint4 kcw[CW], vcw[CW];
+  uint32_t kcw[CWD], vcw[CWD];
 
   auto load_ids = [&](const Cursor& c, int64_t t, int& ki, int& vi) {
     const uint32_t j = row_of(c, t);
@@ -182,37 +249,37 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
     vc_r = load_code_bits<VNB>(c.v_codes + (j * uint32_t(DQ * VB / 8) + uint32_t(dg * VNB)));
     km_r = c.k_meta[j * uint32_t(DQ / G) + uint32_t((dg * CH) / G)];
     vm_r = c.v_meta[j * uint32_t(DQ / G) + uint32_t((dg * CH) / G)];
-    const uint4* kp = reinterpret_cast<const uint4*>(c.k_cent + (uint32_t(ki) * DQ + dg * CH));
-    const uint4* vp = reinterpret_cast<const uint4*>(c.v_cent + (uint32_t(vi) * DQ + dg * CH));
-#pragma unroll
-    for (int i = 0; i < CW; ++i) { kcw[i] = kp[i]; vcw[i] = vp[i]; }
-  };
-
-  // element e of a raw centre chunk as fp32
-  auto cent_at = [&](const uint4 (&w)[CW], int e) -> float {
-    if constexpr (sizeof(cent_t) == 2) {
-      const uint4 q = w[e / 8];
-      const int k = (e % 8) / 2;
-      const uint32_t x = k == 0 ? q.x : k == 1 ? q.y : k == 2 ? q.z : q.w;
-      return (e & 1) ? bf16_hi(x) : bf16_lo(x);
+    const uint16_t* kp = c.k_tab + (uint32_t(ki) * DQ + dg * CH);
+    const uint16_t* vp = c.v_tab + (uint32_t(vi) * DQ + dg * CH);
+    if constexpr (CWD == 2) {
+      const uint2 a = *reinterpret_cast<const uint2*>(kp), b = *reinterpret_cast<const uint2*>(vp);
+      kcw[0] = a.x; kcw[1] = a.y; vcw[0] = b.x; vcw[1] = b.y;
     } else {
-      const uint4 q = w[e / 4];
-      const int k = e % 4;
-      return __uint_as_float(k == 0 ? q.x : k == 1 ? q.y : k == 2 ? q.z : q.w);
+#pragma unroll
+      for (int i = 0; i < CWD / 4; ++i) {
+        const uint4 a = reinterpret_cast<const uint4*>(kp)[i], b = reinterpret_cast<const uint4*>(vp)[i];
+        kcw[4 * i] = a.x; kcw[4 * i + 1] = a.y; kcw[4 * i + 2] = a.z; kcw[4 * i + 3] = a.w;
+        vcw[4 * i] = b.x; vcw[4 * i + 1] = b.y; vcw[4 * i + 2] = b.z; vcw[4 * i + 3] = b.w;
+      }
     }
   };
 
+  // (scale, scale) and (zero, zero) of a metadata word (scale | zero << 16)
+  auto scale2 = [](uint32_t m) { return as_h2(__builtin_amdgcn_perm(m, m, 0x01000100u)); };
+  auto zero2 = [](uint32_t m) { return as_h2(__builtin_amdgcn_perm(m, m, 0x03020302u)); };
+
   auto store_tile = [&](int buf) {
-    const float ks = f16_bits_to_f32(km_r & 0xffffu), kz = f16_bits_to_f32(km_r >> 16);
-    const float vs = f16_bits_to_f32(vm_r & 0xffffu), vz = f16_bits_to_f32(vm_r >> 16);
+    // keys: q*s + z in fp32 (exact but for one fp32 rounding), then one rounding of
+    // the sum with the centre to fp16; the key tile's rounding error moves every
+    // logit, so keys get the single-rounding form
+    const CodePairs<KB, CH> kq(kc_r);
+    const h2 km = as_h2(km_r);
+    const float ks = float(km[0]), kz = float(km[1]);
     uint32_t kw[CH / 2];
 #pragma unroll
-    for (int e = 0; e < CH; e += 2) {
-      const float q0 = float(uint32_t(kc_r >> (KB * e)) & ((1u << KB) - 1));
-      const float q1 = float(uint32_t(kc_r >> (KB * (e + 1))) & ((1u << KB) - 1));
-      const float k0 = cent_at(kcw, e) + fmaf(q0, ks, kz);
-      const float k1 = cent_at(kcw, e + 1) + fmaf(q1, ks, kz);
-      kw[e / 2] = pack_f16x2(k0, k1);
+    for (int j = 0; j < CH / 2; ++j) {
+      const h2 c = kq.pair(j);
+      kw[j] = round_add_f16x2(fmaf(float(c[0]), ks, kz), fmaf(float(c[1]), ks, kz), kcw[j]);
     }
     uint16_t* kdst = &sK[buf][dk * ROWK + dg * CH];
     if constexpr (CH == 16) {
@@ -224,16 +291,16 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
       static_assert(CH == 4, "channels per thread");
       reinterpret_cast<uint2*>(kdst)[0] = make_uint2(kw[0], kw[1]);
     }
+    // values: (q*s + z) and the centre add in packed fp16 (two roundings; an
+    // error in a value moves only its own share of the output)
+    const CodePairs<VB, CH> vq(vc_r);
+    const h2 vs = scale2(vm_r), vz = zero2(vm_r);
     const int vp = vperm(dk);
 #pragma unroll
-    for (int e = 0; e < CH; e += 2) {
-      const float q0 = float(uint32_t(vc_r >> (VB * e)) & ((1u << VB) - 1));
-      const float q1 = float(uint32_t(vc_r >> (VB * (e + 1))) & ((1u << VB) - 1));
-      const float v0 = cent_at(vcw, e) + fmaf(q0, vs, vz);
-      const float v1 = cent_at(vcw, e + 1) + fmaf(q1, vs, vz);
-      const uint32_t w = pack_f16x2(v0, v1);
-      sV[buf][(dg * CH + e) * ROWV + vp] = static_cast<uint16_t>(w & 0xffffu);
-      sV[buf][(dg * CH + e + 1) * ROWV + vp] = static_cast<uint16_t>(w >> 16);
+    for (int j = 0; j < CH / 2; ++j) {
+      const uint32_t w = as_u32(__builtin_elementwise_fma(vq.pair(j), vs, vz) + as_h2(vcw[j]));
+      sV[buf][(dg * CH + 2 * j) * ROWV + vp] = static_cast<uint16_t>(w & 0xffffu);
+      sV[buf][(dg * CH + 2 * j + 1) * ROWV + vp] = static_cast<uint16_t>(w >> 16);
     }
   };
 
@@ -315,26 +382,28 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[b][v] *= alpha;
     }
-    float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v], p.scale_log2, -m_run));
-        sacc[kb][v] = e;
-        psum += e;
-      }
-    l_run += psum;
+      for (int v = 0; v < 16; ++v) sacc[kb][v] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v], p.scale_log2, -m_run));
 
+    // probabilities in fp16; the row sum is taken over the same rounded values
     f16x8 pf[4];
+    float psum = 0.f;
+    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int kb = c / 2, base = 8 * (c % 2);
-      pf[c] = as_f16x8(make_uint4(pack_f16x2(sacc[kb][base + 0], sacc[kb][base + 1]),
-                                  pack_f16x2(sacc[kb][base + 2], sacc[kb][base + 3]),
-                                  pack_f16x2(sacc[kb][base + 4], sacc[kb][base + 5]),
-                                  pack_f16x2(sacc[kb][base + 6], sacc[kb][base + 7])));
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        w[i] = pack_f16x2(sacc[kb][base + 2 * i], sacc[kb][base + 2 * i + 1]);
+        psum = __builtin_amdgcn_fdot2(as_h2(w[i]), ones, psum, false);
+      }
+      pf[c] = as_f16x8(make_uint4(w[0], w[1], w[2], w[3]));
     }
+    l_run += psum;
+
 #pragma unroll
     for (int b = 0; b < NDB; ++b)
 #pragma unroll
@@ -360,7 +429,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
         for (int g4 = 0; g4 < 4; ++g4) {
           const int dim = b * 32 + 8 * g4 + 4 * half;
           *reinterpret_cast<float4*>(dst + dim) =
-              make_float4(o[b][4 * g4] * inv, o[b][4 * g4 + 1] * inv, o[b][4 * g4 + 2] * inv, o[b][4 * g4 + 3] * inv);
+              make_float4(o[b][4 * g4] * inv, o[b][4 * g4 + 2] * inv, o[b][4 * g4 + 1] * inv, o[b][4 * g4 + 3] * inv);
         }
     }
   } else {
@@ -373,9 +442,10 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
       for (int v = 0; v < 16; ++v) {
         const float mine = o[b][v] * inv;
         const float other = __shfl_xor(mine, 32, 64);
-        // row 8*(v/4) + 4*half + v%4 is held by this lane, the other half's by the partner
-        coef[b * 32 + 8 * (v / 4) + (v % 4)] = half == 0 ? mine : other;
-        coef[b * 32 + 8 * (v / 4) + 4 + (v % 4)] = half == 0 ? other : mine;
+        // row 8*(v/4) + 4*half + v%4 is held by this lane, the other half's by the
+        // partner; rows are tile positions, coefficients are stored by channel
+        coef[tile_channel(b * 32 + 8 * (v / 4) + (v % 4))] = half == 0 ? mine : other;
+        coef[tile_channel(b * 32 + 8 * (v / 4) + 4 + (v % 4))] = half == 0 ? other : mine;
       }
     if (q_ok) {
       const float* U = p.basis_v + int64_t(h) * DOUT * DQ;
@@ -449,7 +519,7 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(const float* __restrict_
   lse[int64_t(h) * n_q + qi] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
-// Reduced queries q' = U^T q (fp32 accumulation, bf16 result).
+// Reduced queries q' = U^T q (fp32 accumulation, fp16 result in tile channel order).
 __global__ __launch_bounds__(256) void project_queries_kernel(const uint16_t* __restrict__ q, const float* __restrict__ basis,
                                                               int64_t n_q, int D, int R, uint16_t* __restrict__ qp) {
   const int64_t item = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -461,13 +531,14 @@ __global__ __launch_bounds__(256) void project_queries_kernel(const uint16_t* __
   const float* U = basis + int64_t(h) * D * R;
   float a = 0.f;
   for (int i = 0; i < D; ++i) a = fmaf(__uint_as_float(uint32_t(qr[i]) << 16), U[i * R + k], a);
-  qp[(int64_t(h) * n_q + qi) * R + k] = static_cast<uint16_t>(pack_f16x2(a, 0.f) & 0xffffu);
+  qp[(int64_t(h) * n_q + qi) * R + tile_channel(k)] = static_cast<uint16_t>(pack_f16x2(a, 0.f) & 0xffffu);
 }
 
-// Projected centres c' = U^T c (fp32).
+// Projected centres c' = U^T c (fp32 accumulation), as an fp16 table in tile
+// channel order.
 template <typename CT>
 __global__ __launch_bounds__(256) void project_centres_kernel(const CT* __restrict__ cent, const float* __restrict__ basis,
-                                                              int C, int D, int R, float* __restrict__ proj) {
+                                                              int C, int D, int R, uint16_t* __restrict__ tab) {
   const int item = blockIdx.x * blockDim.x + threadIdx.x;
   const int h = blockIdx.y;
   if (item >= C * R) return;
@@ -483,15 +554,25 @@ __global__ __launch_bounds__(256) void project_centres_kernel(const CT* __restri
       cv = reinterpret_cast<const float*>(cent)[(int64_t(h) * C + c) * D + i];
     a = fmaf(cv, U[i * R + k], a);
   }
-  proj[(int64_t(h) * C + c) * R + k] = a;
+  tab[(int64_t(h) * C + c) * R + tile_channel(k)] = static_cast<uint16_t>(pack_f16x2(a, 0.f) & 0xffffu);
 }
 
-template <int DQ, typename CT, bool LOWDIM, int DOUT>
+// fp16 copy of a bf16 centre table in tile channel order (exact for bf16 values
+// inside the fp16 normal range).  One thread per block of four channels.
+__global__ __launch_bounds__(256) void centre_table_kernel(const uint2* __restrict__ cent, int64_t n_blocks,
+                                                           uint2* __restrict__ tab) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n_blocks) return;
+  const uint2 w = cent[i];   // channels (0, 1), (2, 3)
+  tab[i] = make_uint2(pack_f16x2(bf16_lo(w.x), bf16_lo(w.y)), pack_f16x2(bf16_hi(w.x), bf16_hi(w.y)));
+}
+
+template <int DQ, bool LOWDIM, int DOUT>
 hipError_t pick_bits(const AttendParams& p, const SegList& segs, int kb, int vb, int g, hipStream_t st) {
   const dim3 grid(unsigned((p.n_q + 255) / 256), unsigned(p.heads), unsigned(p.n_split));
 #define KVC_CASE(KB_, VB_, G_)                                                                               \
   if (kb == KB_ && vb == VB_ && g == G_) {                                                                   \
-    hipLaunchKernelGGL((attend_kernel<DQ, KB_, VB_, G_, CT, LOWDIM, DOUT>), grid, dim3(512), 0, st, p, segs); \
+    hipLaunchKernelGGL((attend_kernel<DQ, KB_, VB_, G_, LOWDIM, DOUT>), grid, dim3(512), 0, st, p, segs); \
     return hipGetLastError();                                                                                \
   }
   KVC_CASE(2, 2, 16) KVC_CASE(2, 4, 16) KVC_CASE(4, 2, 16) KVC_CASE(4, 4, 16)
@@ -543,8 +624,8 @@ hipError_t launch_attend(int heads, int64_t n_q, int dim, kvc_dtype q_dtype, con
   p.lse = lse;
   p.basis_v = nullptr;
   if (cdt != KVC_BF16 && segs.total_tiles > 0) return hipErrorInvalidValue;
-  if (dim == 128) return pick_bits<128, bf16_t, false, 128>(p, segs, k_bits, v_bits, group, st);
-  if (dim == 64) return pick_bits<64, bf16_t, false, 64>(p, segs, k_bits, v_bits, group, st);
+  if (dim == 128) return pick_bits<128, false, 128>(p, segs, k_bits, v_bits, group, st);
+  if (dim == 64) return pick_bits<64, false, 64>(p, segs, k_bits, v_bits, group, st);
   return hipErrorInvalidValue;
 }
 
@@ -558,15 +639,25 @@ hipError_t launch_project_queries(int heads, int64_t n_q, int dim, int rank, con
 }
 
 hipError_t launch_project_centres(int heads, int C, int dim, int rank, kvc_dtype cdt, const void* cent,
-                                  const float* basis, float* proj, hipStream_t st) {
+                                  const float* basis, uint16_t* tab, hipStream_t st) {
   if (heads == 0 || C == 0) return hipSuccess;
   const dim3 grid(unsigned((C * rank + 255) / 256), unsigned(heads));
   if (cdt == KVC_BF16)
     hipLaunchKernelGGL((project_centres_kernel<bf16_t>), grid, dim3(256), 0, st, static_cast<const bf16_t*>(cent),
-                       basis, C, dim, rank, proj);
+                       basis, C, dim, rank, tab);
   else
     hipLaunchKernelGGL((project_centres_kernel<float>), grid, dim3(256), 0, st, static_cast<const float*>(cent), basis,
-                       C, dim, rank, proj);
+                       C, dim, rank, tab);
+  return hipGetLastError();
+}
+
+hipError_t launch_centre_table(int heads, int C, int dim, kvc_dtype cdt, const void* cent, uint16_t* tab,
+                               hipStream_t st) {
+  if (heads == 0 || C == 0) return hipSuccess;
+  if (cdt != KVC_BF16 || dim % 4 != 0) return hipErrorInvalidValue;
+  const int64_t n_blocks = int64_t(heads) * C * dim / 4;
+  hipLaunchKernelGGL(centre_table_kernel, dim3(unsigned((n_blocks + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const uint2*>(cent), n_blocks, reinterpret_cast<uint2*>(tab));
   return hipGetLastError();
 }
 
@@ -585,8 +676,8 @@ hipError_t launch_attend_lowdim(int heads, int64_t n_q, int dim, int rank, const
   p.lse = lse;
   p.basis_v = basis_v;
   if (dim != 128) return hipErrorInvalidValue;
-  if (rank == 32) return pick_bits<32, float, true, 128>(p, segs, k_bits, v_bits, group, st);
-  if (rank == 64) return pick_bits<64, float, true, 128>(p, segs, k_bits, v_bits, group, st);
+  if (rank == 32) return pick_bits<32, true, 128>(p, segs, k_bits, v_bits, group, st);
+  if (rank == 64) return pick_bits<64, true, 128>(p, segs, k_bits, v_bits, group, st);
   return hipErrorInvalidValue;
 }
 

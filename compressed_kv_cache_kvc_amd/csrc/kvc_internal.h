@@ -26,8 +26,10 @@ struct SegDev {
   const uint8_t* v_ids;
   const void* k_cent;
   const void* v_cent;
-  const float* k_cent_proj;         // low-dim: projected centres [heads][C][rank] (workspace)
-  const float* v_cent_proj;
+  // fp16 centre tables in tile channel order [heads][C][code dim] (workspace):
+  // the centres themselves (full dim) or their projections (low dim)
+  const uint16_t* k_tab;
+  const uint16_t* v_tab;
 };
 
 struct SegList {
@@ -63,8 +65,10 @@ hipError_t launch_attend(int heads, int64_t n_q, int dim, kvc_dtype q_dtype, con
 hipError_t launch_project_queries(int heads, int64_t n_q, int dim, int rank, const void* q,
                                   const float* basis, uint16_t* q_proj, hipStream_t st);
 hipError_t launch_project_centres(int heads, int C, int dim, int rank, kvc_dtype cdt,
-                                  const void* cent, const float* basis, float* proj,
+                                  const void* cent, const float* basis, uint16_t* tab,
                                   hipStream_t st);
+hipError_t launch_centre_table(int heads, int C, int dim, kvc_dtype cdt, const void* cent,
+                               uint16_t* tab, hipStream_t st);
 hipError_t launch_attend_lowdim(int heads, int64_t n_q, int dim, int rank,
                                 const uint16_t* q_proj, const float* basis_v,
                                 const SegList& segs, int k_bits, int v_bits, int group,

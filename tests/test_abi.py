@@ -111,17 +111,24 @@ def test_attend_validation(lib):
     assert _attend(lib, [_seg(n_tokens=9360)], heads=1, n_q=256, ws=P, wsb=need - 1) == WS
 
 
+def _tables(heads, C, dim):
+    """fp16 copies of the K and V centre tables that full-dim attention stages in its workspace."""
+    return 2 * heads * C * dim * 2
+
+
 def test_split_plan_sizes(lib):
     # self-forcing-like layer: 12 heads x 19 query blocks = 228 workgroups: no split
     arr = (_lib.KvcSegment * 1)(_seg(n_tokens=9360))
-    assert lib.kvc_attend_workspace_bytes(12, 4680, 128, 1, arr, 1) == 0
+    assert lib.kvc_attend_workspace_bytes(12, 4680, 128, 1, arr, 1) == _tables(12, 16, 128)
     # 2 heads x 4 query blocks over 146 tiles: split 8 ways (64 workgroups)
     rows = 2 * 1000
     need = lib.kvc_attend_workspace_bytes(2, 1000, 128, 1, arr, 1)
-    assert need == pytest.approx(8 * rows * 128 * 4 + 8 * rows * 4, rel=1e-3)
+    assert need == pytest.approx(8 * rows * 128 * 4 + 8 * rows * 4 + _tables(2, 16, 128), rel=1e-3)
     # streaming: 720 heads fill the chip without a split
     arr = (_lib.KvcSegment * 1)(_seg(n_tokens=46800))
-    assert lib.kvc_attend_workspace_bytes(720, 4680, 128, 1, arr, 1) == 0
+    assert lib.kvc_attend_workspace_bytes(720, 4680, 128, 1, arr, 1) == _tables(720, 16, 128)
+    # fp32 queries read the fp32 centres directly and never split
+    assert lib.kvc_attend_workspace_bytes(720, 4680, 128, 0, arr, 1) == 0
 
 
 def test_lowdim_validation(lib):
