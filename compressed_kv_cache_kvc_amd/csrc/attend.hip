@@ -136,11 +136,14 @@ __device__ __forceinline__ code_t<NB> load_code_bits(const uint8_t* p) {
   }
 }
 
-// Position of key offset o (0..15) inside a 16-key chunk of the transposed V
-// tile: bits 2 and 3 swapped, matching the row order of the S^T accumulator.
-__device__ __forceinline__ int vperm(int k) {
-  const int o = k & 15;
-  return (k & ~15) | (o & 3) | ((o & 4) << 1) | ((o & 8) >> 1);
+// Transposing LDS read (ds_read_b64_tr_b16).  In each group of 16 lanes, lane
+// 4a + b receives element b of the 8 bytes addressed by lanes a, a+4, a+8, a+12
+// (as its elements 0..3): a 4x4 transpose of 16-bit values across lanes.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<uint16_t*>(p)));
+  return __builtin_bit_cast(uint2, v);
 }
 
 template <int DQ, int KB, int VB, int G, bool LOWDIM, int DOUT>
@@ -148,12 +151,14 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
   constexpr int KC = DQ / 16;     // k-chunks of the QK^T product
   constexpr int NDB = DQ / 32;    // 32-row blocks of O^T
   constexpr int ROWK = DQ + 8;    // padded LDS rows (fp16 elements)
-  constexpr int ROWV = 64 + 8;
+  // V tile rows (keys) padded so that the transposing reads of a value fragment
+  // hit 64 distinct banks: a row stride of 16 or 48 dwords modulo 64
+  constexpr int ROWV = DQ == 128 ? 160 : DQ == 64 ? 96 : 32;
   constexpr int CH = DQ / 8;      // channels per dequantizing thread
   constexpr int KNB = CH * KB / 8, VNB = CH * VB / 8;
   static_assert(G % CH == 0, "a thread's channels must sit in one group");
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][64 * ROWK];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][DQ * ROWV];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[3][64 * ROWV];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -183,8 +188,10 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
   const int64_t t_begin = T * split / p.n_split;
   const int64_t t_end = T * (split + 1) / p.n_split;
 
-  const int dk = lane;            // dequant role: token within the tile
-  const int dg = wave;            // channel group [dg*CH, dg*CH + CH)
+  // dequantization role: eight lanes per token, so that the code, metadata and
+  // centre-row loads of a wavefront cover whole rows (coalesced)
+  const int dk = (wave << 3) | (lane >> 3);   // token within the tile
+  const int dg = lane & 7;                    // channel group [dg*CH, dg*CH + CH)
 
   // a thread's centre chunk: CH fp16 values from the table, as CH/2 channel pairs
   constexpr int CWD = CH / 2;
@@ -268,7 +275,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
   auto scale2 = [](uint32_t m) { return as_h2(__builtin_amdgcn_perm(m, m, 0x01000100u)); };
   auto zero2 = [](uint32_t m) { return as_h2(__builtin_amdgcn_perm(m, m, 0x03020302u)); };
 
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int kbuf, int vbuf) {
     // keys: q*s + z in fp32 (exact but for one fp32 rounding), then one rounding of
     // the sum with the centre to fp16; the key tile's rounding error moves every
     // logit, so keys get the single-rounding form
@@ -281,7 +288,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
       const h2 c = kq.pair(j);
       kw[j] = round_add_f16x2(fmaf(float(c[0]), ks, kz), fmaf(float(c[1]), ks, kz), kcw[j]);
     }
-    uint16_t* kdst = &sK[buf][dk * ROWK + dg * CH];
+    uint16_t* kdst = &sK[kbuf][dk * ROWK + dg * CH];
     if constexpr (CH == 16) {
       reinterpret_cast<uint4*>(kdst)[0] = make_uint4(kw[0], kw[1], kw[2], kw[3]);
       reinterpret_cast<uint4*>(kdst)[1] = make_uint4(kw[4], kw[5], kw[6], kw[7]);
@@ -295,12 +302,17 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
     // error in a value moves only its own share of the output)
     const CodePairs<VB, CH> vq(vc_r);
     const h2 vs = scale2(vm_r), vz = zero2(vm_r);
-    const int vp = vperm(dk);
+    uint32_t vw[CH / 2];
 #pragma unroll
-    for (int j = 0; j < CH / 2; ++j) {
-      const uint32_t w = as_u32(__builtin_elementwise_fma(vq.pair(j), vs, vz) + as_h2(vcw[j]));
-      sV[buf][(dg * CH + 2 * j) * ROWV + vp] = static_cast<uint16_t>(w & 0xffffu);
-      sV[buf][(dg * CH + 2 * j + 1) * ROWV + vp] = static_cast<uint16_t>(w >> 16);
+    for (int j = 0; j < CH / 2; ++j) vw[j] = as_u32(__builtin_elementwise_fma(vq.pair(j), vs, vz) + as_h2(vcw[j]));
+    uint16_t* vdst = &sV[vbuf][dk * ROWV + dg * CH];
+    if constexpr (CH == 16) {
+      reinterpret_cast<uint4*>(vdst)[0] = make_uint4(vw[0], vw[1], vw[2], vw[3]);
+      reinterpret_cast<uint4*>(vdst)[1] = make_uint4(vw[4], vw[5], vw[6], vw[7]);
+    } else if constexpr (CH == 8) {
+      reinterpret_cast<uint4*>(vdst)[0] = make_uint4(vw[0], vw[1], vw[2], vw[3]);
+    } else {
+      reinterpret_cast<uint2*>(vdst)[0] = make_uint2(vw[0], vw[1]);
     }
   };
 
@@ -313,48 +325,25 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
     for (int v = 0; v < 16; ++v) o[b][v] = 0.f;
 
   auto clamp_t = [&](int64_t t) { return t < t_end ? t : t_end - 1; };
-  Cursor cur_ids, cur_data, cur_comp;
-  if (t_begin < t_end) {
-    cursor_load(cur_data, 0);
-    cursor_seek(cur_data, t_begin);
-    cur_ids = cur_data;
-    cur_comp = cur_data;
-    int k0, v0;
-    load_ids(cur_data, t_begin, k0, v0);
-    load_data(cur_data, t_begin, k0, v0);
-    cursor_seek(cur_ids, clamp_t(t_begin + 1));
-    load_ids(cur_ids, clamp_t(t_begin + 1), kid_n, vid_n);
-    store_tile(0);
-  }
-  __syncthreads();
 
-  for (int64_t t = t_begin; t < t_end; ++t) {
-    const int buf = int((t - t_begin) & 1);
-    // issue the loads of tile t+1 (data) and t+2 (ids), clamped to the last tile so
-    // that they are unconditional; they are consumed after the compute
-    {
-      const int64_t t1 = clamp_t(t + 1), t2 = clamp_t(t + 2);
-      cursor_seek(cur_data, t1);
-      load_data(cur_data, t1, kid_n, vid_n);
-      cursor_seek(cur_ids, t2);
-      load_ids(cur_ids, t2, kid_n, vid_n);
-    }
-    cursor_seek(cur_comp, t);
-    const int nvalid_left = cur_comp.n_tokens - int(t - cur_comp.tile_begin) * 64;
-    const int nvalid = nvalid_left >= 64 ? 64 : nvalid_left;
-
-    // S^T = K_hat Q^T for keys [0, 32) and [32, 64)
-    f32x16 sacc[2];
+  // S^T = K_hat Q^T of the K tile in buffer kb_, keys [0, 32) and [32, 64)
+  auto qk = [&](int kb_, f32x16 (&sacc)[2]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const f16x8 a = as_f16x8(*reinterpret_cast<const uint4*>(&sK[buf][(kb * 32 + col) * ROWK + kc * 16 + half * 8]));
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const f16x8 a = as_f16x8(*reinterpret_cast<const uint4*>(&sK[kb_][(kb * 32 + col) * ROWK + kc * 16 + half * 8]));
         sacc[kb] = mfma32h(a, qf[kc], sacc[kb]);
       }
-    }
+  };
+
+  // mask the keys past the end of the segment, raise the reference maximum when
+  // the tile exceeds it by more than 2^8 (rescaling the output accumulator)
+  auto softmax_prep = [&](f32x16 (&sacc)[2], int nvalid) {
     if (nvalid < 64) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -369,8 +358,9 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * p.scale_log2;
-    // raise the reference maximum only when the tile exceeds it by more than 2^8
+    // the other half of the row sits in lane l ^ 32
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2;
     const bool raise = mx > m_run + 8.f;
     if (__any(raise)) {
       const float m_new = raise ? mx : m_run;
@@ -382,38 +372,155 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[b][v] *= alpha;
     }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[kb][v] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v], p.scale_log2, -m_run));
+  };
 
-    // probabilities in fp16; the row sum is taken over the same rounded values
-    f16x8 pf[4];
+  // Software pipeline over tiles: while tile t's exponentials are computed the
+  // matrix cores already form tile t+1's scores, and while tile t's values are
+  // multiplied tile t+2 is dequantized.  K tiles t+1, t+2 live in two buffers and
+  // V tiles t, t+1, t+2 in three; one barrier per tile publishes tile t+2.
+  Cursor cur_ids, cur_data, cur_comp;
+  f32x16 sa[2], sb[2];
+  if (t_begin < t_end) {
+    cursor_load(cur_data, 0);
+    cursor_seek(cur_data, t_begin);
+    cur_ids = cur_data;
+    cur_comp = cur_data;
+    int k0, v0;
+    load_ids(cur_data, t_begin, k0, v0);
+    load_data(cur_data, t_begin, k0, v0);
+    cursor_seek(cur_ids, clamp_t(t_begin + 1));
+    load_ids(cur_ids, clamp_t(t_begin + 1), kid_n, vid_n);
+    store_tile(0, 0);
+    cursor_seek(cur_data, clamp_t(t_begin + 1));
+    load_data(cur_data, clamp_t(t_begin + 1), kid_n, vid_n);
+    cursor_seek(cur_ids, clamp_t(t_begin + 2));
+    load_ids(cur_ids, clamp_t(t_begin + 2), kid_n, vid_n);
+    store_tile(1, 1);
+  }
+  __syncthreads();
+  if (t_begin < t_end) qk(0, sa);
+
+  int vbuf = 0;                     // V buffer of tile t; tile t+2 goes to (vbuf + 2) % 3
+  constexpr int NQK = 2 * KC;       // score products per tile
+  constexpr int NPV = 4 * NDB;      // value products per tile
+  constexpr int PPM = 16 / NQK;     // exponential pairs between two score products
+  static_assert(16 % NQK == 0 && CH % NPV == 0, "work per product");
+  constexpr int IPM = CH / NPV;     // dequantization pairs between two value products
+
+  // One tile step.  The matrix products of the step (tile t+1's scores, then tile
+  // t's values) are issued one at a time, each followed by its share of the vector
+  // work (tile t's exponentials, then tile t+2's dequantization) and preceded two
+  // products earlier by the LDS read of its operand; scheduling fences keep this
+  // order, so the matrix cores and the vector unit work side by side.
+  auto step = [&](int64_t t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    const int kbuf = int((t - t_begin) & 1);
+    auto frag = [&](int f) -> f16x8 {
+      if (f < NQK) {          // K fragment: keys (f & 1)*32 + col, channels (f >> 1)*16 + half*8
+        return as_f16x8(*reinterpret_cast<const uint4*>(
+            &sK[kbuf ^ 1][((f & 1) * 32 + col) * ROWK + (f >> 1) * 16 + half * 8]));
+      }
+      // V^T fragment for product i = f - NQK: dims (i % NDB)*32 + [0, 32), keys of
+      // chunk i / NDB in the order of the probabilities (bits 2 and 3 of the key
+      // offset swapped), read from the row-major V tile with two transposing
+      // loads: lane s supplies key row 8*half_call + 4*(s >> 5) + ((s >> 2) & 3) of
+      // the chunk and four dims from 16*((s >> 4) & 1) + 4*(s & 3); the hardware
+      // hands lane l the four keys of its dim l % 32
+      const int i = f - NQK;
+      const uint16_t* base = &sV[vbuf][((i / NDB) * 16 + 4 * (lane >> 5) + ((lane >> 2) & 3)) * ROWV +
+                                       (i % NDB) * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)];
+      const uint2 lo = lds_read_tr16(base), hi = lds_read_tr16(base + 8 * ROWV);
+      return as_f16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+    };
+    f16x8 fr[3];
+    fr[0] = frag(0);
+    fr[1] = frag(1);
+    {
+      const int64_t t2 = clamp_t(t + 2), t3 = clamp_t(t + 3);
+      cursor_seek(cur_data, t2);
+      load_data(cur_data, t2, kid_n, vid_n);
+      cursor_seek(cur_ids, t3);
+      load_ids(cur_ids, t3, kid_n, vid_n);
+    }
+    cursor_seek(cur_comp, t);
+    const int nvalid_left = cur_comp.n_tokens - int(t - cur_comp.tile_begin) * 64;
+    softmax_prep(cur, nvalid_left >= 64 ? 64 : nvalid_left);
+
+    // tile t's exponentials, one pair of scores at a time, as fp16 probabilities;
+    // the row sum is taken over the same rounded values
+    uint32_t pw[16];
     float psum = 0.f;
     const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int kb = c / 2, base = 8 * (c % 2);
-      uint32_t w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        w[i] = pack_f16x2(sacc[kb][base + 2 * i], sacc[kb][base + 2 * i + 1]);
-        psum = __builtin_amdgcn_fdot2(as_h2(w[i]), ones, psum, false);
+    auto exp_pair = [&](int k) {
+      const int kb = k >> 3, v = 2 * (k & 7);
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(cur[kb][v], p.scale_log2, -m_run));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(cur[kb][v + 1], p.scale_log2, -m_run));
+      pw[k] = pack_f16x2(e0, e1);
+      psum = __builtin_amdgcn_fdot2(as_h2(pw[k]), ones, psum, false);
+    };
+    f16x8 pf[4];
+
+    // tile t+2's dequantization, one channel pair at a time: item j < CH/2 is key
+    // pair j (keys: one rounding of fp32 q*s + z plus the centre), item CH/2 + j
+    // value pair j (packed fp16)
+    const int vstore = vbuf == 0 ? 2 : vbuf - 1;
+    uint32_t kw[CH / 2], vw[CH / 2];
+    auto dq_item = [&](int j, const CodePairs<KB, CH>& kq, float ks, float kz, const CodePairs<VB, CH>& vq, h2 vs,
+                       h2 vz) {
+      if (j < CH / 2) {
+        const h2 c = kq.pair(j);
+        kw[j] = round_add_f16x2(fmaf(float(c[0]), ks, kz), fmaf(float(c[1]), ks, kz), kcw[j]);
+        uint16_t* kdst = &sK[kbuf][dk * ROWK + dg * CH];
+        if constexpr (CH == 4) {
+          if (j == 1) reinterpret_cast<uint2*>(kdst)[0] = make_uint2(kw[0], kw[1]);
+        } else if ((j & 3) == 3) {
+          reinterpret_cast<uint4*>(kdst)[j >> 2] = make_uint4(kw[j - 3], kw[j - 2], kw[j - 1], kw[j]);
+        }
+      } else {
+        const int jj = j - CH / 2;
+        vw[jj] = as_u32(__builtin_elementwise_fma(vq.pair(jj), vs, vz) + as_h2(vcw[jj]));
+        uint16_t* vdst = &sV[vstore][dk * ROWV + dg * CH];
+        if constexpr (CH == 4) {
+          if (jj == 1) reinterpret_cast<uint2*>(vdst)[0] = make_uint2(vw[0], vw[1]);
+        } else if ((jj & 3) == 3) {
+          reinterpret_cast<uint4*>(vdst)[jj >> 2] = make_uint4(vw[jj - 3], vw[jj - 2], vw[jj - 1], vw[jj]);
+        }
       }
-      pf[c] = as_f16x8(make_uint4(w[0], w[1], w[2], w[3]));
+    };
+
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      fr[(i + 2) % 3] = frag(i + 2);
+      if (i < 2)
+        nxt[i] = mfma32h(fr[i % 3], qf[0], f32x16{});
+      else
+        nxt[i & 1] = mfma32h(fr[i % 3], qf[i >> 1], nxt[i & 1]);
+#pragma unroll
+      for (int u = 0; u < PPM; ++u) exp_pair(i * PPM + u);
+      __builtin_amdgcn_sched_barrier(0);
     }
     l_run += psum;
-
 #pragma unroll
-    for (int b = 0; b < NDB; ++b)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f16x8 a = as_f16x8(*reinterpret_cast<const uint4*>(&sV[buf][(b * 32 + col) * ROWV + c * 16 + half * 8]));
-        o[b] = mfma32h(a, pf[c], o[b]);
-      }
+    for (int c = 0; c < 4; ++c) pf[c] = as_f16x8(make_uint4(pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]));
 
-    store_tile(buf ^ 1);           // the last iteration writes a spare copy nobody reads
+    const CodePairs<KB, CH> kq(kc_r);
+    const h2 kmh = as_h2(km_r);
+    const float ks = float(kmh[0]), kz = float(kmh[1]);
+    const CodePairs<VB, CH> vq(vc_r);
+    const h2 vs = scale2(vm_r), vz = zero2(vm_r);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      if (NQK + i + 2 < NQK + NPV) fr[(NQK + i + 2) % 3] = frag(NQK + i + 2);
+      o[i % NDB] = mfma32h(fr[(NQK + i) % 3], pf[i / NDB], o[i % NDB]);
+#pragma unroll
+      for (int u = 0; u < IPM; ++u) dq_item(i * IPM + u, kq, ks, kz, vq, vs, vz);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    vbuf = vbuf == 2 ? 0 : vbuf + 1;
     __syncthreads();
+  };
+  for (int64_t t = t_begin; t < t_end; t += 2) {
+    step(t, sa, sb);
+    if (t + 1 < t_end) step(t + 1, sb, sa);
   }
 
   // epilogue: normalise, write this split's (out, lse)
