@@ -39,6 +39,9 @@ def parse():
                     choices=["self_forcing_layer", "long_history", "larger_backbone", "streaming", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before the warmup, run one plain fp32 negation of MIB MiB (reads and writes MIB MiB) so "
+                         "that a hardware-counter run can scale its byte counters against a kernel of known traffic")
     return ap.parse_args()
 
 
@@ -254,62 +257,89 @@ def make_workload(cfg, dev):
 
 # ------------------------------------------------------------------------------ CPU oracle baseline
 def cpu_baseline(cfg, budget_s):
-    """Time the oracle (as it stands) on a bounded sample of the workload: one
-    head's attention over the full history for as many queries as fit the
-    budget, extrapolated to the workload's unit (TFLOP/s)."""
+    """Time the oracle (as it stands) on a bounded sample of the workload: the
+    fp64 attention of all queries over the history, head after head, until the
+    time budget is spent or every sampled head is done (at most 16 heads are
+    generated).  The codes come from the oracle's own encoder (timed too) with
+    centres drawn from the tokens; ids from the expanded distance."""
     import numpy as np
     import torch
     import oracle
     import synth
     from threadpoolctl import threadpool_info
 
-    H1 = 1
     N = cfg.chunk if cfg.name == "streaming" else (cfg.recent if cfg.name == "larger_backbone" else cfg.hist)
+    H = min(cfg.heads, 16)
     if cfg.dtype == "f32":
         k, _ = synth.tiny_kv(cfg, "k")
         v, _ = synth.tiny_kv(cfg, "v")
     else:
-        k = synth.AR1Stream(cfg, "k", heads=H1).tokens(N)
-        v = synth.AR1Stream(cfg, "v", heads=H1).tokens(N)
-    kn, vn = k[0].float().numpy(), v[0].float().numpy()
+        k = synth.AR1Stream(cfg, "k", heads=H).tokens(N)
+        v = synth.AR1Stream(cfg, "v", heads=H).tokens(N)
+    q_all = synth.queries(cfg, heads=H)
+    H = min(H, k.shape[0])
     C = cfg.n_centroids
     rng = np.random.default_rng(cfg.seed)
-    kc = kn[rng.choice(N, C, replace=False)]
-    vc = vn[rng.choice(N, C, replace=False)]
-    # the encode leg: ids from the expanded distance (input preparation), codes by the oracle
+
     def ids_of(x, c):
         xt, ct = torch.from_numpy(x.astype(np.float64)), torch.from_numpy(c.astype(np.float64))
         return ((ct * ct).sum(1)[None] - 2 * xt @ ct.T).argmin(1).numpy()
-    kid, vid = ids_of(kn, kc), ids_of(vn, vc)
-    t0 = time.perf_counter()
-    n_enc = min(N, 4096)
-    kcodes, kmeta = oracle.encode(kn[:n_enc], kc, kid[:n_enc], cfg.k_bits, cfg.group)
-    vcodes, vmeta = oracle.encode(vn[:n_enc], vc, vid[:n_enc], cfg.v_bits, cfg.group)
-    t_enc = time.perf_counter() - t0
-    kcodes, kmeta = oracle.encode(kn, kc, kid, cfg.k_bits, cfg.group)
-    vcodes, vmeta = oracle.encode(vn, vc, vid, cfg.v_bits, cfg.group)
-    seg = oracle.Segment(kcodes, kmeta, kid, kc, vcodes, vmeta, vid, vc, cfg.k_bits, cfg.v_bits, cfg.group)
-    q = synth.queries(cfg, heads=1)[0].float().numpy()
-    # calibrate on 32 queries, then run as many as the budget allows
-    t0 = time.perf_counter()
-    oracle.attend(q[:32], [seg])
-    per_q = (time.perf_counter() - t0) / 32
-    nq = int(max(32, min(len(q), budget_s / max(per_q, 1e-9))))
-    t0 = time.perf_counter()
-    oracle.attend(q[:nq], [seg])
-    t_att = time.perf_counter() - t0
-    flops = 4.0 * nq * N * cfg.dim
+
+    t_att = t_enc = 0.0
+    flops = 0.0
+    n_enc = heads_done = nq_total = 0
+    wall0 = time.perf_counter()
+    for h in range(H):
+        if h > 0 and time.perf_counter() - wall0 > budget_s:
+            break
+        kn, vn = k[h].float().numpy(), v[h].float().numpy()
+        kc = kn[rng.choice(N, min(C, N), replace=False)]
+        vc = vn[rng.choice(N, min(C, N), replace=False)]
+        kid, vid = ids_of(kn, kc), ids_of(vn, vc)
+        t0 = time.perf_counter()
+        kcodes, kmeta = oracle.encode(kn, kc, kid, cfg.k_bits, cfg.group)
+        vcodes, vmeta = oracle.encode(vn, vc, vid, cfg.v_bits, cfg.group)
+        t_enc += time.perf_counter() - t0
+        n_enc += 2 * N
+        seg = oracle.Segment(kcodes, kmeta, kid, kc, vcodes, vmeta, vid, vc, cfg.k_bits, cfg.v_bits, cfg.group)
+        q = q_all[h].float().numpy()
+        t0 = time.perf_counter()
+        oracle.attend(q, [seg])
+        t_att += time.perf_counter() - t0
+        flops += 4.0 * len(q) * N * cfg.dim
+        nq_total += len(q)
+        heads_done += 1
     threads = 1
     for info in threadpool_info():
         threads = max(threads, int(info.get("num_threads", 1)))
     return {
         "value": flops / t_att / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-        "sample": f"fp64 attention of 1 head, {nq} queries x {N} history tokens (d={cfg.dim}); "
-                  f"encode of {n_enc} tokens x 2 tensors",
-        "encode_tokens_per_s": n_enc / t_enc,
+        "sample": f"fp64 attention of {heads_done} head(s) x {nq_total // max(heads_done, 1)} queries x {N} "
+                  f"history tokens (d={cfg.dim}); oracle encode of the same heads' K and V ({n_enc} token rows)",
+        "encode_tokens_per_s": n_enc / t_enc if t_enc > 0 else None,
         "seconds": t_att + t_enc,
         "cpu_count_affinity": len(os.sched_getaffinity(0)),
     }
+
+
+def measured_traffic(workload):
+    """HBM bytes per attention launch from the committed counter summary of this
+    workload (FETCH_SIZE + WRITE_SIZE, scaled against a copy of known size), or
+    None when there is none or the attention source has changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_attend_kernel_{workload}.md")
+    src = os.path.join(ROOT, "compressed_kv_cache_kvc_amd", "csrc", "attend.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("attend.hip sha256") != sha or "traffic bytes per launch" not in fields:
+        return None
+    return int(float(fields["traffic bytes per launch"]))
 
 
 # ------------------------------------------------------------------------------ main
@@ -330,6 +360,12 @@ def main():
     cfg = synth.get_config(args.workload)
     w = make_workload(cfg, dev)
     torch.cuda.synchronize()
+    if args.copy_calibration > 0:
+        src = torch.ones(args.copy_calibration * (1 << 18), dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         w.step()
@@ -364,7 +400,7 @@ def main():
         launches = 1
     achieved = fl / launches / (attend_ms / launches * 1e-3) / 1e12 if attend_ms > 0 else 0.0
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_MFMA_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_MFMA_TFLOPS, 4), "traffic": measured_traffic(cfg.name),
                 "kernel": "attend_kernel", "flops_per_launch": fl / launches,
                 "avg_launch_ms": attend_ms / launches}
     enc_s = encode_ms * 1e-3
