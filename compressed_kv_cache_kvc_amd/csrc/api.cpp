@@ -186,9 +186,11 @@ const char* kvc_version(void) { return "kvc 0.1.0 (gfx950)"; }
 
 // ------------------------------------------------------------------------------ fit / assign
 size_t kvc_fit_assign_workspace_bytes(int32_t heads, int64_t n_tokens, int32_t dim, int32_t n_centroids) {
-  (void)n_tokens; (void)dim;
+  (void)dim;
   if (heads <= 0 || n_centroids <= 0) return 0;
-  return align_up(size_t(heads) * size_t(n_centroids) * 4);  // centre norms
+  // centre norms, then the member lists of the centre update
+  return align_up(size_t(heads) * size_t(n_centroids) * 4) +
+         align_up(kvc::kmeans_update_workspace(heads, n_tokens > 0 ? n_tokens : 0, n_centroids));
 }
 
 kvc_status kvc_fit_assign(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt, const void* x,
@@ -215,7 +217,9 @@ kvc_status kvc_fit_assign(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtyp
       e = kvc::launch_assign(heads, n_tokens, dim, dt, x, n_centroids, centroids, norms, ids_out, stream);
       if (e != hipSuccess) return hip_status(e, "assign");
       if (it == n_iters) break;
-      e = kvc::launch_kmeans_update(heads, n_tokens, dim, dt, x, n_centroids, centroids, ids_out, stream);
+      e = kvc::launch_kmeans_update(heads, n_tokens, dim, dt, x, n_centroids, centroids, ids_out,
+                                    static_cast<char*>(ws) + align_up(size_t(heads) * size_t(n_centroids) * 4),
+                                    stream);
       if (e != hipSuccess) return hip_status(e, "k-means update");
     }
     return ok();
@@ -227,8 +231,9 @@ kvc_status kvc_fit_assign(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtyp
 // ------------------------------------------------------------------------------ encode
 size_t kvc_encode_workspace_bytes(int32_t heads, int64_t n_tokens, int32_t dim, int32_t n_centroids,
                                   int32_t ids_given) {
-  if (ids_given) return 0;
-  return kvc_fit_assign_workspace_bytes(heads, n_tokens, dim, n_centroids);
+  (void)n_tokens; (void)dim;
+  if (ids_given || heads <= 0 || n_centroids <= 0) return 0;
+  return align_up(size_t(heads) * size_t(n_centroids) * 4);   // centre norms of the assignment
 }
 
 kvc_status kvc_encode(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt, const void* x,

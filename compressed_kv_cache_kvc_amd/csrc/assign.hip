@@ -242,114 +242,132 @@ __device__ __forceinline__ uint32_t f64_to_bits_rne(double d) {
   return (sign << SIGN_SHIFT) | bits;
 }
 
-// One wavefront per (head, CPW consecutive centres).  The ids are scanned in
-// chunks of 1024 tokens (16 consecutive tokens per lane); the members of the
-// wave's centres are listed in token order in LDS through a prefix sum over the
-// lanes, then their rows are added in fp64, eight row loads in flight at a time.
-// The order of the additions is fixed, so the result is deterministic; each
-// centre becomes the mean (one fp64 division) rounded to nearest even in the
-// storage type, and a centre without members keeps its value.
-template <typename T, int D, int CPW>
-__global__ __launch_bounds__(256) void kmeans_update_kernel(const T* __restrict__ x, T* __restrict__ cent,
-                                                            const uint8_t* __restrict__ ids, int C, int64_t n) {
-  constexpr int PER = D / 64;                 // channels per lane
-  constexpr int BATCH = 8;
-  static_assert(CPW <= 16, "centre offsets are stored in 4 bits");
-  __shared__ uint32_t s_list[4][1024];        // per wave: (token in chunk << 4) | centre offset
-  const int lane = threadIdx.x % 64;
-  const int wave = threadIdx.x / 64;
-  const int c0 = (blockIdx.x * 4 + wave) * CPW;
+// Member lists of the centres, in token order.  The ids of a head are taken in
+// chunks of kListChunk tokens, one workgroup of 256 threads per (chunk, head):
+// thread t counts, per centre, the ids of its kListChunk/256 consecutive tokens
+// (16-bit counts, [centre][thread] in LDS); an exclusive scan over (centre,
+// thread) in that order gives each thread its first slot per centre, and a second
+// pass over the same tokens writes their offsets inside the chunk.  Centre c's
+// members of chunk k are then list[k*kListChunk + off[k][c] ... off[k][c+1]), in
+// increasing token order (a stable counting sort).
+__global__ __launch_bounds__(256) void member_lists_kernel(const uint8_t* __restrict__ ids, int64_t n, int C,
+                                                           uint32_t* __restrict__ off, uint16_t* __restrict__ list) {
+  __shared__ __attribute__((aligned(16))) uint16_t cnt[256 * 256];   // [centre][thread]
+  __shared__ uint32_t base[257];
+  const int t = threadIdx.x;
+  const int k = blockIdx.x;
   const int h = blockIdx.y;
-  if (c0 >= C) return;                        // wave-uniform; the kernel has no block barrier
-  const uint8_t* idh = ids + int64_t(h) * n;
-  const T* xh = x + int64_t(h) * n * D;
-  double acc[CPW][PER];
-  int cnt[CPW];
+  const int64_t nk = (n + kListChunk - 1) / kListChunk;
+  const int64_t c0 = int64_t(k) * kListChunk;
+  const int len = int(n - c0 < kListChunk ? n - c0 : kListChunk);
+  const int L = (len + 255) / 256;
+  const int j0 = t * L < len ? t * L : len;
+  const int j1 = j0 + L < len ? j0 + L : len;
+  const uint8_t* idk = ids + int64_t(h) * n + c0;
+  for (int i = t; i < 256 * 256 / 8; i += 256) reinterpret_cast<uint4*>(cnt)[i] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+  for (int j = j0; j < j1; ++j) ++cnt[int(idk[j]) * 256 + t];
+  __syncthreads();
+  // row c: exclusive prefix over the threads, row total to base[c]
+  if (t < C) {
+    uint32_t run = 0;
+    uint4* row = reinterpret_cast<uint4*>(&cnt[t * 256]);
+    for (int i = 0; i < 32; ++i) {
+      uint4 w = row[i];
+      uint32_t* pw = reinterpret_cast<uint32_t*>(&w);
 #pragma unroll
-  for (int k = 0; k < CPW; ++k) {
-    cnt[k] = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) acc[k][i] = 0.0;
-  }
-  uint32_t* list = s_list[wave];
-  for (int64_t j0 = 0; j0 < n; j0 += 1024) {
-    uint32_t m = 0;                           // members among this lane's 16 tokens
-    uint64_t sel = 0;                         // their centre offsets, 4 bits each
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int64_t j = j0 + 16 * lane + k;
-      const int d = j < n ? int(idh[j]) - c0 : -1;
-      if (d >= 0 && d < CPW) {
-        m |= 1u << k;
-        sel |= uint64_t(d) << (4 * k);
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = pw[q] & 0xffffu, hi = pw[q] >> 16;
+        pw[q] = run | ((run + lo) << 16);
+        run += lo + hi;
       }
+      row[i] = w;
     }
-    // exclusive prefix of the member counts over the lanes (token order is lane-major)
-    const int own = __popc(m);
-    int pre = own;
+    base[t] = run;
+  }
+  __syncthreads();
+  if (t == 0) {   // exclusive scan of the row totals (at most 256 additions)
+    uint32_t run = 0;
+    for (int c = 0; c < C; ++c) {
+      const uint32_t v = base[c];
+      base[c] = run;
+      run += v;
+    }
+    base[C] = run;
+  }
+  __syncthreads();
+  uint32_t* offk = off + (int64_t(h) * nk + k) * (C + 1);
+  for (int c = t; c <= C; c += 256) offk[c] = base[c];
+  uint16_t* lk = list + int64_t(h) * n + c0;
+  for (int j = j0; j < j1; ++j) {
+    const int c = idk[j];
+    const uint32_t slot = base[c] + cnt[c * 256 + t]++;
+    lk[slot] = static_cast<uint16_t>(j);
+  }
+}
+
+// One wavefront per (head, centre): the members' rows are added in fp64 in token
+// order (chunk by chunk, each member list in increasing order), BATCH row loads
+// in flight at a time.  The order of the additions is fixed, so the result is
+// deterministic; the centre becomes the mean (one fp64 division) rounded to
+// nearest even in the storage type, and a centre without members keeps its value.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void kmeans_update_kernel(const T* __restrict__ x, T* __restrict__ cent,
+                                                            const uint32_t* __restrict__ off,
+                                                            const uint16_t* __restrict__ list, int C, int64_t n) {
+  constexpr int PER = D / 64;                 // channels per lane
+  constexpr int BATCH = 16;
+  const int lane = threadIdx.x % 64;
+  const int c = blockIdx.x * 4 + threadIdx.x / 64;
+  const int h = blockIdx.y;
+  if (c >= C) return;                         // wave-uniform; the kernel has no block barrier
+  const int64_t nk = (n + kListChunk - 1) / kListChunk;
+  const T* xh = x + int64_t(h) * n * D + lane * PER;
+  double acc[PER];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(pre, off, 64);
-      if (lane >= off) pre += t;
-    }
-    const int total = __shfl(pre, 63, 64);
-    int pos = pre - own;
-    uint32_t mm = m;
-    while (mm) {
-      const int k = __builtin_ctz(mm);
-      mm &= mm - 1;
-      list[pos++] = (uint32_t(16 * lane + k) << 4) | uint32_t((sel >> (4 * k)) & 15u);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (int b0 = 0; b0 < total; b0 += BATCH) {
-      uint32_t e[BATCH];
-      float v[BATCH][PER];
+  for (int i = 0; i < PER; ++i) acc[i] = 0.0;
+  int cnt = 0;
+  for (int64_t k = 0; k < nk; ++k) {
+    const uint32_t* offk = off + (int64_t(h) * nk + k) * (C + 1);
+    const int lo = int(offk[c]), hi = int(offk[c + 1]);
+    const uint16_t* lk = list + int64_t(h) * n + k * kListChunk;
+    const T* xk = xh + k * kListChunk * D;
+    cnt += hi - lo;
+    for (int s0 = lo; s0 < hi; s0 += 64) {
+      const int m = hi - s0 < 64 ? hi - s0 : 64;
+      const int mine = s0 + lane < hi ? int(lk[s0 + lane]) : 0;   // member s0 + lane of the list
+      for (int u0 = 0; u0 < m; u0 += BATCH) {
+        float v[BATCH][PER];
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        e[u] = __builtin_amdgcn_readfirstlane(b0 + u < total ? list[b0 + u] : 0u);
-        const T* row = xh + (j0 + (e[u] >> 4)) * D;
-        if (b0 + u < total) {
+        for (int u = 0; u < BATCH; ++u) {
+          const int j = __builtin_amdgcn_readlane(mine, u0 + u < m ? u0 + u : 0);
+          const T* row = xk + int64_t(j) * D;
 #pragma unroll
           for (int i = 0; i < PER; ++i) {
             if constexpr (sizeof(T) == 2)
-              v[u][i] = __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(row)[lane * PER + i]) << 16);
+              v[u][i] = __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(row)[i]) << 16);
             else
-              v[u][i] = reinterpret_cast<const float*>(row)[lane * PER + i];
+              v[u][i] = reinterpret_cast<const float*>(row)[i];
           }
         }
-      }
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        if (b0 + u < total) {
-          const int ci = int(e[u] & 15u);
+        for (int u = 0; u < BATCH; ++u)
+          if (u0 + u < m) {
 #pragma unroll
-          for (int k = 0; k < CPW; ++k) {
-            if (k == ci) {
-              ++cnt[k];
-#pragma unroll
-              for (int i = 0; i < PER; ++i) acc[k][i] = __dadd_rn(acc[k][i], double(v[u][i]));
-            }
+            for (int i = 0; i < PER; ++i) acc[i] = __dadd_rn(acc[i], double(v[u][i]));
           }
-        }
       }
     }
-    __builtin_amdgcn_wave_barrier();          // the list is rewritten by the next chunk
   }
+  if (cnt == 0) return;                       // empty cluster keeps its centre
+  T* dst = cent + (int64_t(h) * C + c) * D + lane * PER;
 #pragma unroll
-  for (int k = 0; k < CPW; ++k) {
-    const int c = c0 + k;
-    if (c >= C || cnt[k] == 0) continue;      // empty cluster keeps its centre
-    T* dst = cent + (int64_t(h) * C + c) * D;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const double mean = __ddiv_rn(acc[k][i], double(cnt[k]));
-      if constexpr (sizeof(T) == 2)
-        reinterpret_cast<uint16_t*>(dst)[lane * PER + i] = static_cast<uint16_t>(f64_to_bits_rne<8>(mean));
-      else
-        reinterpret_cast<uint32_t*>(dst)[lane * PER + i] = f64_to_bits_rne<24>(mean);
-    }
+  for (int i = 0; i < PER; ++i) {
+    const double mean = __ddiv_rn(acc[i], double(cnt));
+    if constexpr (sizeof(T) == 2)
+      reinterpret_cast<uint16_t*>(dst)[i] = static_cast<uint16_t>(f64_to_bits_rne<8>(mean));
+    else
+      reinterpret_cast<uint32_t*>(dst)[i] = f64_to_bits_rne<24>(mean);
   }
 }
 
@@ -404,30 +422,34 @@ hipError_t launch_assign(int heads, int64_t n, int dim, kvc_dtype dt, const void
   return hipGetLastError();
 }
 
-template <typename T, int D, int CPW>
+template <typename T, int D>
 hipError_t run_kmeans_update(int heads, int64_t n, const void* x, int C, void* cent, const uint8_t* ids,
-                             hipStream_t st) {
-  const dim3 grid(unsigned((C + 4 * CPW - 1) / (4 * CPW)), unsigned(heads));
-  hipLaunchKernelGGL((kmeans_update_kernel<T, D, CPW>), grid, dim3(256), 0, st, static_cast<const T*>(x),
-                     static_cast<T*>(cent), ids, C, n);
+                             uint32_t* off, uint16_t* list, hipStream_t st) {
+  const int64_t nk = (n + kListChunk - 1) / kListChunk;
+  hipLaunchKernelGGL(member_lists_kernel, dim3(unsigned(nk), unsigned(heads)), dim3(256), 0, st, ids, n, C, off,
+                     list);
+  hipLaunchKernelGGL((kmeans_update_kernel<T, D>), dim3(unsigned((C + 3) / 4), unsigned(heads)), dim3(256), 0, st,
+                     static_cast<const T*>(x), static_cast<T*>(cent), off, list, C, n);
   return hipGetLastError();
 }
 
-template <typename T, int D>
-hipError_t pick_cpw(int heads, int64_t n, const void* x, int C, void* cent, const uint8_t* ids, hipStream_t st) {
-  // one centre per wavefront while that gives at most ~16k wavefronts; beyond
-  // that, eight centres share a wavefront and its scan of the ids
-  if (int64_t(heads) * C <= 16384) return run_kmeans_update<T, D, 1>(heads, n, x, C, cent, ids, st);
-  return run_kmeans_update<T, D, 8>(heads, n, x, C, cent, ids, st);
+size_t kmeans_update_workspace(int heads, int64_t n, int C) {
+  const int64_t nk = (n + kListChunk - 1) / kListChunk;
+  const size_t a = (size_t(heads) * size_t(nk) * size_t(C + 1) * 4 + 255) & ~size_t(255);
+  return a + size_t(heads) * size_t(n) * 2;
 }
 
 hipError_t launch_kmeans_update(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C, void* cent,
-                                const uint8_t* ids, hipStream_t st) {
+                                const uint8_t* ids, void* ws, hipStream_t st) {
   if (heads == 0 || n == 0) return hipSuccess;
-  if (dt == KVC_BF16 && dim == 128) return pick_cpw<bf16_t, 128>(heads, n, x, C, cent, ids, st);
-  if (dt == KVC_BF16 && dim == 64) return pick_cpw<bf16_t, 64>(heads, n, x, C, cent, ids, st);
-  if (dt == KVC_F32 && dim == 128) return pick_cpw<float, 128>(heads, n, x, C, cent, ids, st);
-  if (dt == KVC_F32 && dim == 64) return pick_cpw<float, 64>(heads, n, x, C, cent, ids, st);
+  const int64_t nk = (n + kListChunk - 1) / kListChunk;
+  auto* off = static_cast<uint32_t*>(ws);
+  auto* list = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) +
+                                           ((size_t(heads) * size_t(nk) * size_t(C + 1) * 4 + 255) & ~size_t(255)));
+  if (dt == KVC_BF16 && dim == 128) return run_kmeans_update<bf16_t, 128>(heads, n, x, C, cent, ids, off, list, st);
+  if (dt == KVC_BF16 && dim == 64) return run_kmeans_update<bf16_t, 64>(heads, n, x, C, cent, ids, off, list, st);
+  if (dt == KVC_F32 && dim == 128) return run_kmeans_update<float, 128>(heads, n, x, C, cent, ids, off, list, st);
+  if (dt == KVC_F32 && dim == 64) return run_kmeans_update<float, 64>(heads, n, x, C, cent, ids, off, list, st);
   return hipErrorInvalidValue;
 }
 

@@ -47,8 +47,12 @@ hipError_t launch_centroid_norms(int heads, int C, int dim, kvc_dtype dt, const 
                                  float* norms, hipStream_t st);
 hipError_t launch_assign(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C,
                          const void* cent, const float* norms, uint8_t* ids, hipStream_t st);
+// k-means update (member lists + per-centre means); ws holds
+// kmeans_update_workspace(heads, n, C) bytes, 256-byte aligned.
 hipError_t launch_kmeans_update(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C,
-                                void* cent, const uint8_t* ids, hipStream_t st);
+                                void* cent, const uint8_t* ids, void* ws, hipStream_t st);
+size_t kmeans_update_workspace(int heads, int64_t n, int C);
+constexpr int kListChunk = 32768;      // tokens per member-list chunk (16-bit offsets)
 
 hipError_t launch_lse_merge(int heads, int64_t n_q, int dim, int n_parts, const float* const* outs,
                             const float* const* lses, float* out, float* lse, hipStream_t st);

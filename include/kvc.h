@@ -96,7 +96,9 @@ typedef struct {
  *   n_iters    >= 0 (0 = assignment only).
  *   ids_out    [heads][n_tokens]: argmin over centres of the squared L2 distance,
  *              ties to the lowest index.
- *   ws         workspace of at least kvc_fit_assign_workspace_bytes(...) bytes.
+ *   ws         workspace of at least kvc_fit_assign_workspace_bytes(...) bytes
+ *              (centre norms and the per-centre member lists of the update,
+ *              about 2 bytes per token plus 4 per centre and 32768 tokens).
  * dim must be 64 or 128; n_centroids 1..256; n_tokens >= n_centroids is not
  * required. */
 kvc_status kvc_fit_assign(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt,
