@@ -345,13 +345,12 @@ kvc_status kvc_attend(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype
         auto* kt = reinterpret_cast<uint16_t*>(w);
         auto* vt = reinterpret_cast<uint16_t*>(w + tb);
         w += 2 * tb;
-        hipError_t e = kvc::launch_centre_table(heads, C, dim, cdt, segs[i].k_cent, kt, stream);
-        if (e == hipSuccess) e = kvc::launch_centre_table(heads, C, dim, cdt, segs[i].v_cent, vt, stream);
-        if (e != hipSuccess) return hip_status(e, "centre table");
         sl.s[di].k_tab = kt;
         sl.s[di].v_tab = vt;
         ++di;
       }
+      hipError_t e = kvc::launch_centre_tables(heads, dim, sl, stream);
+      if (e != hipSuccess) return hip_status(e, "centre tables");
     }
     hipError_t e = kvc::launch_attend(heads, n_q, dim, q_dtype, q, sl, kb, vb, g, cdt, n_split, part_out, part_lse,
                                       stream);

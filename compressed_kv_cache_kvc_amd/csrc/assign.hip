@@ -199,12 +199,78 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
     const float thr = err_scale * (xx[cb] + 2.f * cmax);
     const bool flag = valid && half == 0 && !(nb2 - nb1 > thr);  // also catches NaN
     uint64_t mask = __ballot(flag);
-    while (mask) {
-      const int b = __builtin_ctzll(mask);
-      mask &= mask - 1;
-      const int64_t t = tok0 + cb * 32 + b;
-      const int e = exact_assign_token<bf16_t, D>(x + (int64_t(h) * n + t) * D, centh, C, lane);
-      if (lane == b) id = e;
+    if (mask) {
+      // The true nearest centre of a flagged token is among the centres whose
+      // computed score is within thr of the best one.  Those candidates are found
+      // by scoring this token half once more, then re-scored exactly (fp64,
+      // dimensions spread over the lanes, a fixed reduction order), ties to the
+      // lowest index.
+      const float lim = nb1 + thr;
+      uint32_t cm[8];                 // candidate bits of block blk: 16 per lane
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) cm[blk] = 0;
+      for (int blk = 0; blk < nblk; ++blk) {
+        f32x16 acc;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 t = *reinterpret_cast<const float4*>(&sN[blk * 32 + 8 * g4 + 4 * half]);
+          acc[4 * g4 + 0] = t.x; acc[4 * g4 + 1] = t.y; acc[4 * g4 + 2] = t.z; acc[4 * g4 + 3] = t.w;
+        }
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&sC[(blk * 32 + col) * ROWP + kc * 16 + half * 8]));
+          acc = mfma32(a, xb[cb][kc], acc);
+        }
+        uint32_t bits = 0;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) bits |= (acc[v] <= lim ? 1u : 0u) << v;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (q == blk) cm[q] = bits;
+      }
+      constexpr int PERL = D / 64;    // dimensions per lane in the exact re-scoring
+      while (mask) {
+        const int b = __builtin_ctzll(mask);
+        mask &= mask - 1;
+        const int64_t t = tok0 + cb * 32 + b;
+        const bf16_t* xr = x + (int64_t(h) * n + t) * D;
+        double xd[PERL];
+#pragma unroll
+        for (int i = 0; i < PERL; ++i)
+          xd[i] = double(__uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(xr)[lane * PERL + i]) << 16));
+        double best = INFINITY;
+        int bi = 0x7fffffff;
+        for (int blk = 0; blk < nblk; ++blk) {
+          uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (q == blk) {
+              w0 = __builtin_amdgcn_readlane(cm[q], b);
+              w1 = __builtin_amdgcn_readlane(cm[q], b + 32);
+            }
+          uint32_t both = w0 | (w1 << 16);   // bit v: row 8*(v/4) + v%4 (+4 for the high half)
+          while (both) {
+            const int bit = __builtin_ctz(both);
+            both &= both - 1;
+            const int v = bit & 15, hh = bit >> 4;
+            const int ci = blk * 32 + 8 * (v / 4) + 4 * hh + (v % 4);
+            double part = 0.0;
+#pragma unroll
+            for (int i = 0; i < PERL; ++i) {
+              const double cv = double(__uint_as_float(uint32_t(sC[ci * ROWP + lane * PERL + i]) << 16));
+              const double dlt = xd[i] - cv;
+              part = __dadd_rn(part, __dmul_rn(dlt, dlt));
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) part = __dadd_rn(part, __shfl_xor(part, o, 64));
+            if (part < best || (part == best && ci < bi)) { best = part; bi = ci; }
+          }
+        }
+        int e = bi;
+        if (bi == 0x7fffffff)           // no candidate (non-finite scores): score every centre exactly
+          e = exact_assign_token<bf16_t, D>(xr, centh, C, lane);
+        if (lane == b) id = e;
+      }
     }
     if (valid && half == 0) ids[int64_t(h) * n + tok] = static_cast<uint8_t>(id);
   }
@@ -253,6 +319,7 @@ __device__ __forceinline__ uint32_t f64_to_bits_rne(double d) {
 __global__ __launch_bounds__(256) void member_lists_kernel(const uint8_t* __restrict__ ids, int64_t n, int C,
                                                            uint32_t* __restrict__ off, uint16_t* __restrict__ list) {
   __shared__ __attribute__((aligned(16))) uint16_t cnt[256 * 256];   // [centre][thread]
+  __shared__ __attribute__((aligned(16))) uint8_t sid[kListChunk];     // the chunk's ids
   __shared__ uint32_t base[257];
   const int t = threadIdx.x;
   const int k = blockIdx.x;
@@ -265,8 +332,9 @@ __global__ __launch_bounds__(256) void member_lists_kernel(const uint8_t* __rest
   const int j1 = j0 + L < len ? j0 + L : len;
   const uint8_t* idk = ids + int64_t(h) * n + c0;
   for (int i = t; i < 256 * 256 / 8; i += 256) reinterpret_cast<uint4*>(cnt)[i] = make_uint4(0, 0, 0, 0);
+  for (int i = t; i < len; i += 256) sid[i] = idk[i];      // coalesced
   __syncthreads();
-  for (int j = j0; j < j1; ++j) ++cnt[int(idk[j]) * 256 + t];
+  for (int j = j0; j < j1; ++j) ++cnt[int(sid[j]) * 256 + t];
   __syncthreads();
   // row c: exclusive prefix over the threads, row total to base[c]
   if (t < C) {
@@ -286,21 +354,31 @@ __global__ __launch_bounds__(256) void member_lists_kernel(const uint8_t* __rest
     base[t] = run;
   }
   __syncthreads();
-  if (t == 0) {   // exclusive scan of the row totals (at most 256 additions)
-    uint32_t run = 0;
-    for (int c = 0; c < C; ++c) {
-      const uint32_t v = base[c];
-      base[c] = run;
-      run += v;
+  // exclusive scan of the row totals: inclusive scan inside each wavefront, then
+  // the wavefront totals added in order
+  {
+    const int lane = t & 63, w = t >> 6;
+    const uint32_t v = t < C ? base[t] : 0u;
+    uint32_t inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t u = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += u;
     }
-    base[C] = run;
+    __shared__ uint32_t wsum[4];
+    if (lane == 63) wsum[w] = inc;
+    __syncthreads();
+    uint32_t add = 0;
+    for (int i = 0; i < w; ++i) add += wsum[i];
+    if (t < C) base[t] = add + inc - v;
+    if (t == 255) base[C] = add + inc;
   }
   __syncthreads();
   uint32_t* offk = off + (int64_t(h) * nk + k) * (C + 1);
   for (int c = t; c <= C; c += 256) offk[c] = base[c];
   uint16_t* lk = list + int64_t(h) * n + c0;
   for (int j = j0; j < j1; ++j) {
-    const int c = idk[j];
+    const int c = sid[j];
     const uint32_t slot = base[c] + cnt[c * 256 + t]++;
     lk[slot] = static_cast<uint16_t>(j);
   }
@@ -316,7 +394,8 @@ __global__ __launch_bounds__(256) void kmeans_update_kernel(const T* __restrict_
                                                             const uint32_t* __restrict__ off,
                                                             const uint16_t* __restrict__ list, int C, int64_t n) {
   constexpr int PER = D / 64;                 // channels per lane
-  constexpr int BATCH = 16;
+  constexpr int WPR = PER * int(sizeof(T)) / 4 > 0 ? PER * int(sizeof(T)) / 4 : 1;   // 32-bit words per lane and row
+  constexpr int BATCH = 64 / WPR < 64 ? 64 / WPR : 64;   // rows in flight (64 registers of raw words)
   const int lane = threadIdx.x % 64;
   const int c = blockIdx.x * 4 + threadIdx.x / 64;
   const int h = blockIdx.y;
@@ -327,6 +406,25 @@ __global__ __launch_bounds__(256) void kmeans_update_kernel(const T* __restrict_
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.0;
   int cnt = 0;
+  // lane's channels of a row as fp32
+  auto load_raw = [&](const T* row, uint32_t (&w)[WPR]) {
+    if constexpr (sizeof(T) == 2 && PER == 1) w[0] = reinterpret_cast<const uint16_t*>(row)[0];
+    else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int q = 0; q < WPR; ++q) w[q] = reinterpret_cast<const uint32_t*>(row)[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < WPR; ++q) w[q] = reinterpret_cast<const uint32_t*>(row)[q];
+    }
+  };
+  auto value = [&](const uint32_t (&w)[WPR], int i) -> float {
+    if constexpr (sizeof(T) == 2) {
+      if constexpr (PER == 1) return __uint_as_float(w[0] << 16);
+      else return (i & 1) ? bf16_hi(w[i / 2]) : bf16_lo(w[i / 2]);
+    } else {
+      return __uint_as_float(w[i]);
+    }
+  };
   for (int64_t k = 0; k < nk; ++k) {
     const uint32_t* offk = off + (int64_t(h) * nk + k) * (C + 1);
     const int lo = int(offk[c]), hi = int(offk[c + 1]);
@@ -337,24 +435,17 @@ __global__ __launch_bounds__(256) void kmeans_update_kernel(const T* __restrict_
       const int m = hi - s0 < 64 ? hi - s0 : 64;
       const int mine = s0 + lane < hi ? int(lk[s0 + lane]) : 0;   // member s0 + lane of the list
       for (int u0 = 0; u0 < m; u0 += BATCH) {
-        float v[BATCH][PER];
+        uint32_t w[BATCH][WPR];
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
           const int j = __builtin_amdgcn_readlane(mine, u0 + u < m ? u0 + u : 0);
-          const T* row = xk + int64_t(j) * D;
-#pragma unroll
-          for (int i = 0; i < PER; ++i) {
-            if constexpr (sizeof(T) == 2)
-              v[u][i] = __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(row)[i]) << 16);
-            else
-              v[u][i] = reinterpret_cast<const float*>(row)[i];
-          }
+          load_raw(xk + int64_t(j) * D, w[u]);
         }
 #pragma unroll
         for (int u = 0; u < BATCH; ++u)
           if (u0 + u < m) {
 #pragma unroll
-            for (int i = 0; i < PER; ++i) acc[i] = __dadd_rn(acc[i], double(v[u][i]));
+            for (int i = 0; i < PER; ++i) acc[i] = __dadd_rn(acc[i], double(value(w[u], i)));
           }
       }
     }

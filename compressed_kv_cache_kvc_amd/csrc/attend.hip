@@ -664,14 +664,25 @@ __global__ __launch_bounds__(256) void project_centres_kernel(const CT* __restri
   tab[(int64_t(h) * C + c) * R + tile_channel(k)] = static_cast<uint16_t>(pack_f16x2(a, 0.f) & 0xffffu);
 }
 
-// fp16 copy of a bf16 centre table in tile channel order (exact for bf16 values
-// inside the fp16 normal range).  One thread per block of four channels.
-__global__ __launch_bounds__(256) void centre_table_kernel(const uint2* __restrict__ cent, int64_t n_blocks,
-                                                           uint2* __restrict__ tab) {
+// fp16 copies of the bf16 centre tables of all segments (K and V), in tile
+// channel order (exact for bf16 values inside the fp16 normal range): one thread
+// per eight channels, table j covering threads [start[j], start[j+1]).
+struct TableJobs {
+  const uint4* src[2 * kMaxSegs];
+  uint4* dst[2 * kMaxSegs];
+  int64_t start[2 * kMaxSegs + 1];
+  int n;
+};
+
+__global__ __launch_bounds__(256) void centre_tables_kernel(TableJobs jobs) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= n_blocks) return;
-  const uint2 w = cent[i];   // channels (0, 1), (2, 3)
-  tab[i] = make_uint2(pack_f16x2(bf16_lo(w.x), bf16_lo(w.y)), pack_f16x2(bf16_hi(w.x), bf16_hi(w.y)));
+  if (i >= jobs.start[jobs.n]) return;
+  int j = 0;
+  while (i >= jobs.start[j + 1]) ++j;
+  const int64_t e = i - jobs.start[j];
+  const uint4 w = jobs.src[j][e];   // channels (0, 1), (2, 3), (4, 5), (6, 7)
+  jobs.dst[j][e] = make_uint4(pack_f16x2(bf16_lo(w.x), bf16_lo(w.y)), pack_f16x2(bf16_hi(w.x), bf16_hi(w.y)),
+                              pack_f16x2(bf16_lo(w.z), bf16_lo(w.w)), pack_f16x2(bf16_hi(w.z), bf16_hi(w.w)));
 }
 
 template <int DQ, bool LOWDIM, int DOUT>
@@ -758,13 +769,23 @@ hipError_t launch_project_centres(int heads, int C, int dim, int rank, kvc_dtype
   return hipGetLastError();
 }
 
-hipError_t launch_centre_table(int heads, int C, int dim, kvc_dtype cdt, const void* cent, uint16_t* tab,
-                               hipStream_t st) {
-  if (heads == 0 || C == 0) return hipSuccess;
-  if (cdt != KVC_BF16 || dim % 4 != 0) return hipErrorInvalidValue;
-  const int64_t n_blocks = int64_t(heads) * C * dim / 4;
-  hipLaunchKernelGGL(centre_table_kernel, dim3(unsigned((n_blocks + 255) / 256)), dim3(256), 0, st,
-                     static_cast<const uint2*>(cent), n_blocks, reinterpret_cast<uint2*>(tab));
+hipError_t launch_centre_tables(int heads, int dim, const SegList& segs, hipStream_t st) {
+  if (heads == 0 || segs.n == 0) return hipSuccess;
+  if (dim % 8 != 0) return hipErrorInvalidValue;
+  TableJobs jobs;
+  jobs.n = 0;
+  jobs.start[0] = 0;
+  for (int i = 0; i < segs.n; ++i) {
+    const int64_t n8 = int64_t(heads) * segs.s[i].n_centroids * dim / 8;
+    for (int t = 0; t < 2; ++t) {
+      jobs.src[jobs.n] = static_cast<const uint4*>(t == 0 ? segs.s[i].k_cent : segs.s[i].v_cent);
+      jobs.dst[jobs.n] = reinterpret_cast<uint4*>(const_cast<uint16_t*>(t == 0 ? segs.s[i].k_tab : segs.s[i].v_tab));
+      jobs.start[jobs.n + 1] = jobs.start[jobs.n] + n8;
+      ++jobs.n;
+    }
+  }
+  const int64_t total = jobs.start[jobs.n];
+  hipLaunchKernelGGL(centre_tables_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, st, jobs);
   return hipGetLastError();
 }
 

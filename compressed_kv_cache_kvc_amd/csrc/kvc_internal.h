@@ -52,7 +52,7 @@ hipError_t launch_assign(int heads, int64_t n, int dim, kvc_dtype dt, const void
 hipError_t launch_kmeans_update(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C,
                                 void* cent, const uint8_t* ids, void* ws, hipStream_t st);
 size_t kmeans_update_workspace(int heads, int64_t n, int C);
-constexpr int kListChunk = 32768;      // tokens per member-list chunk (16-bit offsets)
+constexpr int kListChunk = 16384;      // tokens per member-list chunk (ids staged in LDS)
 
 hipError_t launch_lse_merge(int heads, int64_t n_q, int dim, int n_parts, const float* const* outs,
                             const float* const* lses, float* out, float* lse, hipStream_t st);
@@ -71,8 +71,9 @@ hipError_t launch_project_queries(int heads, int64_t n_q, int dim, int rank, con
 hipError_t launch_project_centres(int heads, int C, int dim, int rank, kvc_dtype cdt,
                                   const void* cent, const float* basis, uint16_t* tab,
                                   hipStream_t st);
-hipError_t launch_centre_table(int heads, int C, int dim, kvc_dtype cdt, const void* cent,
-                               uint16_t* tab, hipStream_t st);
+// fp16 centre tables (k_tab, v_tab, already pointed into the workspace) of every
+// segment from its bf16 centres, in one launch
+hipError_t launch_centre_tables(int heads, int dim, const SegList& segs, hipStream_t st);
 hipError_t launch_attend_lowdim(int heads, int64_t n_q, int dim, int rank,
                                 const uint16_t* q_proj, const float* basis_v,
                                 const SegList& segs, int k_bits, int v_bits, int group,
