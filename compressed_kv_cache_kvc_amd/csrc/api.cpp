@@ -188,9 +188,8 @@ const char* kvc_version(void) { return "kvc 0.1.0 (gfx950)"; }
 size_t kvc_fit_assign_workspace_bytes(int32_t heads, int64_t n_tokens, int32_t dim, int32_t n_centroids) {
   (void)dim;
   if (heads <= 0 || n_centroids <= 0) return 0;
-  // centre norms, then the member lists of the centre update
-  return align_up(size_t(heads) * size_t(n_centroids) * 4) +
-         align_up(kvc::kmeans_update_workspace(heads, n_tokens > 0 ? n_tokens : 0, n_centroids));
+  // the member lists of the centre update
+  return align_up(kvc::kmeans_update_workspace(heads, n_tokens > 0 ? n_tokens : 0, n_centroids));
 }
 
 kvc_status kvc_fit_assign(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt, const void* x,
@@ -210,16 +209,12 @@ kvc_status kvc_fit_assign(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtyp
     const size_t need = kvc_fit_assign_workspace_bytes(heads, n_tokens, dim, n_centroids);
     KVC_REQUIRE(ws_bytes >= need, KVC_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
     KVC_PTR(ws, true, "ws");
-    float* norms = static_cast<float*>(ws);
     for (int it = 0; it <= n_iters; ++it) {
-      hipError_t e = kvc::launch_centroid_norms(heads, n_centroids, dim, dt, centroids, norms, stream);
-      if (e != hipSuccess) return hip_status(e, "centroid norms");
-      e = kvc::launch_assign(heads, n_tokens, dim, dt, x, n_centroids, centroids, norms, ids_out, stream);
+      hipError_t e = kvc::launch_assign(heads, n_tokens, dim, dt, x, n_centroids, centroids, ids_out, stream);
       if (e != hipSuccess) return hip_status(e, "assign");
       if (it == n_iters) break;
       e = kvc::launch_kmeans_update(heads, n_tokens, dim, dt, x, n_centroids, centroids, ids_out,
-                                    static_cast<char*>(ws) + align_up(size_t(heads) * size_t(n_centroids) * 4),
-                                    stream);
+                                    ws, stream);
       if (e != hipSuccess) return hip_status(e, "k-means update");
     }
     return ok();
@@ -231,9 +226,8 @@ kvc_status kvc_fit_assign(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtyp
 // ------------------------------------------------------------------------------ encode
 size_t kvc_encode_workspace_bytes(int32_t heads, int64_t n_tokens, int32_t dim, int32_t n_centroids,
                                   int32_t ids_given) {
-  (void)n_tokens; (void)dim;
-  if (ids_given || heads <= 0 || n_centroids <= 0) return 0;
-  return align_up(size_t(heads) * size_t(n_centroids) * 4);   // centre norms of the assignment
+  (void)heads; (void)n_tokens; (void)dim; (void)n_centroids; (void)ids_given;
+  return 0;   // the assignment (ids_in NULL) needs no workspace
 }
 
 kvc_status kvc_encode(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt, const void* x,
@@ -266,13 +260,8 @@ kvc_status kvc_encode(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt
     const uint8_t* ids = ids_in;
     if (ids == nullptr) {
       KVC_REQUIRE(ids_out != nullptr, KVC_ERR_INVALID_ARG, "ids_out is needed when ids_in is NULL");
-      const size_t need = kvc_encode_workspace_bytes(heads, n_tokens, dim, n_centroids, 0);
-      KVC_REQUIRE(ws_bytes >= need, KVC_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
-      KVC_PTR(ws, true, "ws");
-      float* norms = static_cast<float*>(ws);
-      hipError_t e = kvc::launch_centroid_norms(heads, n_centroids, dim, dt, centroids, norms, stream);
-      if (e != hipSuccess) return hip_status(e, "centroid norms");
-      e = kvc::launch_assign(heads, n_tokens, dim, dt, x, n_centroids, centroids, norms, ids_out, stream);
+      (void)ws; (void)ws_bytes;
+      hipError_t e = kvc::launch_assign(heads, n_tokens, dim, dt, x, n_centroids, centroids, ids_out, stream);
       if (e != hipSuccess) return hip_status(e, "assign");
       ids = ids_out;
     } else if (ids_out != nullptr) {

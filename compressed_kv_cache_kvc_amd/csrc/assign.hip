@@ -15,22 +15,6 @@
 namespace kvc {
 namespace {
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void centroid_norms_kernel(const T* __restrict__ cent, int64_t total,
-                                                             float* __restrict__ norms) {
-  const int64_t item = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (item >= total) return;
-  float s = 0.f;
-#pragma unroll
-  for (int c8 = 0; c8 < D / 8; ++c8) {
-    float v[8];
-    load_row<8>(cent + item * D + c8 * 8, v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s = fmaf(v[i], v[i], s);
-  }
-  norms[item] = s;
-}
-
 // Exact fp64 squared distance between a token row (global) and a centre row.
 template <typename T, int D>
 __device__ __forceinline__ double exact_dist(const T* __restrict__ xr, const T* __restrict__ cr) {
@@ -92,8 +76,7 @@ __device__ __forceinline__ uint32_t scale_m2_bf16x2(uint32_t w) {
 
 template <int D>
 __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ cent,
-                                                          const float* __restrict__ norms, int C, int64_t n,
-                                                          uint8_t* __restrict__ ids) {
+                                                          int C, int64_t n, uint8_t* __restrict__ ids) {
   constexpr int ROWP = D + 8;          // padded LDS row (bf16 elements): conflict-free fragment reads
   constexpr int KC = D / 16;
   __shared__ __attribute__((aligned(16))) uint16_t sC[256 * ROWP];
@@ -116,14 +99,36 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
     if (row < C) w = *reinterpret_cast<const uint4*>(centh + int64_t(row) * D + c8 * 8);
     *reinterpret_cast<uint4*>(&sC[row * ROWP + c8 * 8]) = w;
   }
-  for (int c = tid; c < rows; c += 256) sN[c] = c < C ? norms[int64_t(h) * C + c] : INFINITY;
+  __syncthreads();
+  // ||c||^2 in fp32, channels in order (one fused multiply-add each); padding rows
+  // score +inf
+  {
+    float sn = INFINITY;
+    if (tid < C) {
+      sn = 0.f;
+#pragma unroll
+      for (int c8 = 0; c8 < D / 8; ++c8) {
+        const uint4 w = *reinterpret_cast<const uint4*>(&sC[tid * ROWP + c8 * 8]);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sn = fmaf(bf16_lo(ww[i]), bf16_lo(ww[i]), sn);
+          sn = fmaf(bf16_hi(ww[i]), bf16_hi(ww[i]), sn);
+        }
+      }
+    }
+    if (tid < rows) sN[tid] = sn;
+  }
+  __syncthreads();
   float cmax = 0.f;
-  for (int c = lane; c < C; c += 64) cmax = fmaxf(cmax, norms[int64_t(h) * C + c]);
+  for (int c = lane; c < C; c += 64) cmax = fmaxf(cmax, sN[c]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, off, 64));
 
+  for (int round = 0; round < kAssignRounds; ++round) {
   // token fragments (B operand), pre-scaled by -2, and ||x||^2
-  const int64_t tok0 = int64_t(blockIdx.x) * 256 + wave * 64;
+  const int64_t tok0 = (int64_t(blockIdx.x) * kAssignRounds + round) * 256 + wave * 64;
+  if (tok0 >= n) break;                // wave-uniform; no barrier follows
   bf16x8 xb[2][KC];
   float xx[2];
 #pragma unroll
@@ -146,7 +151,6 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
     }
     xx[cb] = s + __shfl_xor(s, 32, 64);
   }
-  __syncthreads();
 
   float b1[2] = {INFINITY, INFINITY}, b2[2] = {INFINITY, INFINITY};
   int i1[2] = {0, 0};
@@ -273,6 +277,7 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
       }
     }
     if (valid && half == 0) ids[int64_t(h) * n + tok] = static_cast<uint8_t>(id);
+  }
   }
 }
 
@@ -464,39 +469,17 @@ __global__ __launch_bounds__(256) void kmeans_update_kernel(const T* __restrict_
 
 }  // namespace
 
-hipError_t launch_centroid_norms(int heads, int C, int dim, kvc_dtype dt, const void* cent, float* norms,
-                                 hipStream_t st) {
-  const int64_t total = int64_t(heads) * C;
-  if (total == 0) return hipSuccess;
-  const unsigned blocks = unsigned((total + 255) / 256);
-  if (dt == KVC_BF16 && dim == 128)
-    hipLaunchKernelGGL((centroid_norms_kernel<bf16_t, 128>), dim3(blocks), dim3(256), 0, st,
-                       static_cast<const bf16_t*>(cent), total, norms);
-  else if (dt == KVC_BF16 && dim == 64)
-    hipLaunchKernelGGL((centroid_norms_kernel<bf16_t, 64>), dim3(blocks), dim3(256), 0, st,
-                       static_cast<const bf16_t*>(cent), total, norms);
-  else if (dt == KVC_F32 && dim == 128)
-    hipLaunchKernelGGL((centroid_norms_kernel<float, 128>), dim3(blocks), dim3(256), 0, st,
-                       static_cast<const float*>(cent), total, norms);
-  else if (dt == KVC_F32 && dim == 64)
-    hipLaunchKernelGGL((centroid_norms_kernel<float, 64>), dim3(blocks), dim3(256), 0, st,
-                       static_cast<const float*>(cent), total, norms);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
 hipError_t launch_assign(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C, const void* cent,
-                         const float* norms, uint8_t* ids, hipStream_t st) {
+                         uint8_t* ids, hipStream_t st) {
   if (heads == 0 || n == 0) return hipSuccess;
   if (dt == KVC_BF16) {
-    const dim3 grid(unsigned((n + 255) / 256), unsigned(heads));
+    const dim3 grid(unsigned((n + 256 * kAssignRounds - 1) / (256 * kAssignRounds)), unsigned(heads));
     if (dim == 128)
       hipLaunchKernelGGL((assign_mfma_kernel<128>), grid, dim3(256), 0, st, static_cast<const bf16_t*>(x),
-                         static_cast<const bf16_t*>(cent), norms, C, n, ids);
+                         static_cast<const bf16_t*>(cent), C, n, ids);
     else if (dim == 64)
       hipLaunchKernelGGL((assign_mfma_kernel<64>), grid, dim3(256), 0, st, static_cast<const bf16_t*>(x),
-                         static_cast<const bf16_t*>(cent), norms, C, n, ids);
+                         static_cast<const bf16_t*>(cent), C, n, ids);
     else
       return hipErrorInvalidValue;
   } else {

@@ -43,10 +43,10 @@ hipError_t launch_encode(int heads, int64_t n, int dim, kvc_dtype dt, const void
                          const void* cent, const uint8_t* ids, const float* basis, int rank,
                          int bits, int group, uint8_t* codes, uint16_t* meta, hipStream_t st);
 
-hipError_t launch_centroid_norms(int heads, int C, int dim, kvc_dtype dt, const void* cent,
-                                 float* norms, hipStream_t st);
+// Nearest-centre ids; the centre norms are computed inside the kernel.
 hipError_t launch_assign(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C,
-                         const void* cent, const float* norms, uint8_t* ids, hipStream_t st);
+                         const void* cent, uint8_t* ids, hipStream_t st);
+constexpr int kAssignRounds = 1;       // 256-token rounds per assignment workgroup
 // k-means update (member lists + per-centre means); ws holds
 // kmeans_update_workspace(heads, n, C) bytes, 256-byte aligned.
 hipError_t launch_kmeans_update(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C,

@@ -116,8 +116,9 @@ size_t kvc_fit_assign_workspace_bytes(int32_t heads, int64_t n_tokens, int32_t d
  * fl32((max - z) / (2^bits - 1)), zero values stored as +0; code q =
  * clamp(round-half-even(fl32(fl32(r - z) * fl32(1/s))), 0, 2^bits - 1), q = 0
  * when s = 0.
- *   ids_in     [heads][n_tokens] or NULL; NULL runs the assignment first (then a
- *              workspace of kvc_encode_workspace_bytes(..., 0) bytes is needed).
+ *   ids_in     [heads][n_tokens] or NULL; NULL runs the assignment first.
+ *   ws         kvc_encode_workspace_bytes(...) bytes (currently 0: encode keeps
+ *              the argument so that a later version may stage data in it).
  *   ids_out    NULL, or where the ids used are written (may equal ids_in only
  *              when ids_in is NULL).
  *   basis      NULL or [heads][dim][rank] fp32; rank = 0 without a basis.
