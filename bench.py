@@ -56,6 +56,26 @@ class Workload:
         self.synth = synth
         self.phase_ms = {}
         self.events = []
+        self.side = None
+
+    def both(self, fk, fv):
+        """Run fk() on the current stream and fv() on a second stream (default
+        priority), both after the work already queued; the current stream then
+        waits for the second.  The K and V fits are independent, so their small,
+        latency-bound launches overlap."""
+        torch = self.torch
+        cur = torch.cuda.current_stream()
+        if self.side is None:
+            self.side = torch.cuda.Stream()
+        self.side.wait_stream(cur)
+        rk = fk()
+        with torch.cuda.stream(self.side):
+            rv = fv()
+        for t in (rv if isinstance(rv, (list, tuple)) else [rv]):
+            if isinstance(t, torch.Tensor):
+                t.record_stream(cur)
+        cur.wait_stream(self.side)
+        return rk, rv
 
     def ev(self):
         e = self.torch.cuda.Event(enable_timing=True)
@@ -73,24 +93,21 @@ class Workload:
         return acc
 
 
-def fit_encode(w, x, cent0, bits, basis=None, n_iter=2):
-    """Fit centres on x (from cent0) and encode: returns (codes, meta, ids, cent)."""
+def fit_encode_pair(w, k, kc0, v, vc0, n_iter=2):
+    """Fit the K and V centres (from kc0, vc0) side by side, then encode both:
+    returns (kcodes, kmeta, kid, kc), (vcodes, vmeta, vid, vc)."""
     import compressed_kv_cache_kvc_amd as kvc
-    cent = cent0.clone()
+    cfg = w.cfg
+    kc, vc = kc0.clone(), vc0.clone()
     e0 = w.ev()
-    ids = kvc.fit_assign(x, cent, n_iter=n_iter)
+    kid, vid = w.both(lambda: kvc.fit_assign(k, kc, n_iter=n_iter), lambda: kvc.fit_assign(v, vc, n_iter=n_iter))
     e1 = w.ev()
-    codes, meta, _ = kvc.encode(x, cent, bits, w.cfg.group, ids=ids)
+    kco, kme, _ = kvc.encode(k, kc, cfg.k_bits, cfg.group, ids=kid)
+    vco, vme, _ = kvc.encode(v, vc, cfg.v_bits, cfg.group, ids=vid)
     e2 = w.ev()
     w.mark("fit", e0, e1)
     w.mark("encode", e1, e2)
-    out = [codes, meta, ids, cent]
-    if basis is not None:
-        lc, lm, _ = kvc.encode(x, cent, bits, w.cfg.group, ids=ids, basis=basis)
-        e3 = w.ev()
-        w.mark("encode", e2, e3)
-        out += [lc, lm]
-    return out
+    return (kco, kme, kid, kc), (vco, vme, vid, vc)
 
 
 class SingleLayer(Workload):
@@ -125,16 +142,16 @@ class SingleLayer(Workload):
         import compressed_kv_cache_kvc_amd as kvc
         cfg = self.cfg
         if len(self.bounds) == 2:
-            kcodes, kmeta, kid, kc = fit_encode(self, self.k, self.kc0, cfg.k_bits)
-            vcodes, vmeta, vid, vc = fit_encode(self, self.v, self.vc0, cfg.v_bits)
+            (kcodes, kmeta, kid, kc), (vcodes, vmeta, vid, vc) = fit_encode_pair(
+                self, self.k, self.kc0, self.v, self.vc0, n_iter=cfg.n_iter)
             segs = [kvc.Segment(kcodes, kmeta, kid, kc, vcodes, vmeta, vid, vc, cfg.k_bits, cfg.v_bits, cfg.group)]
         else:
             # one centre table per head over the whole history; each history
             # segment is encoded from its own slice (segments are attention splits)
             kc, vc = self.kc0.clone(), self.vc0.clone()
             e0 = self.ev()
-            kid = kvc.fit_assign(self.k, kc, n_iter=cfg.n_iter)
-            vid = kvc.fit_assign(self.v, vc, n_iter=cfg.n_iter)
+            kid, vid = self.both(lambda: kvc.fit_assign(self.k, kc, n_iter=cfg.n_iter),
+                                 lambda: kvc.fit_assign(self.v, vc, n_iter=cfg.n_iter))
             e1 = self.ev()
             segs = []
             for (a, b), ks, vs in zip(zip(self.bounds[:-1], self.bounds[1:]), self.k_parts, self.v_parts):
@@ -181,8 +198,8 @@ class LargerBackbone(Workload):
         torch = self.torch
         kc, vc = self.kc0.clone(), self.vc0.clone()
         e0 = self.ev()
-        kid = kvc.fit_assign(self.k, kc, n_iter=cfg.n_iter)
-        vid = kvc.fit_assign(self.v, vc, n_iter=cfg.n_iter)
+        kid, vid = self.both(lambda: kvc.fit_assign(self.k, kc, n_iter=cfg.n_iter),
+                             lambda: kvc.fit_assign(self.v, vc, n_iter=cfg.n_iter))
         e1 = self.ev()
         F = cfg.far
         kidf, kidr = kid[:, :F].contiguous(), kid[:, F:].contiguous()
@@ -237,8 +254,8 @@ class Streaming(Workload):
         segs = []
         out = None
         for (k, v, q, kc0, vc0) in self.chunks:
-            kcodes, kmeta, kid, kc = fit_encode(self, k, kc0, cfg.k_bits)
-            vcodes, vmeta, vid, vc = fit_encode(self, v, vc0, cfg.v_bits)
+            (kcodes, kmeta, kid, kc), (vcodes, vmeta, vid, vc) = fit_encode_pair(self, k, kc0, v, vc0,
+                                                                                 n_iter=cfg.n_iter)
             segs.append(kvc.Segment(kcodes, kmeta, kid, kc, vcodes, vmeta, vid, vc, cfg.k_bits, cfg.v_bits, cfg.group))
             e0 = self.ev()
             out, lse = kvc.attend(q, segs)
