@@ -149,9 +149,8 @@ def test_fit_matches_oracle_per_iteration(dtype, storage):
             cent_o[h] = c1
 
 
-def test_fit_many_heads_eight_centres_per_wave():
-    # heads x centres above 16384 selects the update kernel that gives eight
-    # centres to one wavefront; C = 100 leaves a partial last group
+def test_fit_many_heads():
+    # 200 heads x 100 centres: C = 100 leaves a partial last workgroup of centres
     H, N, C, d = 200, 300, 100, 64
     x = _bf16_tokens(H, N, d, 13)
     init = synth.forgy_init(x, C, 14)
@@ -171,6 +170,27 @@ def test_fit_many_heads_eight_centres_per_wave():
         assert not ((ids_g.cpu().numpy()[h] != ids1) & ~tie).any()
         checked += 1
     assert checked >= 3
+
+
+def test_fit_long_history_member_list_chunks():
+    # 40000 tokens per head: the member lists of the centre update span three
+    # chunks of 16384 tokens, whose sums must continue in token order
+    # (seed 16 with these centres has no near-tie token, before or after the update)
+    H, N, C, d = 1, 40000, 16, 64
+    x = _bf16_tokens(H, N, d, 16)
+    init = synth.forgy_init(x, C, 116)
+    cg = init.to(DEV).clone()
+    ids_g = kvc().fit_assign(x.to(DEV), cg, n_iter=1)
+    torch.cuda.synchronize()
+    xn, cn = np32(x), np32(init)
+    for h in range(H):
+        _, d1, d2 = oracle.assign(xn[h], cn[h])
+        assert not near_tie(d1, d2).any(), "near-tie in the update test input"
+        c1, ids1 = oracle.fit(xn[h], cn[h], n_iter=1, storage="bf16")
+        assert np.array_equal(np32(cg)[h].view(np.uint32), c1.view(np.uint32)), f"head {h}"
+        _, e1, e2 = oracle.assign(xn[h], c1)
+        tie = near_tie(e1, e2) & (e1 != e2)
+        assert not ((ids_g.cpu().numpy()[h] != ids1) & ~tie).any()
 
 
 # ------------------------------------------------------------------------------ attention
