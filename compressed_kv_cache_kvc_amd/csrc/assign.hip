@@ -92,12 +92,26 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
   const int rows = nblk * 32;
   const bf16_t* centh = cent + int64_t(h) * C * D;
 
-  for (int e = tid; e < rows * (D / 8); e += 256) {
-    const int row = e / (D / 8);
-    const int c8 = e % (D / 8);
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (row < C) w = *reinterpret_cast<const uint4*>(centh + int64_t(row) * D + c8 * 8);
-    *reinterpret_cast<uint4*>(&sC[row * ROWP + c8 * 8]) = w;
+  // the centre table into LDS: all of a thread's loads are issued before the
+  // first store (a fixed, unrolled trip count), so their latencies overlap
+  {
+    constexpr int PER_T = 256 * (D / 8) / 256;
+    uint4 w[PER_T];
+#pragma unroll
+    for (int it = 0; it < PER_T; ++it) {
+      const int e = tid + it * 256;
+      const int row = e / (D / 8);
+      const int c8 = e % (D / 8);
+      w[it] = make_uint4(0, 0, 0, 0);
+      if (row < C) w[it] = *reinterpret_cast<const uint4*>(centh + int64_t(row) * D + c8 * 8);
+    }
+#pragma unroll
+    for (int it = 0; it < PER_T; ++it) {
+      const int e = tid + it * 256;
+      const int row = e / (D / 8);
+      const int c8 = e % (D / 8);
+      if (row < rows) *reinterpret_cast<uint4*>(&sC[row * ROWP + c8 * 8]) = w[it];
+    }
   }
   __syncthreads();
   // ||c||^2 in fp32, channels in order (one fused multiply-add each); padding rows

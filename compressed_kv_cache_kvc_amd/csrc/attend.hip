@@ -184,9 +184,9 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
     qf[kc] = as_f16x8(w);
   }
 
-  const int64_t T = segs.total_tiles;
-  const int64_t t_begin = T * split / p.n_split;
-  const int64_t t_end = T * (split + 1) / p.n_split;
+  const int T = int(segs.total_tiles);           // at most 24 * 2^19 tiles
+  const int t_begin = int(int64_t(T) * split / p.n_split);
+  const int t_end = int(int64_t(T) * (split + 1) / p.n_split);
 
   // dequantization role: eight lanes per token, so that the code, metadata and
   // centre-row loads of a wavefront cover whole rows (coalesced)
@@ -201,39 +201,63 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
   // already offset to this workgroup's head; being wave-uniform its fields live
   // in scalar registers, and are reloaded only when the cursor crosses into the
   // next segment, so no scalar memory load sits in the tile loop otherwise.
-  struct Cursor {
-    int si;
-    int64_t tile_begin, tile_end;
-    int n_tokens;
-    const uint8_t *k_codes, *v_codes, *k_ids, *v_ids;
+  // Three cursors walk the tiles (ids two tiles ahead, data one ahead of the
+  // dequantization, and the tile being scored); each holds the segment it is in
+  // and only the arrays it reads, already offset to this workgroup's head.  Being
+  // wave-uniform their fields live in scalar registers and are reloaded only when
+  // a cursor crosses into the next segment.
+  struct Span {
+    int si, tile_begin, tile_end, n_tokens;
+  };
+  struct IdCur {
+    Span s;
+    const uint8_t *k_ids, *v_ids;
+  };
+  struct DataCur {
+    Span s;
+    const uint8_t *k_codes, *v_codes;
     const uint32_t *k_meta, *v_meta;
     const uint16_t *k_tab, *v_tab;
   };
-  auto cursor_load = [&](Cursor& c, int si) {
-    const SegDev& s = segs.s[si];
+  auto span_load = [&](Span& c, int si) {
     c.si = si;
-    c.tile_begin = s.tile_begin;
-    c.tile_end = si + 1 < segs.n ? segs.s[si + 1].tile_begin : segs.total_tiles;
-    c.n_tokens = int(s.n_tokens);
+    c.tile_begin = int(segs.s[si].tile_begin);
+    c.tile_end = int(si + 1 < segs.n ? segs.s[si + 1].tile_begin : segs.total_tiles);
+    c.n_tokens = int(segs.s[si].n_tokens);
+  };
+  auto ids_load = [&](IdCur& c, int si) {
+    span_load(c.s, si);
+    const SegDev& s = segs.s[si];
+    const int64_t hn = int64_t(h) * s.n_tokens;
+    c.k_ids = s.k_ids + hn;
+    c.v_ids = s.v_ids + hn;
+  };
+  auto data_load = [&](DataCur& c, int si) {
+    span_load(c.s, si);
+    const SegDev& s = segs.s[si];
     const int64_t hn = int64_t(h) * s.n_tokens;
     c.k_codes = s.k_codes + hn * (DQ * KB / 8);
     c.v_codes = s.v_codes + hn * (DQ * VB / 8);
-    c.k_ids = s.k_ids + hn;
-    c.v_ids = s.v_ids + hn;
     c.k_meta = s.k_meta + hn * (DQ / G);
     c.v_meta = s.v_meta + hn * (DQ / G);
     const int64_t hc = int64_t(h) * s.n_centroids * DQ;
     c.k_tab = s.k_tab + hc;
     c.v_tab = s.v_tab + hc;
   };
-  auto cursor_seek = [&](Cursor& c, int64_t t) {
-    while (t >= c.tile_end) cursor_load(c, c.si + 1);
+  auto ids_seek = [&](IdCur& c, int t) {
+    while (t >= c.s.tile_end) ids_load(c, c.s.si + 1);
+  };
+  auto data_seek = [&](DataCur& c, int t) {
+    while (t >= c.s.tile_end) data_load(c, c.s.si + 1);
+  };
+  auto span_seek = [&](Span& c, int t) {
+    while (t >= c.tile_end) span_load(c, c.si + 1);
   };
   // token (within the head) of this thread's row in tile t, clamped into the
   // segment so that every load is in bounds; rows past the end read real
   // (finite) data and are masked out of the softmax
-  auto row_of = [&](const Cursor& c, int64_t t) -> uint32_t {
-    const int j0 = int(t - c.tile_begin) * 64;
+  auto row_of = [&](const Span& c, int t) -> uint32_t {
+    const int j0 = (t - c.tile_begin) * 64;
     const int last = c.n_tokens - 1;
     return uint32_t(j0 + dk < last ? j0 + dk : last);
   };
@@ -245,13 +269,13 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
   uint32_t km_r = 0, vm_r = 0;
   uint32_t kcw[CWD], vcw[CWD];
 
-  auto load_ids = [&](const Cursor& c, int64_t t, int& ki, int& vi) {
-    const uint32_t j = row_of(c, t);
+  auto load_ids = [&](const IdCur& c, int t, int& ki, int& vi) {
+    const uint32_t j = row_of(c.s, t);
     ki = c.k_ids[j];
     vi = c.v_ids[j];
   };
-  auto load_data = [&](const Cursor& c, int64_t t, int ki, int vi) {
-    const uint32_t j = row_of(c, t);
+  auto load_data = [&](const DataCur& c, int t, int ki, int vi) {
+    const uint32_t j = row_of(c.s, t);
     kc_r = load_code_bits<KNB>(c.k_codes + (j * uint32_t(DQ * KB / 8) + uint32_t(dg * KNB)));
     vc_r = load_code_bits<VNB>(c.v_codes + (j * uint32_t(DQ * VB / 8) + uint32_t(dg * VNB)));
     km_r = c.k_meta[j * uint32_t(DQ / G) + uint32_t((dg * CH) / G)];
@@ -324,7 +348,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[b][v] = 0.f;
 
-  auto clamp_t = [&](int64_t t) { return t < t_end ? t : t_end - 1; };
+  auto clamp_t = [&](int t) { return t < t_end ? t : t_end - 1; };
 
   // S^T = K_hat Q^T of the K tile in buffer kb_, keys [0, 32) and [32, 64)
   auto qk = [&](int kb_, f32x16 (&sacc)[2]) {
@@ -378,22 +402,26 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
   // matrix cores already form tile t+1's scores, and while tile t's values are
   // multiplied tile t+2 is dequantized.  K tiles t+1, t+2 live in two buffers and
   // V tiles t, t+1, t+2 in three; one barrier per tile publishes tile t+2.
-  Cursor cur_ids, cur_data, cur_comp;
+  IdCur cur_ids;
+  DataCur cur_data;
+  Span cur_comp;
   f32x16 sa[2], sb[2];
   if (t_begin < t_end) {
-    cursor_load(cur_data, 0);
-    cursor_seek(cur_data, t_begin);
-    cur_ids = cur_data;
-    cur_comp = cur_data;
+    data_load(cur_data, 0);
+    data_seek(cur_data, t_begin);
+    ids_load(cur_ids, 0);
+    ids_seek(cur_ids, t_begin);
+    span_load(cur_comp, 0);
+    span_seek(cur_comp, t_begin);
     int k0, v0;
-    load_ids(cur_data, t_begin, k0, v0);
+    load_ids(cur_ids, t_begin, k0, v0);
     load_data(cur_data, t_begin, k0, v0);
-    cursor_seek(cur_ids, clamp_t(t_begin + 1));
+    ids_seek(cur_ids, clamp_t(t_begin + 1));
     load_ids(cur_ids, clamp_t(t_begin + 1), kid_n, vid_n);
     store_tile(0, 0);
-    cursor_seek(cur_data, clamp_t(t_begin + 1));
+    data_seek(cur_data, clamp_t(t_begin + 1));
     load_data(cur_data, clamp_t(t_begin + 1), kid_n, vid_n);
-    cursor_seek(cur_ids, clamp_t(t_begin + 2));
+    ids_seek(cur_ids, clamp_t(t_begin + 2));
     load_ids(cur_ids, clamp_t(t_begin + 2), kid_n, vid_n);
     store_tile(1, 1);
   }
@@ -412,7 +440,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
   // work (tile t's exponentials, then tile t+2's dequantization) and preceded two
   // products earlier by the LDS read of its operand; scheduling fences keep this
   // order, so the matrix cores and the vector unit work side by side.
-  auto step = [&](int64_t t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+  auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
     const int kbuf = int((t - t_begin) & 1);
     auto frag = [&](int f) -> f16x8 {
       if (f < NQK) {          // K fragment: keys (f & 1)*32 + col, channels (f >> 1)*16 + half*8
@@ -435,14 +463,14 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
     fr[0] = frag(0);
     fr[1] = frag(1);
     {
-      const int64_t t2 = clamp_t(t + 2), t3 = clamp_t(t + 3);
-      cursor_seek(cur_data, t2);
+      const int t2 = clamp_t(t + 2), t3 = clamp_t(t + 3);
+      data_seek(cur_data, t2);
       load_data(cur_data, t2, kid_n, vid_n);
-      cursor_seek(cur_ids, t3);
+      ids_seek(cur_ids, t3);
       load_ids(cur_ids, t3, kid_n, vid_n);
     }
-    cursor_seek(cur_comp, t);
-    const int nvalid_left = cur_comp.n_tokens - int(t - cur_comp.tile_begin) * 64;
+    span_seek(cur_comp, t);
+    const int nvalid_left = cur_comp.n_tokens - (t - cur_comp.tile_begin) * 64;
     softmax_prep(cur, nvalid_left >= 64 ? 64 : nvalid_left);
 
     // tile t's exponentials, one pair of scores at a time, as fp16 probabilities;
@@ -518,7 +546,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
     vbuf = vbuf == 2 ? 0 : vbuf + 1;
     __syncthreads();
   };
-  for (int64_t t = t_begin; t < t_end; t += 2) {
+  for (int t = t_begin; t < t_end; t += 2) {
     step(t, sa, sb);
     if (t + 1 < t_end) step(t + 1, sb, sa);
   }
