@@ -655,18 +655,46 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(const float* __restrict_
 }
 
 // Reduced queries q' = U^T q (fp32 accumulation, fp16 result in tile channel order).
-__global__ __launch_bounds__(256) void project_queries_kernel(const uint16_t* __restrict__ q, const float* __restrict__ basis,
-                                                              int64_t n_q, int D, int R, uint16_t* __restrict__ qp) {
-  const int64_t item = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+// One thread per query, R accumulators; the head's basis is staged in LDS and
+// read by all lanes at the same address (broadcast).
+template <int D, int R>
+__global__ __launch_bounds__(256) void project_queries_kernel(const uint16_t* __restrict__ q,
+                                                              const float* __restrict__ basis, int64_t n_q,
+                                                              uint16_t* __restrict__ qp) {
+  __shared__ __attribute__((aligned(16))) float sU[D * R];
   const int h = blockIdx.y;
-  if (item >= n_q * R) return;
-  const int64_t qi = item / R;
-  const int k = int(item % R);
+  const float* Uh = basis + int64_t(h) * D * R;
+  for (int i = threadIdx.x; i < D * R / 4; i += 256)
+    reinterpret_cast<float4*>(sU)[i] = reinterpret_cast<const float4*>(Uh)[i];
+  __syncthreads();
+  const int64_t qi = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (qi >= n_q) return;
   const uint16_t* qr = q + (int64_t(h) * n_q + qi) * D;
-  const float* U = basis + int64_t(h) * D * R;
-  float a = 0.f;
-  for (int i = 0; i < D; ++i) a = fmaf(__uint_as_float(uint32_t(qr[i]) << 16), U[i * R + k], a);
-  qp[(int64_t(h) * n_q + qi) * R + tile_channel(k)] = static_cast<uint16_t>(pack_f16x2(a, 0.f) & 0xffffu);
+  float acc[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) acc[k] = 0.f;
+  for (int c8 = 0; c8 < D / 8; ++c8) {
+    const uint4 w = reinterpret_cast<const uint4*>(qr)[c8];
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float xv = (e & 1) ? bf16_hi(ww[e / 2]) : bf16_lo(ww[e / 2]);
+      const float4* Urow = reinterpret_cast<const float4*>(&sU[(c8 * 8 + e) * R]);
+#pragma unroll
+      for (int k4 = 0; k4 < R / 4; ++k4) {
+        const float4 u = Urow[k4];
+        acc[4 * k4 + 0] = fmaf(xv, u.x, acc[4 * k4 + 0]);
+        acc[4 * k4 + 1] = fmaf(xv, u.y, acc[4 * k4 + 1]);
+        acc[4 * k4 + 2] = fmaf(xv, u.z, acc[4 * k4 + 2]);
+        acc[4 * k4 + 3] = fmaf(xv, u.w, acc[4 * k4 + 3]);
+      }
+    }
+  }
+  // position p holds coefficient tile_channel(p); pairs of positions per word
+  uint32_t* dst = reinterpret_cast<uint32_t*>(qp + (int64_t(h) * n_q + qi) * R);
+#pragma unroll
+  for (int p2 = 0; p2 < R / 2; ++p2)
+    dst[p2] = pack_f16x2(acc[tile_channel(2 * p2)], acc[tile_channel(2 * p2 + 1)]);
 }
 
 // Projected centres c' = U^T c (fp32 accumulation), as an fp16 table in tile
@@ -778,9 +806,14 @@ hipError_t launch_attend(int heads, int64_t n_q, int dim, kvc_dtype q_dtype, con
 hipError_t launch_project_queries(int heads, int64_t n_q, int dim, int rank, const void* q, const float* basis,
                                   uint16_t* q_proj, hipStream_t st) {
   if (heads == 0 || n_q == 0) return hipSuccess;
-  const dim3 grid(unsigned((n_q * rank + 255) / 256), unsigned(heads));
-  hipLaunchKernelGGL(project_queries_kernel, grid, dim3(256), 0, st, static_cast<const uint16_t*>(q), basis, n_q, dim,
-                     rank, q_proj);
+  const dim3 grid(unsigned((n_q + 255) / 256), unsigned(heads));
+  const auto* qb = static_cast<const uint16_t*>(q);
+  if (dim == 128 && rank == 32)
+    hipLaunchKernelGGL((project_queries_kernel<128, 32>), grid, dim3(256), 0, st, qb, basis, n_q, q_proj);
+  else if (dim == 128 && rank == 64)
+    hipLaunchKernelGGL((project_queries_kernel<128, 64>), grid, dim3(256), 0, st, qb, basis, n_q, q_proj);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -90,9 +90,13 @@ __global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, co
 }
 
 // Low-dimensional encode: coefficients a = U^T r of each token in a rank-R basis,
-// then the same quantizer over groups of G coefficients.  One thread per
-// (token, coefficient); R consecutive lanes hold one token.  The basis of the
-// head and the residual rows of the batch are staged in LDS.
+// then the same quantizer over groups of G coefficients.  A workgroup takes 64
+// tokens per pass; a thread computes 4 consecutive coefficients of TT tokens
+// (register tiling: one basis read and TT residual reads feed 4*TT products),
+// each coefficient summed over the channels in ascending order from +0 with the
+// product and the sum rounded separately.  The basis of the head and the
+// residual rows of the pass (transposed, channel-major) are staged in LDS; the
+// G/4 threads of a coefficient group are adjacent lanes.
 template <typename T, int D, int R, int G, int BITS>
 __global__ __launch_bounds__(256) void encode_lowdim_kernel(const T* __restrict__ x, const T* __restrict__ cent,
                                                             const uint8_t* __restrict__ ids, int C, int64_t n,
@@ -100,25 +104,33 @@ __global__ __launch_bounds__(256) void encode_lowdim_kernel(const T* __restrict_
                                                             int tokens_per_block,
                                                             uint8_t* __restrict__ codes,
                                                             uint32_t* __restrict__ meta) {
-  constexpr int TPB = 256 / R;                 // tokens per pass
+  constexpr int TP = 64;                       // tokens per pass
+  constexpr int KQ = R / 4;                    // threads per token (4 coefficients each)
+  constexpr int TS = 256 / KQ;                 // token slots per pass
+  constexpr int TT = TP / TS;                  // tokens per thread
+  constexpr int SR = TP + 1;                   // padded row of the transposed residuals
   constexpr int NG = R / G;
   constexpr int ROW_BYTES = R * BITS / 8;
-  __shared__ float sU[D * R];
-  __shared__ float sR[TPB][D + 4];
+  constexpr int GL = G / 4;                    // lanes of one coefficient group
+  static_assert(TS * TT == TP && KQ <= 64, "thread layout");
+  __shared__ __attribute__((aligned(16))) float sU[D * R];
+  __shared__ float sR[D * SR];
   const int h = blockIdx.y;
   const int64_t j0 = int64_t(blockIdx.x) * tokens_per_block;
   const float* Uh = basis + int64_t(h) * D * R;
-  for (int i = threadIdx.x; i < D * R; i += 256) sU[i] = Uh[i];
+  for (int i = threadIdx.x; i < D * R / 4; i += 256)
+    reinterpret_cast<float4*>(sU)[i] = reinterpret_cast<const float4*>(Uh)[i];
 
-  const int k = threadIdx.x % R;               // coefficient index
-  const int tl = threadIdx.x / R;              // token within the pass
-  for (int p = 0; p < tokens_per_block; p += TPB) {
+  const int kq = threadIdx.x % KQ;             // coefficients 4kq .. 4kq+3
+  const int ts = threadIdx.x / KQ;             // tokens ts*TT .. ts*TT + TT-1 of the pass
+  for (int p = 0; p < tokens_per_block; p += TP) {
     __syncthreads();
-    // stage residual rows: each thread produces D*TPB/256 = D/R channels
-    for (int e = threadIdx.x; e < TPB * (D / 8); e += 256) {
-      const int t = e / (D / 8);
+    // residual rows of the pass, r = fl32(x - c[id]), stored channel-major
+    for (int e = threadIdx.x; e < TP * (D / 8); e += 256) {
       const int c8 = e % (D / 8);
+      const int t = e / (D / 8);
       const int64_t j = j0 + p + t;
+      float rv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       if (j < n) {
         const int64_t tok = int64_t(h) * n + j;
         const int id = ids[tok];
@@ -126,46 +138,63 @@ __global__ __launch_bounds__(256) void encode_lowdim_kernel(const T* __restrict_
         load_row<8>(x + tok * D + c8 * 8, xv);
         load_row<8>(cent + (int64_t(h) * C + id) * D + c8 * 8, cv);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sR[t][c8 * 8 + i] = __fsub_rn(xv[i], cv[i]);
+        for (int i = 0; i < 8; ++i) rv[i] = __fsub_rn(xv[i], cv[i]);
       }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sR[(c8 * 8 + i) * SR + t] = rv[i];
     }
     __syncthreads();
-    const int64_t j = j0 + p + tl;
-    // a_k = sum_i fl(U[i][k] * r[i]), i ascending, from +0
-    float a = 0.0f;
-#pragma unroll 8
-    for (int i = 0; i < D; ++i) a = __fadd_rn(a, __fmul_rn(sU[i * R + k], sR[tl][i]));
-
-    // group min / max across the G lanes holding the group's coefficients
-    float mn = a, mx = a;
+    float a[TT][4];
 #pragma unroll
-    for (int off = 1; off < G; off <<= 1) {
-      mn = fminf(mn, __shfl_xor(mn, off, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    }
-    uint32_t z16 = f32_to_f16_directed(mn, false);
-    if ((z16 & 0x7fffu) == 0) z16 = 0;
-    const float z = f16_bits_to_f32(z16);
-    constexpr float L = float((1 << BITS) - 1);
-    uint32_t s16 = f32_to_f16_directed(__fdiv_rn(__fsub_rn(mx, z), L), true);
-    if ((s16 & 0x7fffu) == 0) s16 = 0;
-    const float s = f16_bits_to_f32(s16);
-    uint32_t q = 0;
-    if (s16 != 0) {
-      const float inv = __fdiv_rn(1.0f, s);
-      float t = rintf(__fmul_rn(__fsub_rn(a, z), inv));
-      q = static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), L));
-    }
-    // pack 32/BITS consecutive coefficients into one word by an OR reduction
-    constexpr int PER_WORD = 32 / BITS;
-    uint32_t wbits = q << (BITS * (k % PER_WORD));
+    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-    for (int off = 1; off < PER_WORD; off <<= 1) wbits |= __shfl_xor(wbits, off, 64);
-    if (j < n) {
-      const int64_t tok = int64_t(h) * n + j;
-      if (k % PER_WORD == 0)
-        reinterpret_cast<uint32_t*>(codes + tok * ROW_BYTES)[k / PER_WORD] = wbits;
-      if (k % G == 0) meta[tok * NG + k / G] = s16 | (z16 << 16);
+      for (int c = 0; c < 4; ++c) a[tt][c] = 0.0f;
+#pragma unroll 4
+    for (int i = 0; i < D; ++i) {
+      const float4 u = *reinterpret_cast<const float4*>(&sU[i * R + 4 * kq]);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const float r = sR[i * SR + ts * TT + tt];
+        a[tt][0] = __fadd_rn(a[tt][0], __fmul_rn(u.x, r));
+        a[tt][1] = __fadd_rn(a[tt][1], __fmul_rn(u.y, r));
+        a[tt][2] = __fadd_rn(a[tt][2], __fmul_rn(u.z, r));
+        a[tt][3] = __fadd_rn(a[tt][3], __fmul_rn(u.w, r));
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      // group min / max across the GL lanes holding the group's coefficients
+      float mn = fminf(fminf(a[tt][0], a[tt][1]), fminf(a[tt][2], a[tt][3]));
+      float mx = fmaxf(fmaxf(a[tt][0], a[tt][1]), fmaxf(a[tt][2], a[tt][3]));
+#pragma unroll
+      for (int off = 1; off < GL; off <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, off, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+      }
+      uint32_t z16 = f32_to_f16_directed(mn, false);
+      if ((z16 & 0x7fffu) == 0) z16 = 0;
+      const float z = f16_bits_to_f32(z16);
+      constexpr float L = float((1 << BITS) - 1);
+      uint32_t s16 = f32_to_f16_directed(__fdiv_rn(__fsub_rn(mx, z), L), true);
+      if ((s16 & 0x7fffu) == 0) s16 = 0;
+      const float s = f16_bits_to_f32(s16);
+      uint32_t bits = 0;
+      if (s16 != 0) {
+        const float inv = __fdiv_rn(1.0f, s);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float t = rintf(__fmul_rn(__fsub_rn(a[tt][c], z), inv));
+          bits |= static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), L)) << (BITS * c);
+        }
+      }
+      const int64_t j = j0 + p + ts * TT + tt;
+      if (j < n) {
+        const int64_t tok = int64_t(h) * n + j;
+        uint8_t* crow = codes + tok * ROW_BYTES;
+        if constexpr (BITS == 2) crow[kq] = static_cast<uint8_t>(bits);
+        else reinterpret_cast<uint16_t*>(crow)[kq] = static_cast<uint16_t>(bits);
+        if (kq % GL == 0) meta[tok * NG + kq / GL] = s16 | (z16 << 16);
+      }
     }
   }
 }
