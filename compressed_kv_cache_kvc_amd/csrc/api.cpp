@@ -303,6 +303,8 @@ kvc_status kvc_attend(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype
     KVC_PTR(out, work, "out");
     KVC_PTR(lse, work, "lse");
     if (!work) return ok();
+    KVC_REQUIRE(heads <= 65535 && (n_q + 255) / 256 * heads <= (int64_t(1) << 27), KVC_ERR_UNSUPPORTED,
+                "at most 65535 heads and 2^27 blocks of 256 queries per call");
     if (sl.total_tiles > 0) {
       KVC_REQUIRE(g == 16 || g == 32, KVC_ERR_UNSUPPORTED, "group must be 16 or 32");
       KVC_REQUIRE(q_dtype == cdt, KVC_ERR_UNSUPPORTED, "queries and centres must share a dtype");
@@ -386,6 +388,8 @@ kvc_status kvc_attend_lowdim(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype 
     KVC_PTR(out, work, "out");
     KVC_PTR(lse, work, "lse");
     if (!work) return ok();
+    KVC_REQUIRE(heads <= 65535 && (n_q + 255) / 256 * heads <= (int64_t(1) << 27), KVC_ERR_UNSUPPORTED,
+                "at most 65535 heads and 2^27 blocks of 256 queries per call");
     if (sl.total_tiles > 0) {
       KVC_REQUIRE(g == 16 || g == 32, KVC_ERR_UNSUPPORTED, "group must be 16 or 32");
       KVC_REQUIRE(cdt == KVC_BF16, KVC_ERR_UNSUPPORTED, "low-dim path needs bf16 centres");

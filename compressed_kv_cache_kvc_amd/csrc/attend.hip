@@ -165,9 +165,22 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
   const int wave = tid >> 6;
   const int half = lane >> 5;
   const int col = lane & 31;
-  const int h = blockIdx.y;
-  const int split = blockIdx.z;
-  const int64_t qi = int64_t(blockIdx.x) * 256 + wave * 32 + col;
+  // Workgroups go to the 8 XCDs in turn (workgroup i to XCD i mod 8). Renumber
+  // them so that each XCD receives a contiguous range of (query block, split,
+  // head) triples, query block fastest: the workgroups that read the same
+  // history tiles then share one XCD's L2.
+  int qb, split, h;
+  {
+    const unsigned nb = gridDim.x, q8 = nb >> 3, r8 = nb & 7;
+    const unsigned xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const unsigned logical = xcd < r8 ? xcd * (q8 + 1) + slot : r8 * (q8 + 1) + (xcd - r8) * q8 + slot;
+    const unsigned nqb = unsigned((p.n_q + 255) >> 8);
+    qb = int(logical % nqb);
+    const unsigned rest = logical / nqb;
+    split = int(rest % unsigned(p.n_split));
+    h = int(rest / unsigned(p.n_split));
+  }
+  const int64_t qi = int64_t(qb) * 256 + wave * 32 + col;
   const bool q_ok = qi < p.n_q;
 
   // B operand Q^T in fp16, channels in tile order: bf16 queries convert exactly
@@ -743,7 +756,7 @@ __global__ __launch_bounds__(256) void centre_tables_kernel(TableJobs jobs) {
 
 template <int DQ, bool LOWDIM, int DOUT>
 hipError_t pick_bits(const AttendParams& p, const SegList& segs, int kb, int vb, int g, hipStream_t st) {
-  const dim3 grid(unsigned((p.n_q + 255) / 256), unsigned(p.heads), unsigned(p.n_split));
+  const dim3 grid(unsigned((p.n_q + 255) / 256) * unsigned(p.heads) * unsigned(p.n_split));
 #define KVC_CASE(KB_, VB_, G_)                                                                               \
   if (kb == KB_ && vb == VB_ && g == G_) {                                                                   \
     hipLaunchKernelGGL((attend_kernel<DQ, KB_, VB_, G_, LOWDIM, DOUT>), grid, dim3(512), 0, st, p, segs); \

@@ -145,7 +145,9 @@ size_t kvc_encode_workspace_bytes(int32_t heads, int64_t n_tokens, int32_t dim,
  *              own centre tables.
  *   out, lse   fp32 outputs.
  *   ws         at least kvc_attend_workspace_bytes(...) bytes (partial results of
- *              the split over history, merged by LSE inside the call). */
+ *              the split over history, merged by LSE inside the call).
+ * Limits: heads <= 65535 and ceil(n_q / 256) * heads <= 2^27 (else
+ * KVC_ERR_UNSUPPORTED); the same limits hold for kvc_attend_lowdim. */
 kvc_status kvc_attend(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype, const void* q,
                       const kvc_segment* segs, int32_t n_segs, float* out, float* lse,
                       void* ws, size_t ws_bytes, hipStream_t stream);
