@@ -151,14 +151,15 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
   constexpr int KC = DQ / 16;     // k-chunks of the QK^T product
   constexpr int NDB = DQ / 32;    // 32-row blocks of O^T
   constexpr int ROWK = DQ + 8;    // padded LDS rows (fp16 elements)
-  // V tile rows (keys) padded so that the transposing reads of a value fragment
-  // hit 64 distinct banks: a row stride of 16 or 48 dwords modulo 64
-  constexpr int ROWV = DQ == 128 ? 160 : DQ == 64 ? 96 : 32;
+  // V tile rows (keys) padded against bank conflicts of the transposing reads
+  // (a row stride of 8, 16 or 48 dwords modulo 64; at DQ = 128 the LDS budget of
+  // four K and five V buffers leaves room for 8)
+  constexpr int ROWV = DQ == 128 ? 144 : DQ == 64 ? 96 : 32;
   constexpr int CH = DQ / 8;      // channels per dequantizing thread
   constexpr int KNB = CH * KB / 8, VNB = CH * VB / 8;
   static_assert(G % CH == 0, "a thread's channels must sit in one group");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][64 * ROWK];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[3][64 * ROWV];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[4][64 * ROWK];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[5][64 * ROWV];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -413,8 +414,10 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
 
   // Software pipeline over tiles: while tile t's exponentials are computed the
   // matrix cores already form tile t+1's scores, and while tile t's values are
-  // multiplied tile t+2 is dequantized.  K tiles t+1, t+2 live in two buffers and
-  // V tiles t, t+1, t+2 in three; one barrier per tile publishes tile t+2.
+  // multiplied tile t+3 is dequantized.  K tiles live in four buffers and V tiles
+  // in five, so that one barrier per two tiles suffices: a tile is written at
+  // least two steps before it is read, and a buffer is rewritten at least two
+  // steps after its last read (the barriers follow every second step).
   IdCur cur_ids;
   DataCur cur_data;
   Span cur_comp;
@@ -437,11 +440,16 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
     ids_seek(cur_ids, clamp_t(t_begin + 2));
     load_ids(cur_ids, clamp_t(t_begin + 2), kid_n, vid_n);
     store_tile(1, 1);
+    data_seek(cur_data, clamp_t(t_begin + 2));
+    load_data(cur_data, clamp_t(t_begin + 2), kid_n, vid_n);
+    ids_seek(cur_ids, clamp_t(t_begin + 3));
+    load_ids(cur_ids, clamp_t(t_begin + 3), kid_n, vid_n);
+    store_tile(2, 2);
   }
   __syncthreads();
   if (t_begin < t_end) qk(0, sa);
 
-  int vbuf = 0;                     // V buffer of tile t; tile t+2 goes to (vbuf + 2) % 3
+  int vbuf = 0;                     // V buffer of tile t; tile t+3 goes to (vbuf + 3) % 5
   constexpr int NQK = 2 * KC;       // score products per tile
   constexpr int NPV = 4 * NDB;      // value products per tile
   constexpr int PPM = 16 / NQK;     // exponential pairs between two score products
@@ -454,11 +462,11 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
   // products earlier by the LDS read of its operand; scheduling fences keep this
   // order, so the matrix cores and the vector unit work side by side.
   auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-    const int kbuf = int((t - t_begin) & 1);
+    const int kbuf = int((t - t_begin) & 3);   // K buffer of tile t
     auto frag = [&](int f) -> f16x8 {
       if (f < NQK) {          // K fragment: keys (f & 1)*32 + col, channels (f >> 1)*16 + half*8
         return as_f16x8(*reinterpret_cast<const uint4*>(
-            &sK[kbuf ^ 1][((f & 1) * 32 + col) * ROWK + (f >> 1) * 16 + half * 8]));
+            &sK[(kbuf + 1) & 3][((f & 1) * 32 + col) * ROWK + (f >> 1) * 16 + half * 8]));
       }
       // V^T fragment for product i = f - NQK: dims (i % NDB)*32 + [0, 32), keys of
       // chunk i / NDB in the order of the probabilities (bits 2 and 3 of the key
@@ -476,11 +484,11 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
     fr[0] = frag(0);
     fr[1] = frag(1);
     {
-      const int t2 = clamp_t(t + 2), t3 = clamp_t(t + 3);
-      data_seek(cur_data, t2);
-      load_data(cur_data, t2, kid_n, vid_n);
-      ids_seek(cur_ids, t3);
-      load_ids(cur_ids, t3, kid_n, vid_n);
+      const int t3 = clamp_t(t + 3), t4 = clamp_t(t + 4);
+      data_seek(cur_data, t3);
+      load_data(cur_data, t3, kid_n, vid_n);
+      ids_seek(cur_ids, t4);
+      load_ids(cur_ids, t4, kid_n, vid_n);
     }
     span_seek(cur_comp, t);
     const int nvalid_left = cur_comp.n_tokens - (t - cur_comp.tile_begin) * 64;
@@ -500,17 +508,18 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
     };
     f16x8 pf[4];
 
-    // tile t+2's dequantization, one channel pair at a time: item j < CH/2 is key
+    // tile t+3's dequantization, one channel pair at a time: item j < CH/2 is key
     // pair j (keys: one rounding of fp32 q*s + z plus the centre), item CH/2 + j
     // value pair j (packed fp16)
-    const int vstore = vbuf == 0 ? 2 : vbuf - 1;
+    const int vstore = vbuf >= 2 ? vbuf - 2 : vbuf + 3;
+    const int kstore = (kbuf + 3) & 3;
     uint32_t kw[CH / 2], vw[CH / 2];
     auto dq_item = [&](int j, const CodePairs<KB, CH>& kq, float ks, float kz, const CodePairs<VB, CH>& vq, h2 vs,
                        h2 vz) {
       if (j < CH / 2) {
         const h2 c = kq.pair(j);
         kw[j] = round_add_f16x2(fmaf(float(c[0]), ks, kz), fmaf(float(c[1]), ks, kz), kcw[j]);
-        uint16_t* kdst = &sK[kbuf][dk * ROWK + dg * CH];
+        uint16_t* kdst = &sK[kstore][dk * ROWK + dg * CH];
         if constexpr (CH == 4) {
           if (j == 1) reinterpret_cast<uint2*>(kdst)[0] = make_uint2(kw[0], kw[1]);
         } else if ((j & 3) == 3) {
@@ -556,12 +565,12 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
       for (int u = 0; u < IPM; ++u) dq_item(i * IPM + u, kq, ks, kz, vq, vs, vz);
       __builtin_amdgcn_sched_barrier(0);
     }
-    vbuf = vbuf == 2 ? 0 : vbuf + 1;
-    __syncthreads();
+    vbuf = vbuf == 4 ? 0 : vbuf + 1;
   };
   for (int t = t_begin; t < t_end; t += 2) {
     step(t, sa, sb);
     if (t + 1 < t_end) step(t + 1, sb, sa);
+    __syncthreads();
   }
 
   // epilogue: normalise, write this split's (out, lse)
