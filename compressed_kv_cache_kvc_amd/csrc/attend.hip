@@ -458,8 +458,8 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
 
   // One tile step.  The matrix products of the step (tile t+1's scores, then tile
   // t's values) are issued one at a time, each followed by its share of the vector
-  // work (tile t's exponentials, then tile t+2's dequantization) and preceded two
-  // products earlier by the LDS read of its operand; scheduling fences keep this
+  // work (tile t's exponentials, then tile t+3's dequantization) and preceded
+  // three products earlier by the LDS read of its operand; scheduling fences keep this
   // order, so the matrix cores and the vector unit work side by side.
   auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
     const int kbuf = int((t - t_begin) & 3);   // K buffer of tile t
@@ -480,9 +480,10 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
       const uint2 lo = lds_read_tr16(base), hi = lds_read_tr16(base + 8 * ROWV);
       return as_f16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
     };
-    f16x8 fr[3];
+    f16x8 fr[4];
     fr[0] = frag(0);
     fr[1] = frag(1);
+    fr[2] = frag(2);
     {
       const int t3 = clamp_t(t + 3), t4 = clamp_t(t + 4);
       data_seek(cur_data, t3);
@@ -539,11 +540,11 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
 
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
-      fr[(i + 2) % 3] = frag(i + 2);
+      fr[(i + 3) & 3] = frag(i + 3);
       if (i < 2)
-        nxt[i] = mfma32h(fr[i % 3], qf[0], f32x16{});
+        nxt[i] = mfma32h(fr[i & 3], qf[0], f32x16{});
       else
-        nxt[i & 1] = mfma32h(fr[i % 3], qf[i >> 1], nxt[i & 1]);
+        nxt[i & 1] = mfma32h(fr[i & 3], qf[i >> 1], nxt[i & 1]);
 #pragma unroll
       for (int u = 0; u < PPM; ++u) exp_pair(i * PPM + u);
       __builtin_amdgcn_sched_barrier(0);
@@ -559,8 +560,8 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
     const h2 vs = scale2(vm_r), vz = zero2(vm_r);
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
-      if (NQK + i + 2 < NQK + NPV) fr[(NQK + i + 2) % 3] = frag(NQK + i + 2);
-      o[i % NDB] = mfma32h(fr[(NQK + i) % 3], pf[i / NDB], o[i % NDB]);
+      if (NQK + i + 3 < NQK + NPV) fr[(NQK + i + 3) & 3] = frag(NQK + i + 3);
+      o[i % NDB] = mfma32h(fr[(NQK + i) & 3], pf[i / NDB], o[i % NDB]);
 #pragma unroll
       for (int u = 0; u < IPM; ++u) dq_item(i * IPM + u, kq, ks, kz, vq, vs, vz);
       __builtin_amdgcn_sched_barrier(0);
