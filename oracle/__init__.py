@@ -17,7 +17,9 @@ video generation):
   section 3.3 Eq. 2 (residual against a prediction, reconstruction = prediction
   + dequantized residual);
 * QuantWM (2609.26425), section 4.1 (k-means assignment of each token to its
-  nearest centre, then quantization of the residual);
+  nearest centre, then quantization of the residual; QSAC, the query-aware
+  choice among the nearest centres, Eqs. 6-12, and its cold start in the
+  appendix);
 * NanoKV (2611.06377), Table 4 (256 centres each for K and V, two k-means
   iterations, one residual stage), Table 5 caption (centres fitted separately
   for K and V) and Figure 4 (mixed-dimensional attention: reduce the queries,
@@ -48,3 +50,4 @@ from .codec import (  # noqa: F401
     storage_bytes,
 )
 from .attention import attend, attend_lowdim, lse_merge, Segment  # noqa: F401
+from .qsac import assign_qsac, query_stats  # noqa: F401
