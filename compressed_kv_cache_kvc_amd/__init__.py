@@ -11,6 +11,8 @@ Entry points (names follow the C ABI):
   attend(q, segments)                       -> (out, lse)
   attend_lowdim(q, basis_k, basis_v, segs)  -> (out, lse)
   lse_merge(outs, lses)                     -> (out, lse)
+  assign_qsac(x, centroids, w, n_cand, group) -> ids          (query-aware key assignment)
+  query_stats(q, w, n_prev)                 -> w              (running E[q_c^2], in place)
 """
 from __future__ import annotations
 
@@ -24,7 +26,7 @@ from . import _lib
 from ._lib import KvcSegment
 
 __all__ = ["KvcError", "Segment", "fit_assign", "encode", "attend", "attend_lowdim", "lse_merge",
-           "library", "version"]
+           "assign_qsac", "query_stats", "library", "version"]
 
 
 class KvcError(RuntimeError):
@@ -106,6 +108,40 @@ def fit_assign(x: torch.Tensor, centroids: torch.Tensor, n_iter: int = 2,
     _check(lib.kvc_fit_assign(H, N, d, _dtype_code(x), _ptr(x), C, _ptr(centroids), n_iter, _ptr(ids),
                               _ptr(ws), wsb, _stream(x.device)))
     return ids
+
+
+# ------------------------------------------------------------------------------ query-aware assignment
+def assign_qsac(x: torch.Tensor, centroids: torch.Tensor, w: Optional[torch.Tensor], n_cand: int, group: int,
+                ids_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """QSAC ids [H, N] (uint8) of key tokens x [H, N, d] against centroids [H, C, d];
+    w [H, d] fp32 channel weights or None (all ones)."""
+    _need(x, "x")
+    H, N, d = x.shape
+    _need(centroids, "centroids", x.device, x.dtype)
+    C = centroids.shape[1]
+    if tuple(centroids.shape) != (H, C, d):
+        raise ValueError("centroids must be [H, C, d]")
+    if w is not None:
+        _need(w, "w", x.device, torch.float32, (H, d))
+    ids = ids_out if ids_out is not None else torch.empty(H, N, dtype=torch.uint8, device=x.device)
+    _need(ids, "ids_out", x.device, torch.uint8, (H, N))
+    _check(library().kvc_assign_qsac(H, N, d, _dtype_code(x), _ptr(x), C, _ptr(centroids), _ptr(w), n_cand, group,
+                                     _ptr(ids), _stream(x.device)))
+    return ids
+
+
+def query_stats(q: torch.Tensor, w: Optional[torch.Tensor] = None, n_prev: int = 0) -> torch.Tensor:
+    """Running per-channel second moments of the queries q [H, n_q, d]: w [H, d]
+    fp32 is updated in place (allocated when None, with n_prev = 0) and returned."""
+    _need(q, "q")
+    H, n_q, d = q.shape
+    if w is None:
+        if n_prev:
+            raise ValueError("n_prev > 0 needs the previous statistics w")
+        w = torch.empty(H, d, dtype=torch.float32, device=q.device)
+    _need(w, "w", q.device, torch.float32, (H, d))
+    _check(library().kvc_query_stats(H, n_q, d, _dtype_code(q), _ptr(q), n_prev, _ptr(w), _stream(q.device)))
+    return w
 
 
 # ------------------------------------------------------------------------------ encode

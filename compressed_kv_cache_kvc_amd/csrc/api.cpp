@@ -223,6 +223,52 @@ kvc_status kvc_fit_assign(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtyp
   }
 }
 
+// ------------------------------------------------------------------------------ query-aware assignment
+kvc_status kvc_assign_qsac(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt, const void* x,
+                           int32_t n_centroids, const void* centroids, const float* w, int32_t n_cand,
+                           int32_t group, uint8_t* ids_out, hipStream_t stream) {
+  try {
+    KVC_REQUIRE(heads >= 0 && n_tokens >= 0, KVC_ERR_INVALID_ARG, "heads and n_tokens must be >= 0");
+    KVC_REQUIRE(heads <= 65535, KVC_ERR_UNSUPPORTED, "at most 65535 heads per call");
+    KVC_REQUIRE(dim == 64 || dim == 128, KVC_ERR_INVALID_ARG, "dim must be 64 or 128");
+    KVC_REQUIRE(valid_dtype(dt), KVC_ERR_INVALID_ARG, "bad dtype");
+    KVC_REQUIRE(n_centroids >= 1 && n_centroids <= 256, KVC_ERR_INVALID_ARG, "n_centroids must be in [1, 256]");
+    KVC_REQUIRE(n_cand >= 1, KVC_ERR_INVALID_ARG, "n_cand must be >= 1");
+    KVC_REQUIRE(n_cand == 1 || n_cand == 2 || n_cand == 4 || n_cand == 8, KVC_ERR_UNSUPPORTED,
+                "n_cand must be 1, 2, 4 or 8");
+    KVC_REQUIRE(group > 0 && dim % group == 0, KVC_ERR_INVALID_ARG, "group must divide dim");
+    KVC_REQUIRE(group == 16 || group == 32, KVC_ERR_UNSUPPORTED, "group must be 16 or 32");
+    const bool work = heads > 0 && n_tokens > 0;
+    KVC_PTR(x, work, "x");
+    KVC_PTR(centroids, work, "centroids");
+    KVC_PTR(ids_out, work, "ids_out");
+    if (w) KVC_PTR(w, work, "w");
+    if (!work) return ok();
+    return hip_status(kvc::launch_assign_qsac(heads, n_tokens, dim, dt, x, n_centroids, centroids, w, n_cand,
+                                              group, ids_out, stream),
+                      "qsac assign");
+  } catch (...) {
+    return fail(KVC_ERR_HIP, "unexpected exception in kvc_assign_qsac");
+  }
+}
+
+kvc_status kvc_query_stats(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype, const void* q,
+                           int64_t n_prev, float* w, hipStream_t stream) {
+  try {
+    KVC_REQUIRE(heads >= 0 && n_q >= 0 && n_prev >= 0, KVC_ERR_INVALID_ARG, "heads, n_q and n_prev must be >= 0");
+    KVC_REQUIRE(heads <= 65535, KVC_ERR_UNSUPPORTED, "at most 65535 heads per call");
+    KVC_REQUIRE(dim == 64 || dim == 128, KVC_ERR_INVALID_ARG, "dim must be 64 or 128");
+    KVC_REQUIRE(valid_dtype(q_dtype), KVC_ERR_INVALID_ARG, "bad dtype");
+    const bool work = heads > 0 && n_q > 0;
+    KVC_PTR(q, work, "q");
+    KVC_PTR(w, work, "w");
+    if (!work) return ok();
+    return hip_status(kvc::launch_query_stats(heads, n_q, dim, q_dtype, q, n_prev, w, stream), "query stats");
+  } catch (...) {
+    return fail(KVC_ERR_HIP, "unexpected exception in kvc_query_stats");
+  }
+}
+
 // ------------------------------------------------------------------------------ encode
 size_t kvc_encode_workspace_bytes(int32_t heads, int64_t n_tokens, int32_t dim, int32_t n_centroids,
                                   int32_t ids_given) {

@@ -54,6 +54,15 @@ hipError_t launch_kmeans_update(int heads, int64_t n, int dim, kvc_dtype dt, con
 size_t kmeans_update_workspace(int heads, int64_t n, int C);
 constexpr int kListChunk = 16384;      // tokens per member-list chunk (ids staged in LDS)
 
+// Query-aware assignment (QSAC) of key tokens; n_cand in {1, 2, 4, 8}, group 16 or 32;
+// w [heads][dim] fp32 or NULL (all ones).
+hipError_t launch_assign_qsac(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C,
+                              const void* cent, const float* w, int n_cand, int group, uint8_t* ids,
+                              hipStream_t st);
+// Running per-channel second moments of the queries (w updated in place).
+hipError_t launch_query_stats(int heads, int64_t n_q, int dim, kvc_dtype dt, const void* q, int64_t n_prev,
+                              float* w, hipStream_t st);
+
 hipError_t launch_lse_merge(int heads, int64_t n_q, int dim, int n_parts, const float* const* outs,
                             const float* const* lses, float* out, float* lse, hipStream_t st);
 hipError_t launch_lse_merge_strided(int heads, int64_t n_q, int dim, int n_parts,

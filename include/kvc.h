@@ -97,8 +97,8 @@ typedef struct {
  *   ids_out    [heads][n_tokens]: argmin over centres of the squared L2 distance,
  *              ties to the lowest index.
  *   ws         workspace of at least kvc_fit_assign_workspace_bytes(...) bytes
- *              (centre norms and the per-centre member lists of the update,
- *              about 2 bytes per token plus 4 per centre and 32768 tokens).
+ *              (the per-centre member lists of the update: 2 bytes per token
+ *              plus 4 per centre and chunk of 16384 tokens).
  * dim must be 64 or 128; n_centroids 1..256; n_tokens >= n_centroids is not
  * required. */
 kvc_status kvc_fit_assign(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt,
@@ -107,6 +107,34 @@ kvc_status kvc_fit_assign(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtyp
                           void* ws, size_t ws_bytes, hipStream_t stream);
 size_t kvc_fit_assign_workspace_bytes(int32_t heads, int64_t n_tokens, int32_t dim,
                                       int32_t n_centroids);
+
+/* Query-aware assignment of key tokens, QSAC (QuantWM, section 4.1, Eqs. 9-12).
+ * Per token x: the n_cand centres nearest in d_w(x, mu) = sum_c w_c (x_c - mu_c)^2
+ * are candidates (ties to the lower index); each is scored by
+ * S = sum_g (sum_{c in g} w_c) (max_{c in g} r_c - min_{c in g} r_c)^2 with
+ * r = x - mu and g the channel groups of the residual codec; the token takes the
+ * smallest score, ties to the lower index.  n_cand = 1 with w = NULL is the plain
+ * nearest-centre assignment.
+ *   x, centroids  [heads][n_tokens][dim] / [heads][n_centroids][dim], dtype dt.
+ *   w          NULL (all channel weights 1: the cold start) or [heads][dim] fp32
+ *              non-negative weights, e.g. from kvc_query_stats.
+ *   n_cand     1, 2, 4 or 8 (others: KVC_ERR_UNSUPPORTED).
+ *   group      16 or 32, dividing dim.
+ *   ids_out    [heads][n_tokens].
+ * bf16 candidate sets are exact (a near tie at the candidate boundary is
+ * re-scored in fp64); candidate scores are fp32 for bf16 and fp64 for fp32
+ * tokens.  No workspace; dim 64 or 128; heads <= 65535. */
+kvc_status kvc_assign_qsac(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt,
+                           const void* x, int32_t n_centroids, const void* centroids,
+                           const float* w, int32_t n_cand, int32_t group, uint8_t* ids_out,
+                           hipStream_t stream);
+
+/* Running second moments of the queries per head and channel (QuantWM, section
+ * 4.1, Eqs. 6-8, diagonal): w <- (n_prev * w + sum_i q_ic^2) / (n_prev + n_q),
+ * summed in fp64.  With n_prev = 0 the previous contents of w are ignored.
+ *   q   [heads][n_q][dim], dtype q_dtype;  w  [heads][dim] fp32, in/out. */
+kvc_status kvc_query_stats(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype,
+                           const void* q, int64_t n_prev, float* w, hipStream_t stream);
 
 /* Encode tokens against their centres (TempoKV, section 3.1 Eq. 1 and section
  * 3.3 Eq. 2).  Per token: r = fl32(x - c[id]); with a basis, r is replaced by

@@ -148,3 +148,30 @@ def test_merge_validation(lib):
     assert f(1, 10, 127, 2, po, po, P, P, None) == INV
     assert f(1, 10, 128, 2, po, po, P, P, None) == INV        # part 1 aliases the output
     assert f(0, 10, 128, 2, po, po, P, P, None) == OK
+
+
+def test_qsac_validation(lib):
+    f = lib.kvc_assign_qsac
+    # (heads, n, dim, dt, x, C, cent, w, n_cand, group, ids, stream)
+    assert f(1, 10, 100, 1, P, 16, P, None, 4, 16, P, None) == INV        # dim
+    assert f(1, 10, 128, 7, P, 16, P, None, 4, 16, P, None) == INV        # dtype
+    assert f(1, 10, 128, 1, P, 0, P, None, 4, 16, P, None) == INV         # C
+    assert f(1, 10, 128, 1, P, 16, P, None, 0, 16, P, None) == INV        # n_cand
+    assert f(1, 10, 128, 1, P, 16, P, None, 3, 16, P, None) == UNS        # n_cand not built
+    assert f(1, 10, 128, 1, P, 16, P, None, 4, 24, P, None) == INV        # group does not divide dim
+    assert f(1, 10, 128, 1, P, 16, P, None, 4, 64, P, None) == UNS        # group not built
+    assert f(1, 10, 128, 1, None, 16, P, None, 4, 16, P, None) == INV     # x NULL
+    assert f(1, 10, 128, 1, MIS, 16, P, None, 4, 16, P, None) == INV      # misaligned
+    assert f(1, 10, 128, 1, P, 16, P, MIS, 4, 16, P, None) == INV         # misaligned weights
+    assert f(70000, 10, 128, 1, P, 16, P, None, 4, 16, P, None) == UNS    # heads
+    assert f(1, 0, 128, 1, None, 16, None, None, 4, 16, None, None) == OK  # empty
+
+
+def test_query_stats_validation(lib):
+    f = lib.kvc_query_stats
+    # (heads, n_q, dim, dt, q, n_prev, w, stream)
+    assert f(1, 10, 100, 1, P, 0, P, None) == INV
+    assert f(1, 10, 128, 9, P, 0, P, None) == INV
+    assert f(1, 10, 128, 1, P, -1, P, None) == INV
+    assert f(1, 10, 128, 1, P, 0, None, None) == INV
+    assert f(1, 0, 128, 1, None, 0, None, None) == OK
