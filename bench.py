@@ -39,6 +39,10 @@ def parse():
                     choices=["self_forcing_layer", "long_history", "larger_backbone", "streaming", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--qsac", type=int, default=0, metavar="M",
+                    help="re-assign the keys after the fit with the query-aware assignment (QuantWM section 4.1) "
+                         "over M candidates, weighted by the statistics of the previous chunks' queries, and "
+                         "update those statistics after the attention (self_forcing_layer, streaming); 0 = off")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the warmup, run one plain fp32 negation of MIB MiB (reads and writes MIB MiB) so "
                          "that a hardware-counter run can scale its byte counters against a kernel of known traffic")
@@ -57,6 +61,9 @@ class Workload:
         self.phase_ms = {}
         self.events = []
         self.side = None
+        self.qsac = 0                 # candidates of the query-aware key assignment (0: plain ids)
+        self.wq = None                # running query statistics [H, d] fp32
+        self.n_seen = 0               # queries folded into wq
 
     def both(self, fk, fv):
         """Run fk() on the current stream and fv() on a second stream (default
@@ -102,12 +109,27 @@ def fit_encode_pair(w, k, kc0, v, vc0, n_iter=2):
     e0 = w.ev()
     kid, vid = w.both(lambda: kvc.fit_assign(k, kc, n_iter=n_iter), lambda: kvc.fit_assign(v, vc, n_iter=n_iter))
     e1 = w.ev()
+    w.mark("fit", e0, e1)
+    if w.qsac:
+        kid = kvc.assign_qsac(k, kc, w.wq, w.qsac, cfg.group)
+        e1b = w.ev()
+        w.mark("qsac", e1, e1b)
+        e1 = e1b
     kco, kme, _ = kvc.encode(k, kc, cfg.k_bits, cfg.group, ids=kid)
     vco, vme, _ = kvc.encode(v, vc, cfg.v_bits, cfg.group, ids=vid)
     e2 = w.ev()
-    w.mark("fit", e0, e1)
     w.mark("encode", e1, e2)
     return (kco, kme, kid, kc), (vco, vme, vid, vc)
+
+
+def update_query_stats(w, q):
+    """Fold the chunk's queries into the running statistics (timed as a phase)."""
+    import compressed_kv_cache_kvc_amd as kvc
+    e0 = w.ev()
+    w.wq = kvc.query_stats(q, w.wq, n_prev=w.n_seen)
+    e1 = w.ev()
+    w.mark("query_stats", e0, e1)
+    w.n_seen += q.shape[1]
 
 
 class SingleLayer(Workload):
@@ -166,7 +188,19 @@ class SingleLayer(Workload):
         out, lse = kvc.attend(self.q, segs)
         e1 = self.ev()
         self.mark("attend", e0, e1)
+        if self.qsac:
+            update_query_stats(self, self.q)
         return out
+
+    def enable_qsac(self, m):
+        """Query-aware key assignment; the statistics start from a previous chunk's queries."""
+        import compressed_kv_cache_kvc_amd as kvc
+        if len(self.bounds) != 2:
+            raise SystemExit("--qsac covers the single-segment workloads (self_forcing_layer, streaming, tiny)")
+        self.qsac = m
+        prev = self.synth.queries(self.cfg, device=self.dev, stream_id=1)
+        self.wq = kvc.query_stats(prev)
+        self.n_seen = prev.shape[1]
 
 
 class LargerBackbone(Workload):
@@ -253,6 +287,8 @@ class Streaming(Workload):
         cfg = self.cfg
         segs = []
         out = None
+        if self.qsac:                 # each rollout starts cold: unit weights for the first chunk
+            self.wq, self.n_seen = None, 0
         for (k, v, q, kc0, vc0) in self.chunks:
             (kcodes, kmeta, kid, kc), (vcodes, vmeta, vid, vc) = fit_encode_pair(self, k, kc0, v, vc0,
                                                                                  n_iter=cfg.n_iter)
@@ -261,7 +297,12 @@ class Streaming(Workload):
             out, lse = kvc.attend(q, segs)
             e1 = self.ev()
             self.mark("attend", e0, e1)
+            if self.qsac:
+                update_query_stats(self, q)
         return out
+
+    def enable_qsac(self, m):
+        self.qsac = m
 
 
 def make_workload(cfg, dev):
@@ -376,6 +417,10 @@ def main():
     kvc.library()
     cfg = synth.get_config(args.workload)
     w = make_workload(cfg, dev)
+    if args.qsac:
+        if not hasattr(w, "enable_qsac"):
+            raise SystemExit("--qsac covers the single-segment workloads (self_forcing_layer, streaming, tiny)")
+        w.enable_qsac(args.qsac)
     torch.cuda.synchronize()
     if args.copy_calibration > 0:
         src = torch.ones(args.copy_calibration * (1 << 18), dtype=torch.float32, device=dev)
@@ -446,6 +491,16 @@ def main():
                      "lse_merge": round(phases.get("lse_merge", 0.0) / K, 4)},
         "roofline": roofline,
     }
+    if w.qsac:
+        # keys re-assigned per step: H*N tokens (all chunks for streaming); the
+        # weighted distances are 2*C*d FLOP per token, the tokens are read once
+        qs = phases.get("qsac", 0.0) / K * 1e-3
+        qtok = w.enc_tokens
+        line["phase_ms"]["qsac"] = round(qs * 1e3, 4)
+        line["phase_ms"]["query_stats"] = round(phases.get("query_stats", 0.0) / K, 4)
+        line["qsac"] = {"n_cand": w.qsac, "tokens_per_s": round(qtok / qs, 1) if qs > 0 else None,
+                        "distance_TFLOPs": round(2.0 * qtok * cfg.n_centroids * cfg.dim / qs / 1e12, 2) if qs else None,
+                        "read_GBps": round(qtok * cfg.dim * (4 if cfg.dtype == "f32" else 2) / qs / 1e9, 1) if qs else None}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -17,8 +17,9 @@
 // the dot product to about 2^-18 relative; the accumulator starts at ||mu_j||_w^2.
 // Each lane keeps its M+1 best (score, index) pairs.  When the gap between the
 // M-th and (M+1)-th score is not larger than twice a bound on the score error,
-// the candidate set is recomputed exactly (fp64 distances of every centre).  The
-// candidates' QSAC scores are computed in fp32.  fp32 tokens take the exact path
+// the candidate set is recomputed exactly: fp64 distances of the centres whose
+// computed score lies within that margin.  The candidates' QSAC scores are
+// computed in fp32.  fp32 tokens take the exact path
 // throughout, with fp64 scores.
 #include "kvc_internal.h"
 #include "dev_common.h"
@@ -157,7 +158,6 @@ __global__ __launch_bounds__(256) void qsac_mfma_kernel(const bf16_t* __restrict
   __shared__ float sN[256];
   __shared__ float sW[D];
   __shared__ float sWg[D / 16];
-  __shared__ double sD[4][256];
 
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
@@ -285,14 +285,87 @@ __global__ __launch_bounds__(256) void qsac_mfma_kernel(const bf16_t* __restrict
     const float thr = err_scale * (xxw + 2.f * cmax);
     const bool flag = valid && C > M && !(top.s[M] - top.s[M - 1] > 2.f * thr);   // also catches NaN
     uint64_t mask = __ballot(flag && half == 0);
-    while (mask) {
-      const int b = __builtin_ctzll(mask);
-      mask &= mask - 1;
-      TopList<double, M> ex;
-      exact_candidates<bf16_t, D, M>(x + (int64_t(h) * n + tok0 + b) * D, centh, sW, C, lane, sD[wave], ex);
-      if (col == b) {
+    if (mask) {
+      // Each computed score is within thr of its exact value, so every centre of
+      // the exact M nearest scores at most 2*thr above the M-th computed score:
+      // this pass's scores are formed once more to mark the centres under that
+      // limit, and only those are re-scored exactly (fp64, dimensions spread over
+      // the lanes, a fixed reduction order).
+      const float lim = top.s[M - 1] + 2.f * thr;
+      uint32_t cm[8];                 // marked rows of block blk: 16 bits per lane
 #pragma unroll
-        for (int k = 0; k < M; ++k) cand[k] = ex.i[k];
+      for (int q = 0; q < 8; ++q) cm[q] = 0;
+      for (int blk = 0; blk < nblk; ++blk) {
+        f32x16 acc;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 t = *reinterpret_cast<const float4*>(&sN[blk * 32 + 8 * g4 + 4 * half]);
+          acc[4 * g4 + 0] = t.x; acc[4 * g4 + 1] = t.y; acc[4 * g4 + 2] = t.z; acc[4 * g4 + 3] = t.w;
+        }
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&sC[(blk * 32 + col) * ROWP + kc * 16 + half * 8]));
+          acc = mfma32(a, bhi[kc], acc);
+          acc = mfma32(a, blo[kc], acc);
+        }
+        uint32_t bits = 0;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) bits |= (acc[v] <= lim ? 1u : 0u) << v;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (q == blk) cm[q] = bits;
+      }
+      constexpr int PERL = D / 64;    // dimensions per lane in the exact re-scoring
+      while (mask) {
+        const int b = __builtin_ctzll(mask);
+        mask &= mask - 1;
+        const uint16_t* xr = reinterpret_cast<const uint16_t*>(x + (int64_t(h) * n + tok0 + b) * D);
+        double xd[PERL], wd[PERL];
+#pragma unroll
+        for (int i = 0; i < PERL; ++i) {
+          xd[i] = double(__uint_as_float(uint32_t(xr[lane * PERL + i]) << 16));
+          wd[i] = double(sW[lane * PERL + i]);
+        }
+        auto exact = [&](int ci) -> double {
+          double part = 0.0;
+#pragma unroll
+          for (int i = 0; i < PERL; ++i) {
+            const double t = xd[i] - double(__uint_as_float(uint32_t(sC[ci * ROWP + lane * PERL + i]) << 16));
+            part = __dadd_rn(part, __dmul_rn(wd[i], __dmul_rn(t, t)));
+          }
+#pragma unroll
+          for (int o = 32; o >= 1; o >>= 1) part = __dadd_rn(part, __shfl_xor(part, o, 64));
+          return part;
+        };
+        TopList<double, M> ex;
+        ex.init();
+        int seen = 0;
+        for (int blk = 0; blk < nblk; ++blk) {
+          uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (q == blk) {
+              w0 = __builtin_amdgcn_readlane(cm[q], b);
+              w1 = __builtin_amdgcn_readlane(cm[q], b + 32);
+            }
+          uint32_t both = w0 | (w1 << 16);   // bit v: row 8*(v/4) + v%4 (+4 for the high half)
+          while (both) {
+            const int bit = __builtin_ctz(both);
+            both &= both - 1;
+            const int v = bit & 15, hh = bit >> 4;
+            const int ci = blk * 32 + 8 * (v / 4) + 4 * hh + (v % 4);
+            ex.insert(exact(ci), ci);
+            ++seen;
+          }
+        }
+        if (seen < M) {               // non-finite scores: every centre, exactly
+          ex.init();
+          for (int ci = 0; ci < C; ++ci) ex.insert(exact(ci), ci);
+        }
+        if (col == b) {
+#pragma unroll
+          for (int k = 0; k < M; ++k) cand[k] = ex.i[k];
+        }
       }
     }
 
@@ -336,31 +409,37 @@ __global__ __launch_bounds__(256) void qsac_mfma_kernel(const bf16_t* __restrict
 
 // Second moments of the queries per head and channel (QuantWM, section 4.1,
 // Eqs. 6-8, diagonal): w <- (n_prev * w + sum_i q_ic^2) / (n_prev + n_q), sums in
-// fp64 over the queries in order (four interleaved partial sums, then combined).
-template <typename T>
-__global__ __launch_bounds__(128) void query_stats_kernel(const T* __restrict__ q, int64_t n_q, int D,
-                                                          int64_t n_prev, float* __restrict__ w) {
-  const int h = blockIdx.y;
-  const int c = blockIdx.x * 128 + threadIdx.x;
-  if (c >= D) return;
+// fp64.  One workgroup per head: 1024 / D row groups, group r summing the rows
+// i = r mod groups in increasing order; the groups' sums are then added in
+// group order (a fixed reduction order).
+template <typename T, int D>
+__global__ __launch_bounds__(1024) void query_stats_kernel(const T* __restrict__ q, int64_t n_q, int64_t n_prev,
+                                                           float* __restrict__ w) {
+  constexpr int RG = 1024 / D;
+  __shared__ double part[RG][D];
+  const int h = blockIdx.x;
+  const int c = threadIdx.x % D, r = threadIdx.x / D;
   const T* qh = q + int64_t(h) * n_q * D;
-  double s[4] = {0.0, 0.0, 0.0, 0.0};
-  int64_t i = 0;
-  for (; i + 4 <= n_q; i += 4) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const double v = elem64<T>(qh + (i + u) * D, c);
-      s[u] = __dadd_rn(s[u], __dmul_rn(v, v));
-    }
+  double s0 = 0.0, s1 = 0.0;
+  int64_t i = r;
+  for (; i + RG < n_q; i += 2 * RG) {
+    const double a = elem64<T>(qh + i * D, c), b = elem64<T>(qh + (i + RG) * D, c);
+    s0 = __dadd_rn(s0, __dmul_rn(a, a));
+    s1 = __dadd_rn(s1, __dmul_rn(b, b));
   }
-  for (; i < n_q; ++i) {
-    const double v = elem64<T>(qh + i * D, c);
-    s[0] = __dadd_rn(s[0], __dmul_rn(v, v));
+  if (i < n_q) {
+    const double a = elem64<T>(qh + i * D, c);
+    s0 = __dadd_rn(s0, __dmul_rn(a, a));
   }
-  double tot = (s[0] + s[1]) + (s[2] + s[3]);
-  float* wc = w + int64_t(h) * D + c;
-  if (n_prev > 0) tot = __dadd_rn(tot, __dmul_rn(double(*wc), double(n_prev)));
-  *wc = float(tot / double(n_prev + n_q));
+  part[r][c] = s0 + s1;
+  __syncthreads();
+  if (r == 0) {
+    double tot = part[0][c];
+    for (int k = 1; k < RG; ++k) tot += part[k][c];
+    float* wc = w + int64_t(h) * D + c;
+    if (n_prev > 0) tot = __dadd_rn(tot, __dmul_rn(double(*wc), double(n_prev)));
+    *wc = float(tot / double(n_prev + n_q));
+  }
 }
 
 template <int D, int M>
@@ -403,13 +482,15 @@ hipError_t launch_assign_qsac(int heads, int64_t n, int dim, kvc_dtype dt, const
 hipError_t launch_query_stats(int heads, int64_t n_q, int dim, kvc_dtype dt, const void* q, int64_t n_prev,
                               float* w, hipStream_t st) {
   if (heads == 0 || n_q == 0) return hipSuccess;
-  const dim3 grid(unsigned((dim + 127) / 128), unsigned(heads));
-  if (dt == KVC_BF16)
-    hipLaunchKernelGGL(query_stats_kernel<bf16_t>, grid, dim3(128), 0, st, static_cast<const bf16_t*>(q), n_q, dim,
-                       n_prev, w);
-  else
-    hipLaunchKernelGGL(query_stats_kernel<float>, grid, dim3(128), 0, st, static_cast<const float*>(q), n_q, dim,
-                       n_prev, w);
+  const dim3 grid(static_cast<unsigned>(heads), 1, 1);
+#define KVC_STATS(T, D) \
+  hipLaunchKernelGGL((query_stats_kernel<T, D>), grid, dim3(1024), 0, st, static_cast<const T*>(q), n_q, n_prev, w)
+  if (dt == KVC_BF16) {
+    if (dim == 128) KVC_STATS(bf16_t, 128); else KVC_STATS(bf16_t, 64);
+  } else {
+    if (dim == 128) KVC_STATS(float, 128); else KVC_STATS(float, 64);
+  }
+#undef KVC_STATS
   return hipGetLastError();
 }
 
