@@ -491,6 +491,18 @@ def main():
                      "lse_merge": round(phases.get("lse_merge", 0.0) / K, 4)},
         "roofline": roofline,
     }
+    if cfg.name == "larger_backbone" and lowdim_ms > 0:
+        # the far part is bound by the softmax's vector work rather than the
+        # matrix cores: one exponential per score; the reference rate is one
+        # exponential per lane and clock (256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz)
+        scores = float(cfg.heads) * cfg.n_q * cfg.far
+        exp_peak = 256 * 4 * 16 * 2.4e9
+        line["lowdim"] = {"ms": round(lowdim_ms, 4),
+                          "TFLOP/s": round((4.0 * cfg.heads * cfg.n_q * cfg.far * cfg.rank
+                                            + 4.0 * cfg.heads * cfg.n_q * cfg.dim * cfg.rank) / (lowdim_ms * 1e-3) / 1e12, 2),
+                          "scores_per_s": round(scores / (lowdim_ms * 1e-3), 1),
+                          "exp_peak_per_s": exp_peak,
+                          "exp_bound_frac": round(scores / (lowdim_ms * 1e-3) / exp_peak, 4)}
     if w.qsac:
         # keys re-assigned per step: H*N tokens (all chunks for streaming); the
         # weighted distances are 2*C*d FLOP per token, the tokens are read once

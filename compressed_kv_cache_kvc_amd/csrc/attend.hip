@@ -146,8 +146,16 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// SEQ (the rank-32 coefficient path): a tile's scores, softmax and values in one
+// step, four wavefronts per SIMD (two workgroups per compute unit) instead of the
+// two-tile overlap inside a wavefront.
+template <int DQ, bool LOWDIM>
+constexpr bool kSeqSchedule = LOWDIM && DQ == 32;
+
 template <int DQ, int KB, int VB, int G, bool LOWDIM, int DOUT>
-__global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList segs) {
+__global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void attend_kernel(AttendParams p, SegList segs) {
+  constexpr bool SEQ = kSeqSchedule<DQ, LOWDIM>;
+  constexpr int NK = SEQ ? 5 : 4;  // K tile buffers
   constexpr int KC = DQ / 16;     // k-chunks of the QK^T product
   constexpr int NDB = DQ / 32;    // 32-row blocks of O^T
   constexpr int ROWK = DQ + 8;    // padded LDS rows (fp16 elements)
@@ -158,7 +166,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
   constexpr int CH = DQ / 8;      // channels per dequantizing thread
   constexpr int KNB = CH * KB / 8, VNB = CH * VB / 8;
   static_assert(G % CH == 0, "a thread's channels must sit in one group");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[4][64 * ROWK];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[NK][64 * ROWK];
   __shared__ __attribute__((aligned(16))) uint16_t sV[5][64 * ROWV];
 
   const int tid = threadIdx.x;
@@ -447,9 +455,11 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
     store_tile(2, 2);
   }
   __syncthreads();
-  if (t_begin < t_end) qk(0, sa);
+  if constexpr (!SEQ)
+    if (t_begin < t_end) qk(0, sa);
 
   int vbuf = 0;                     // V buffer of tile t; tile t+3 goes to (vbuf + 3) % 5
+  int kbuf = 0;                     // K buffer of tile t; tile t+3 goes to (kbuf + 3) % NK
   constexpr int NQK = 2 * KC;       // score products per tile
   constexpr int NPV = 4 * NDB;      // value products per tile
   constexpr int PPM = 16 / NQK;     // exponential pairs between two score products
@@ -462,11 +472,12 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
   // three products earlier by the LDS read of its operand; scheduling fences keep this
   // order, so the matrix cores and the vector unit work side by side.
   auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-    const int kbuf = int((t - t_begin) & 3);   // K buffer of tile t
+    // the K tile scored in this step: t+1, or t itself in the SEQ schedule
+    const int kread = SEQ ? kbuf : (kbuf == NK - 1 ? 0 : kbuf + 1);
     auto frag = [&](int f) -> f16x8 {
       if (f < NQK) {          // K fragment: keys (f & 1)*32 + col, channels (f >> 1)*16 + half*8
         return as_f16x8(*reinterpret_cast<const uint4*>(
-            &sK[(kbuf + 1) & 3][((f & 1) * 32 + col) * ROWK + (f >> 1) * 16 + half * 8]));
+            &sK[kread][((f & 1) * 32 + col) * ROWK + (f >> 1) * 16 + half * 8]));
       }
       // V^T fragment for product i = f - NQK: dims (i % NDB)*32 + [0, 32), keys of
       // chunk i / NDB in the order of the probabilities (bits 2 and 3 of the key
@@ -493,7 +504,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
     }
     span_seek(cur_comp, t);
     const int nvalid_left = cur_comp.n_tokens - (t - cur_comp.tile_begin) * 64;
-    softmax_prep(cur, nvalid_left >= 64 ? 64 : nvalid_left);
+    if constexpr (!SEQ) softmax_prep(cur, nvalid_left >= 64 ? 64 : nvalid_left);
 
     // tile t's exponentials, one pair of scores at a time, as fp16 probabilities;
     // the row sum is taken over the same rounded values
@@ -513,7 +524,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
     // pair j (keys: one rounding of fp32 q*s + z plus the centre), item CH/2 + j
     // value pair j (packed fp16)
     const int vstore = vbuf >= 2 ? vbuf - 2 : vbuf + 3;
-    const int kstore = (kbuf + 3) & 3;
+    const int kstore = kbuf + 3 < NK ? kbuf + 3 : kbuf + 3 - NK;
     uint32_t kw[CH / 2], vw[CH / 2];
     auto dq_item = [&](int j, const CodePairs<KB, CH>& kq, float ks, float kz, const CodePairs<VB, CH>& vq, h2 vs,
                        h2 vz) {
@@ -538,16 +549,31 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
       }
     };
 
+    if constexpr (SEQ) {
+      // tile t's scores, then its softmax and exponentials
 #pragma unroll
-    for (int i = 0; i < NQK; ++i) {
-      fr[(i + 3) & 3] = frag(i + 3);
-      if (i < 2)
-        nxt[i] = mfma32h(fr[i & 3], qf[0], f32x16{});
-      else
-        nxt[i & 1] = mfma32h(fr[i & 3], qf[i >> 1], nxt[i & 1]);
+      for (int i = 0; i < NQK; ++i) {
+        fr[(i + 3) & 3] = frag(i + 3);
+        if (i < 2)
+          cur[i] = mfma32h(fr[i & 3], qf[0], f32x16{});
+        else
+          cur[i & 1] = mfma32h(fr[i & 3], qf[i >> 1], cur[i & 1]);
+      }
+      softmax_prep(cur, nvalid_left >= 64 ? 64 : nvalid_left);
 #pragma unroll
-      for (int u = 0; u < PPM; ++u) exp_pair(i * PPM + u);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int k = 0; k < 16; ++k) exp_pair(k);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NQK; ++i) {
+        fr[(i + 3) & 3] = frag(i + 3);
+        if (i < 2)
+          nxt[i] = mfma32h(fr[i & 3], qf[0], f32x16{});
+        else
+          nxt[i & 1] = mfma32h(fr[i & 3], qf[i >> 1], nxt[i & 1]);
+#pragma unroll
+        for (int u = 0; u < PPM; ++u) exp_pair(i * PPM + u);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     l_run += psum;
 #pragma unroll
@@ -567,10 +593,16 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttendParams p, SegList 
       __builtin_amdgcn_sched_barrier(0);
     }
     vbuf = vbuf == 4 ? 0 : vbuf + 1;
+    kbuf = kbuf == NK - 1 ? 0 : kbuf + 1;
   };
   for (int t = t_begin; t < t_end; t += 2) {
-    step(t, sa, sb);
-    if (t + 1 < t_end) step(t + 1, sb, sa);
+    if constexpr (SEQ) {
+      step(t, sa, sa);
+      if (t + 1 < t_end) step(t + 1, sa, sa);
+    } else {
+      step(t, sa, sb);
+      if (t + 1 < t_end) step(t + 1, sb, sa);
+    }
     __syncthreads();
   }
 
