@@ -150,7 +150,8 @@ def encode(x: torch.Tensor, centroids: torch.Tensor, bits: int, group: int,
            codes_out: Optional[torch.Tensor] = None, meta_out: Optional[torch.Tensor] = None):
     """Encode [H, N, d] tokens against [H, C, d] centres.  Returns (codes uint8
     [H, N, code_dim*bits/8], meta uint16 [H, N, code_dim/group, 2] (fp16 bits of
-    scale, zero), ids uint8 [H, N]).  Without ``ids`` the assignment runs first."""
+    scale, zero), ids uint8 [H, N]).  Without ``ids`` the assignment runs first.
+    bits=16 stores the fp16 residual itself (full dimension) and returns meta None."""
     _need(x, "x")
     H, N, d = x.shape
     _need(centroids, "centroids", x.device, x.dtype)
@@ -166,10 +167,13 @@ def encode(x: torch.Tensor, centroids: torch.Tensor, bits: int, group: int,
     code_dim = rank or d
     codes = codes_out if codes_out is not None else torch.empty(
         H, N, code_dim * bits // 8, dtype=torch.uint8, device=x.device)
-    meta = meta_out if meta_out is not None else torch.empty(
-        H, N, code_dim // group, 2, dtype=torch.uint16, device=x.device)
     _need(codes, "codes_out", x.device, torch.uint8, (H, N, code_dim * bits // 8))
-    _need(meta, "meta_out", x.device, torch.uint16, (H, N, code_dim // group, 2))
+    if bits == 16:
+        meta = None
+    else:
+        meta = meta_out if meta_out is not None else torch.empty(
+            H, N, code_dim // group, 2, dtype=torch.uint16, device=x.device)
+        _need(meta, "meta_out", x.device, torch.uint16, (H, N, code_dim // group, 2))
     lib = library()
     if ids is None:
         ids_out = torch.empty(H, N, dtype=torch.uint8, device=x.device)
@@ -191,7 +195,7 @@ def encode(x: torch.Tensor, centroids: torch.Tensor, bits: int, group: int,
 class Segment:
     """One run of encoded history (all heads) with its own centre tables."""
     k_codes: torch.Tensor     # [H, n, code_dim*k_bits/8] uint8
-    k_meta: torch.Tensor      # [H, n, code_dim/group, 2] uint16
+    k_meta: Optional[torch.Tensor]  # [H, n, code_dim/group, 2] uint16; None for 16-bit residuals
     k_ids: torch.Tensor       # [H, n] uint8
     k_cent: torch.Tensor      # [H, C, d]
     v_codes: torch.Tensor
@@ -218,6 +222,9 @@ class Segment:
         s.cent_dtype = _dtype_code(self.k_cent)
         for name in ("k_codes", "v_codes", "k_meta", "v_meta", "k_ids", "v_ids", "k_cent", "v_cent"):
             t = getattr(self, name)
+            if t is None and name.endswith("_meta"):
+                setattr(s, name, None)       # 16-bit residual segments carry no metadata
+                continue
             _need(t, name)
             setattr(s, name, t.data_ptr())
         return s

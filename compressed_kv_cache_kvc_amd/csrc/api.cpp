@@ -54,18 +54,31 @@ size_t dtype_size(kvc_dtype d) { return d == KVC_F32 ? 4 : 2; }
 
 int64_t tiles_of(int64_t n) { return (n + kvc::kAttendTile - 1) / kvc::kAttendTile; }
 
-// Validate a segment list for attention; fills the device list.
+// Codec of a segment: what one attention kernel instantiation handles.
+struct CodecKey {
+  int kb, vb, g;
+  kvc_dtype cdt;
+  bool operator==(const CodecKey& o) const { return kb == o.kb && vb == o.vb && g == o.g && cdt == o.cdt; }
+};
+
+CodecKey codec_of(const kvc_segment& s) {
+  // 16-bit residual segments have no groups: one nominal group value
+  return CodecKey{s.k_bits, s.v_bits, s.k_bits == 16 ? 16 : s.group, s.cent_dtype};
+}
+
+// Validate a segment list for attention; fills the device list with every
+// non-empty segment (tiles numbered across the whole list) and, per device
+// segment, the index of its codec among the distinct codecs of the call (in order
+// of first appearance).  Without allow_mixed every segment must share one codec.
 kvc_status check_segments(int32_t heads, int32_t dim, const kvc_segment* segs, int32_t n_segs,
-                          int32_t want_rank, kvc::SegList* out, int* kb, int* vb, int* g,
-                          kvc_dtype* cdt) {
+                          int32_t want_rank, bool allow_mixed, kvc::SegList* out, CodecKey* codecs,
+                          int* n_codecs, int* codec_of_seg) {
   KVC_REQUIRE(n_segs >= 0, KVC_ERR_INVALID_ARG, "n_segs < 0");
   KVC_REQUIRE(n_segs == 0 || segs != nullptr, KVC_ERR_INVALID_ARG, "segs is NULL");
   KVC_REQUIRE(n_segs <= kvc::kMaxSegs, KVC_ERR_UNSUPPORTED, "at most %d segments per call", kvc::kMaxSegs);
   out->n = 0;
   out->total_tiles = 0;
-  *kb = *vb = *g = 0;
-  *cdt = KVC_BF16;
-  bool first = true;
+  *n_codecs = 0;
   for (int i = 0; i < n_segs; ++i) {
     const kvc_segment& s = segs[i];
     KVC_REQUIRE(s.n_tokens >= 0, KVC_ERR_INVALID_ARG, "segment %d: n_tokens < 0", i);
@@ -75,29 +88,36 @@ kvc_status check_segments(int32_t heads, int32_t dim, const kvc_segment* segs, i
     KVC_REQUIRE(s.rank == want_rank, KVC_ERR_INVALID_ARG, "segment %d: rank %d, expected %d", i, s.rank,
                 want_rank);
     const int code_dim = want_rank ? want_rank : dim;
-    KVC_REQUIRE(s.k_bits == 2 || s.k_bits == 4, KVC_ERR_INVALID_ARG, "segment %d: k_bits must be 2 or 4", i);
-    KVC_REQUIRE(s.v_bits == 2 || s.v_bits == 4, KVC_ERR_INVALID_ARG, "segment %d: v_bits must be 2 or 4", i);
-    KVC_REQUIRE(s.group > 0 && code_dim % s.group == 0, KVC_ERR_INVALID_ARG,
+    const bool raw = s.k_bits == 16 || s.v_bits == 16;
+    KVC_REQUIRE(s.k_bits == 2 || s.k_bits == 4 || s.k_bits == 16, KVC_ERR_INVALID_ARG,
+                "segment %d: k_bits must be 2, 4 or 16", i);
+    KVC_REQUIRE(s.v_bits == 2 || s.v_bits == 4 || s.v_bits == 16, KVC_ERR_INVALID_ARG,
+                "segment %d: v_bits must be 2, 4 or 16", i);
+    KVC_REQUIRE(!raw || (s.k_bits == 16 && s.v_bits == 16 && want_rank == 0), KVC_ERR_UNSUPPORTED,
+                "segment %d: 16-bit residuals need k_bits = v_bits = 16 and full dimension", i);
+    KVC_REQUIRE(raw || (s.group > 0 && code_dim % s.group == 0), KVC_ERR_INVALID_ARG,
                 "segment %d: group %d does not divide %d", i, s.group, code_dim);
     KVC_REQUIRE(s.n_centroids >= 1 && s.n_centroids <= 256, KVC_ERR_INVALID_ARG,
                 "segment %d: n_centroids must be in [1, 256]", i);
     KVC_REQUIRE(valid_dtype(s.cent_dtype), KVC_ERR_INVALID_ARG, "segment %d: bad centre dtype", i);
     if (s.n_tokens == 0) continue;
-    if (first) {
-      *kb = s.k_bits; *vb = s.v_bits; *g = s.group; *cdt = s.cent_dtype;
-      first = false;
-    } else {
-      KVC_REQUIRE(s.k_bits == *kb && s.v_bits == *vb && s.group == *g && s.cent_dtype == *cdt,
-                  KVC_ERR_UNSUPPORTED, "segment %d: all segments of a call must share bits, group and centre dtype", i);
+    const CodecKey key = codec_of(s);
+    int ci = 0;
+    while (ci < *n_codecs && !(codecs[ci] == key)) ++ci;
+    if (ci == *n_codecs) {
+      KVC_REQUIRE(allow_mixed || *n_codecs == 0, KVC_ERR_UNSUPPORTED,
+                  "segment %d: all segments of a call must share bits, group and centre dtype", i);
+      codecs[(*n_codecs)++] = key;
     }
     KVC_PTR(s.k_codes, true, "segment k_codes");
     KVC_PTR(s.v_codes, true, "segment v_codes");
-    KVC_PTR(s.k_meta, true, "segment k_meta");
-    KVC_PTR(s.v_meta, true, "segment v_meta");
+    KVC_PTR(s.k_meta, !raw, "segment k_meta");
+    KVC_PTR(s.v_meta, !raw, "segment v_meta");
     KVC_PTR(s.k_ids, true, "segment k_ids");
     KVC_PTR(s.v_ids, true, "segment v_ids");
     KVC_PTR(s.k_cent, true, "segment k_cent");
     KVC_PTR(s.v_cent, true, "segment v_cent");
+    codec_of_seg[out->n] = ci;
     kvc::SegDev& d = out->s[out->n++];
     d.n_tokens = s.n_tokens;
     d.tile_begin = out->total_tiles;
@@ -116,6 +136,40 @@ kvc_status check_segments(int32_t heads, int32_t dim, const kvc_segment* segs, i
   }
   (void)heads;
   return ok();
+}
+
+// The segments of one codec, tiles renumbered from 0.
+kvc::SegList codec_subset(const kvc::SegList& all, const int* codec_of_seg, int ci) {
+  kvc::SegList sl;
+  sl.n = 0;
+  sl.total_tiles = 0;
+  for (int i = 0; i < all.n; ++i) {
+    if (codec_of_seg[i] != ci) continue;
+    sl.s[sl.n] = all.s[i];
+    sl.s[sl.n].tile_begin = sl.total_tiles;
+    sl.total_tiles += tiles_of(all.s[i].n_tokens);
+    ++sl.n;
+  }
+  return sl;
+}
+
+// Partial results of a full-dim bf16 attention call: the splits of every codec's
+// launch (one launch per distinct codec), merged by LSE at the end.
+int attend_parts(int32_t heads, int64_t n_q, const kvc_segment* segs, int32_t n_segs) {
+  CodecKey keys[kvc::kMaxSegs];
+  int64_t tiles[kvc::kMaxSegs];
+  int n = 0;
+  for (int i = 0; segs != nullptr && i < n_segs && i < kvc::kMaxSegs; ++i) {
+    if (segs[i].n_tokens <= 0) continue;
+    const CodecKey key = codec_of(segs[i]);
+    int ci = 0;
+    while (ci < n && !(keys[ci] == key)) ++ci;
+    if (ci == n) { keys[n] = key; tiles[n] = 0; ++n; }
+    tiles[ci] += tiles_of(segs[i].n_tokens);
+  }
+  int parts = 0;
+  for (int ci = 0; ci < n; ++ci) parts += kvc::attend_split_plan(heads, n_q, tiles[ci], kvc::kAttendRows);
+  return parts > 0 ? parts : 1;
 }
 
 int64_t total_tokens(const kvc_segment* segs, int32_t n_segs) {
@@ -285,12 +339,16 @@ kvc_status kvc_encode(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt
     KVC_REQUIRE(dim == 64 || dim == 128, KVC_ERR_INVALID_ARG, "dim must be 64 or 128");
     KVC_REQUIRE(valid_dtype(dt), KVC_ERR_INVALID_ARG, "bad dtype");
     KVC_REQUIRE(n_centroids >= 1 && n_centroids <= 256, KVC_ERR_INVALID_ARG, "n_centroids must be in [1, 256]");
-    KVC_REQUIRE(bits == 2 || bits == 4, KVC_ERR_INVALID_ARG, "bits must be 2 or 4");
+    KVC_REQUIRE(bits == 2 || bits == 4 || bits == 16, KVC_ERR_INVALID_ARG, "bits must be 2, 4 or 16");
     KVC_REQUIRE((basis == nullptr) == (rank == 0), KVC_ERR_INVALID_ARG, "rank must be 0 exactly when basis is NULL");
     const int code_dim = rank ? rank : dim;
-    KVC_REQUIRE(rank == 0 || (rank >= group && rank <= dim), KVC_ERR_INVALID_ARG, "rank must be 0 or in [group, dim]");
-    KVC_REQUIRE(group > 0 && code_dim % group == 0, KVC_ERR_INVALID_ARG, "group must divide the coded dimension");
-    KVC_REQUIRE(group == 16 || group == 32, KVC_ERR_UNSUPPORTED, "group must be 16 or 32");
+    const bool raw = bits == 16;      // fp16 residuals: no groups, no metadata
+    KVC_REQUIRE(!raw || rank == 0, KVC_ERR_UNSUPPORTED, "16-bit residuals are full-dimensional only");
+    KVC_REQUIRE(raw || rank == 0 || (rank >= group && rank <= dim), KVC_ERR_INVALID_ARG,
+                "rank must be 0 or in [group, dim]");
+    KVC_REQUIRE(raw || (group > 0 && code_dim % group == 0), KVC_ERR_INVALID_ARG,
+                "group must divide the coded dimension");
+    KVC_REQUIRE(raw || group == 16 || group == 32, KVC_ERR_UNSUPPORTED, "group must be 16 or 32");
     KVC_REQUIRE(rank == 0 || ((rank == 32 || rank == 64) && dim == 128), KVC_ERR_UNSUPPORTED,
                 "coefficient codes need dim 128 and rank 32 or 64");
     KVC_REQUIRE(ids_out == nullptr || ids_out != ids_in, KVC_ERR_INVALID_ARG, "ids_out must not alias ids_in");
@@ -298,7 +356,7 @@ kvc_status kvc_encode(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt
     KVC_PTR(x, work, "x");
     KVC_PTR(centroids, work, "centroids");
     KVC_PTR(codes, work, "codes");
-    KVC_PTR(meta, work, "meta");
+    KVC_PTR(meta, work && !raw, "meta");
     KVC_PTR(basis, work && rank > 0, "basis");
     if (ids_in) KVC_PTR(ids_in, work, "ids_in");
     if (ids_out) KVC_PTR(ids_out, work, "ids_out");
@@ -328,8 +386,8 @@ size_t kvc_attend_workspace_bytes(int32_t heads, int64_t n_q, int32_t dim, kvc_d
                                   const kvc_segment* segs, int32_t n_segs) {
   if (heads <= 0 || n_q <= 0 || (dim != 64 && dim != 128)) return 0;
   if (q_dtype == KVC_F32) return 0;  // the fp32 path reads the fp32 centres and does not split
-  const int s = kvc::attend_split_plan(heads, n_q, total_tiles_of(segs, n_segs), kvc::kAttendRows);
-  return split_bytes(heads, n_q, dim, s) + table_bytes(heads, dim, segs, n_segs);
+  const int parts = attend_parts(heads, n_q, segs, n_segs);
+  return split_bytes(heads, n_q, dim, parts) + table_bytes(heads, dim, segs, n_segs);
 }
 
 kvc_status kvc_attend(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype, const void* q,
@@ -340,9 +398,11 @@ kvc_status kvc_attend(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype
     KVC_REQUIRE(dim == 64 || dim == 128, KVC_ERR_INVALID_ARG, "dim must be 64 or 128");
     KVC_REQUIRE(valid_dtype(q_dtype), KVC_ERR_INVALID_ARG, "bad q dtype");
     kvc::SegList sl;
-    int kb, vb, g;
-    kvc_dtype cdt;
-    kvc_status st = check_segments(heads, dim, segs, n_segs, 0, &sl, &kb, &vb, &g, &cdt);
+    CodecKey codecs[kvc::kMaxSegs];
+    int n_codecs = 0;
+    int codec_of_seg[kvc::kMaxSegs];
+    kvc_status st = check_segments(heads, dim, segs, n_segs, 0, /*allow_mixed=*/true, &sl, codecs, &n_codecs,
+                                   codec_of_seg);
     if (st != KVC_OK) return st;
     const bool work = heads > 0 && n_q > 0;
     KVC_PTR(q, work, "q");
@@ -351,50 +411,73 @@ kvc_status kvc_attend(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype
     if (!work) return ok();
     KVC_REQUIRE(heads <= 65535 && (n_q + 255) / 256 * heads <= (int64_t(1) << 27), KVC_ERR_UNSUPPORTED,
                 "at most 65535 heads and 2^27 blocks of 256 queries per call");
-    if (sl.total_tiles > 0) {
-      KVC_REQUIRE(g == 16 || g == 32, KVC_ERR_UNSUPPORTED, "group must be 16 or 32");
-      KVC_REQUIRE(q_dtype == cdt, KVC_ERR_UNSUPPORTED, "queries and centres must share a dtype");
+    for (int ci = 0; ci < n_codecs; ++ci) {
+      KVC_REQUIRE(codecs[ci].g == 16 || codecs[ci].g == 32, KVC_ERR_UNSUPPORTED, "group must be 16 or 32");
+      KVC_REQUIRE(q_dtype == codecs[ci].cdt, KVC_ERR_UNSUPPORTED, "queries and centres must share a dtype");
     }
-    int n_split = 1;
-    size_t need = 0;
-    if (q_dtype == KVC_BF16) {
-      n_split = kvc::attend_split_plan(heads, n_q, sl.total_tiles, kvc::kAttendRows);
-      need = split_bytes(heads, n_q, dim, n_split) + table_bytes(heads, dim, segs, n_segs);
+    if (q_dtype == KVC_F32) {
+      // fp32 queries: one launch over the fp32 centres (a single 2/4-bit codec)
+      KVC_REQUIRE(n_codecs <= 1, KVC_ERR_UNSUPPORTED, "fp32 queries need one codec for all segments");
+      KVC_REQUIRE(n_codecs == 0 || codecs[0].kb != 16, KVC_ERR_UNSUPPORTED,
+                  "fp32 queries do not read 16-bit residual segments");
+      const CodecKey c = n_codecs ? codecs[0] : CodecKey{2, 2, 16, KVC_F32};
+      return hip_status(kvc::launch_attend(heads, n_q, dim, q_dtype, q, sl, c.kb, c.vb, c.g, c.cdt, 1, out, lse,
+                                           stream),
+                        "attend");
     }
+    // bf16 queries: one launch per codec of the segment list, each split over the
+    // history as planned; all partial results are merged by LSE at the end
+    int split_of[kvc::kMaxSegs];
+    int parts = 0;
+    kvc::SegList sub[kvc::kMaxSegs];
+    for (int ci = 0; ci < n_codecs; ++ci) {
+      sub[ci] = codec_subset(sl, codec_of_seg, ci);
+      split_of[ci] = kvc::attend_split_plan(heads, n_q, sub[ci].total_tiles, kvc::kAttendRows);
+      parts += split_of[ci];
+    }
+    if (parts == 0) parts = 1;
+    const size_t need = split_bytes(heads, n_q, dim, parts) + table_bytes(heads, dim, segs, n_segs);
     KVC_REQUIRE(ws_bytes >= need, KVC_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
     if (need) KVC_PTR(ws, true, "ws");
     char* w = static_cast<char*>(ws);
     float* part_out = out;
     float* part_lse = lse;
-    if (n_split > 1) {
+    if (parts > 1) {
       part_out = reinterpret_cast<float*>(w);
-      w += align_up(size_t(n_split) * heads * n_q * dim * 4);
+      w += align_up(size_t(parts) * heads * n_q * dim * 4);
       part_lse = reinterpret_cast<float*>(w);
-      w += align_up(size_t(n_split) * heads * n_q * 4);
+      w += align_up(size_t(parts) * heads * n_q * 4);
     }
-    if (q_dtype == KVC_BF16) {
-      // fp16 centre tables in the attention tiles' channel order
-      int di = 0;
-      for (int i = 0; i < n_segs; ++i) {
-        if (segs[i].n_tokens == 0) continue;
-        const int C = segs[i].n_centroids;
-        const size_t tb = align_up(size_t(heads) * C * dim * 2);
-        auto* kt = reinterpret_cast<uint16_t*>(w);
-        auto* vt = reinterpret_cast<uint16_t*>(w + tb);
-        w += 2 * tb;
-        sl.s[di].k_tab = kt;
-        sl.s[di].v_tab = vt;
-        ++di;
-      }
-      hipError_t e = kvc::launch_centre_tables(heads, dim, sl, stream);
-      if (e != hipSuccess) return hip_status(e, "centre tables");
+    // fp16 centre tables in the attention tiles' channel order, every segment in one launch
+    for (int i = 0; i < sl.n; ++i) {
+      const size_t tb = align_up(size_t(heads) * size_t(sl.s[i].n_centroids) * dim * 2);
+      sl.s[i].k_tab = reinterpret_cast<uint16_t*>(w);
+      sl.s[i].v_tab = reinterpret_cast<uint16_t*>(w + tb);
+      w += 2 * tb;
     }
-    hipError_t e = kvc::launch_attend(heads, n_q, dim, q_dtype, q, sl, kb, vb, g, cdt, n_split, part_out, part_lse,
-                                      stream);
-    if (e != hipSuccess) return hip_status(e, "attend");
-    if (n_split > 1) {
-      e = kvc::launch_lse_merge_strided(heads, n_q, dim, n_split, part_out, part_lse, out, lse, stream);
-      if (e != hipSuccess) return hip_status(e, "split merge");
+    hipError_t e = kvc::launch_centre_tables(heads, dim, sl, stream);
+    if (e != hipSuccess) return hip_status(e, "centre tables");
+    if (n_codecs == 0) {
+      // empty history: out = 0, lse = -inf
+      e = kvc::launch_attend(heads, n_q, dim, q_dtype, q, sl, 2, 2, 16, KVC_BF16, 1, out, lse, stream);
+      return hip_status(e, "attend");
+    }
+    const int64_t rows = int64_t(heads) * n_q;
+    int slot = 0;
+    for (int ci = 0; ci < n_codecs; ++ci) {
+      kvc::SegList& g = sub[ci];
+      for (int i = 0, j = 0; i < sl.n; ++i)
+        if (codec_of_seg[i] == ci) { g.s[j].k_tab = sl.s[i].k_tab; g.s[j].v_tab = sl.s[i].v_tab; ++j; }
+      float* po = parts > 1 ? part_out + slot * rows * dim : out;
+      float* pl = parts > 1 ? part_lse + slot * rows : lse;
+      e = kvc::launch_attend(heads, n_q, dim, q_dtype, q, g, codecs[ci].kb, codecs[ci].vb, codecs[ci].g,
+                             codecs[ci].cdt, split_of[ci], po, pl, stream);
+      if (e != hipSuccess) return hip_status(e, "attend");
+      slot += split_of[ci];
+    }
+    if (parts > 1) {
+      e = kvc::launch_lse_merge_strided(heads, n_q, dim, parts, part_out, part_lse, out, lse, stream);
+      if (e != hipSuccess) return hip_status(e, "partial merge");
     }
     return ok();
   } catch (...) {
@@ -423,9 +506,11 @@ kvc_status kvc_attend_lowdim(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype 
     KVC_REQUIRE(dim == 128 && (rank == 32 || rank == 64), KVC_ERR_UNSUPPORTED, "low-dim path needs dim 128, rank 32 or 64");
     KVC_REQUIRE(q_dtype == KVC_BF16, KVC_ERR_UNSUPPORTED, "low-dim path needs bf16 queries");
     kvc::SegList sl;
-    int kb, vb, g;
-    kvc_dtype cdt;
-    kvc_status st = check_segments(heads, dim, segs, n_segs, rank, &sl, &kb, &vb, &g, &cdt);
+    CodecKey codecs[kvc::kMaxSegs];
+    int n_codecs = 0;
+    int codec_of_seg[kvc::kMaxSegs];
+    kvc_status st = check_segments(heads, dim, segs, n_segs, rank, /*allow_mixed=*/false, &sl, codecs, &n_codecs,
+                                   codec_of_seg);
     if (st != KVC_OK) return st;
     const bool work = heads > 0 && n_q > 0;
     KVC_PTR(q, work, "q");
@@ -436,10 +521,13 @@ kvc_status kvc_attend_lowdim(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype 
     if (!work) return ok();
     KVC_REQUIRE(heads <= 65535 && (n_q + 255) / 256 * heads <= (int64_t(1) << 27), KVC_ERR_UNSUPPORTED,
                 "at most 65535 heads and 2^27 blocks of 256 queries per call");
+    const CodecKey c = n_codecs ? codecs[0] : CodecKey{2, 2, 16, KVC_BF16};
     if (sl.total_tiles > 0) {
-      KVC_REQUIRE(g == 16 || g == 32, KVC_ERR_UNSUPPORTED, "group must be 16 or 32");
-      KVC_REQUIRE(cdt == KVC_BF16, KVC_ERR_UNSUPPORTED, "low-dim path needs bf16 centres");
+      KVC_REQUIRE(c.g == 16 || c.g == 32, KVC_ERR_UNSUPPORTED, "group must be 16 or 32");
+      KVC_REQUIRE(c.cdt == KVC_BF16, KVC_ERR_UNSUPPORTED, "low-dim path needs bf16 centres");
     }
+    const int kb = c.kb, vb = c.vb, g = c.g;
+    const kvc_dtype cdt = c.cdt;
     const size_t need = kvc_attend_lowdim_workspace_bytes(heads, n_q, dim, rank, segs, n_segs);
     KVC_REQUIRE(ws_bytes >= need, KVC_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
     KVC_PTR(ws, true, "ws");

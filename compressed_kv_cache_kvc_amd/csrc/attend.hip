@@ -111,6 +111,29 @@ struct CodePairs<4, CH> {
   }
 };
 
+// 16-bit residuals (fp16, stored in channel order): word k of the chunk holds
+// channels 2k, 2k+1; pair j is gathered from the two words of its block of four.
+struct Code32 {
+  uint4 lo, hi;
+};
+template <int CH>
+struct CodePairs<16, CH> {
+  uint32_t w[CH / 2];
+  __device__ __forceinline__ explicit CodePairs(uint4 v) {
+    static_assert(CH == 8, "16-byte chunk");
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+  __device__ __forceinline__ explicit CodePairs(const Code32& v) {
+    static_assert(CH == 16, "32-byte chunk");
+    w[0] = v.lo.x; w[1] = v.lo.y; w[2] = v.lo.z; w[3] = v.lo.w;
+    w[4] = v.hi.x; w[5] = v.hi.y; w[6] = v.hi.z; w[7] = v.hi.w;
+  }
+  __device__ __forceinline__ h2 pair(int j) const {
+    const int m = j >> 1;     // block of four channels: words 2m (4m, 4m+1) and 2m+1 (4m+2, 4m+3)
+    return as_h2(__builtin_amdgcn_perm(w[2 * m + 1], w[2 * m], (j & 1) ? 0x07060302u : 0x05040100u));
+  }
+};
+
 // (fp16(t0 + c.lo), fp16(t1 + c.hi)) for fp32 t and a packed fp16 pair c, each with
 // a single rounding: v_fma_mix{lo,hi}_f16 with fp32 sources t and 1.0 and the fp16
 // source c, computed in fp32 and rounded once to the destination half.
@@ -122,17 +145,23 @@ __device__ __forceinline__ uint32_t round_add_f16x2(float t0, float t1, uint32_t
 }
 
 template <int NB>
-using code_t = typename std::conditional<(NB > 4), uint64_t, uint32_t>::type;
+using code_t = typename std::conditional<
+    (NB > 16), Code32,
+    typename std::conditional<(NB > 8), uint4, typename std::conditional<(NB > 4), uint64_t, uint32_t>::type>::type>::type;
 
 template <int NB>
 __device__ __forceinline__ code_t<NB> load_code_bits(const uint8_t* p) {
   if constexpr (NB == 1) return *p;
   else if constexpr (NB == 2) return *reinterpret_cast<const uint16_t*>(p);
   else if constexpr (NB == 4) return *reinterpret_cast<const uint32_t*>(p);
-  else {
-    static_assert(NB == 8, "code chunk");
+  else if constexpr (NB == 8) {
     const uint2 w = *reinterpret_cast<const uint2*>(p);
     return uint64_t(w.x) | (uint64_t(w.y) << 32);
+  } else if constexpr (NB == 16) {
+    return *reinterpret_cast<const uint4*>(p);
+  } else {
+    static_assert(NB == 32, "code chunk");
+    return Code32{reinterpret_cast<const uint4*>(p)[0], reinterpret_cast<const uint4*>(p)[1]};
   }
 }
 
@@ -286,9 +315,10 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
 
   // ---- register pipeline (raw loaded words; converted only at dequantization)
   int kid_n = 0, vid_n = 0;       // ids of the tile to load next (t+1)
-  code_t<KNB> kc_r = 0;
-  code_t<VNB> vc_r = 0;
-  uint32_t km_r = 0, vm_r = 0;
+  code_t<KNB> kc_r{};
+  code_t<VNB> vc_r{};
+  // metadata words (scale | zero << 16); 16-bit residuals keep (1, 0)
+  uint32_t km_r = KB == 16 ? 0x3c00u : 0u, vm_r = VB == 16 ? 0x3c00u : 0u;
   uint32_t kcw[CWD], vcw[CWD];
 
   auto load_ids = [&](const IdCur& c, int t, int& ki, int& vi) {
@@ -300,8 +330,8 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
     const uint32_t j = row_of(c.s, t);
     kc_r = load_code_bits<KNB>(c.k_codes + (j * uint32_t(DQ * KB / 8) + uint32_t(dg * KNB)));
     vc_r = load_code_bits<VNB>(c.v_codes + (j * uint32_t(DQ * VB / 8) + uint32_t(dg * VNB)));
-    km_r = c.k_meta[j * uint32_t(DQ / G) + uint32_t((dg * CH) / G)];
-    vm_r = c.v_meta[j * uint32_t(DQ / G) + uint32_t((dg * CH) / G)];
+    if constexpr (KB != 16) km_r = c.k_meta[j * uint32_t(DQ / G) + uint32_t((dg * CH) / G)];
+    if constexpr (VB != 16) vm_r = c.v_meta[j * uint32_t(DQ / G) + uint32_t((dg * CH) / G)];
     const uint16_t* kp = c.k_tab + (uint32_t(ki) * DQ + dg * CH);
     const uint16_t* vp = c.v_tab + (uint32_t(vi) * DQ + dg * CH);
     if constexpr (CWD == 2) {
@@ -806,6 +836,9 @@ hipError_t pick_bits(const AttendParams& p, const SegList& segs, int kb, int vb,
   }
   KVC_CASE(2, 2, 16) KVC_CASE(2, 4, 16) KVC_CASE(4, 2, 16) KVC_CASE(4, 4, 16)
   KVC_CASE(2, 2, 32) KVC_CASE(2, 4, 32) KVC_CASE(4, 2, 32) KVC_CASE(4, 4, 32)
+  if constexpr (!LOWDIM) {
+    KVC_CASE(16, 16, 16)     // 16-bit residual segments (no groups; G is nominal)
+  }
 #undef KVC_CASE
   return hipErrorInvalidValue;
 }

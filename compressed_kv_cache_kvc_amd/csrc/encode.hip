@@ -9,6 +9,7 @@
 // fused and the sequence matches the stated operation order.
 #include "kvc_internal.h"
 #include "dev_common.h"
+#include "mfma.h"
 
 namespace kvc {
 namespace {
@@ -87,6 +88,28 @@ __global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, co
     *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
   }
   meta[tok * NG + g] = m;
+}
+
+// 16-bit residuals (no quantizer, no metadata): r = fl32(x - c[id]) rounded to
+// fp16 nearest-even, stored per element in channel order.  One thread per
+// (token, 8 channels), one 16-byte store.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void encode_raw_kernel(const T* __restrict__ x, const T* __restrict__ cent,
+                                                         const uint8_t* __restrict__ ids, int C, int64_t n,
+                                                         int64_t total_items, uint8_t* __restrict__ codes) {
+  const int64_t item = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (item >= total_items) return;
+  const int g = int(item % (D / 8));
+  const int64_t tok = item / (D / 8);
+  const int64_t h = tok / n;
+  const int id = ids[tok];
+  float xv[8], cv[8];
+  load_row<8>(x + tok * D + g * 8, xv);
+  load_row<8>(cent + (h * C + id) * D + g * 8, cv);
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = pack_f16x2(__fsub_rn(xv[2 * i], cv[2 * i]), __fsub_rn(xv[2 * i + 1], cv[2 * i + 1]));
+  *reinterpret_cast<uint4*>(codes + tok * (D * 2) + g * 16) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // Low-dimensional encode: coefficients a = U^T r of each token in a rank-R basis,
@@ -226,6 +249,13 @@ hipError_t run_lowdim(int heads, int64_t n, const void* x, int C, const void* ce
 template <typename T, int D>
 hipError_t dispatch_full(int heads, int64_t n, const void* x, int C, const void* cent, const uint8_t* ids,
                          int bits, int group, uint8_t* codes, uint16_t* meta, hipStream_t st) {
+  if (bits == 16) {
+    const int64_t items = int64_t(heads) * n * (D / 8);
+    if (items == 0) return hipSuccess;
+    hipLaunchKernelGGL((encode_raw_kernel<T, D>), dim3(unsigned((items + 255) / 256)), dim3(256), 0, st,
+                       static_cast<const T*>(x), static_cast<const T*>(cent), ids, C, n, items, codes);
+    return hipGetLastError();
+  }
   if (group == 16 && bits == 2) return run_full<T, D, 16, 2>(heads, n, x, C, cent, ids, codes, meta, st);
   if (group == 16 && bits == 4) return run_full<T, D, 16, 4>(heads, n, x, C, cent, ids, codes, meta, st);
   if (group == 32 && bits == 2) return run_full<T, D, 32, 2>(heads, n, x, C, cent, ids, codes, meta, st);

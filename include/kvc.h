@@ -151,6 +151,10 @@ kvc_status kvc_query_stats(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_
  *              when ids_in is NULL).
  *   basis      NULL or [heads][dim][rank] fp32; rank = 0 without a basis.
  *   bits       2 or 4; group divides the coded dimension (dim or rank).
+ *              bits = 16 stores the residual itself, fp16 nearest-even per
+ *              element ([heads][n_tokens][dim] fp16 in `codes`, 2*dim bytes a
+ *              row), with no groups and no metadata (meta may be NULL; group is
+ *              ignored); full dimension only (TempoKV, Table 7: 16-bit anchors).
  *   codes, meta  outputs as laid out above.
  * Supported: dim 64 or 128; group 16 or 32 (and group <= coded dimension);
  * rank 0, or 32 or 64 with dim 128. */

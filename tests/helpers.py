@@ -26,7 +26,7 @@ def encode_heads(x, cent, ids, bits, group, basis=None):
         c, m = oracle.encode(x[h], cent[h], ids[h], bits, group, None if basis is None else basis[h])
         codes.append(c)
         metas.append(m)
-    return np.stack(codes), np.stack(metas)
+    return np.stack(codes), (None if metas[0] is None else np.stack(metas))   # 16-bit residuals: no meta
 
 
 def nearest_ids(x: np.ndarray, cent: np.ndarray) -> np.ndarray:
@@ -59,8 +59,10 @@ class Cache:
         return self.kid.shape[1]
 
     def oracle_segment(self, h: int) -> oracle.Segment:
-        return oracle.Segment(self.k_codes[h], self.k_meta[h], self.kid[h], self.kc[h],
-                              self.v_codes[h], self.v_meta[h], self.vid[h], self.vc[h],
+        km = None if self.k_meta is None else self.k_meta[h]
+        vm = None if self.v_meta is None else self.v_meta[h]
+        return oracle.Segment(self.k_codes[h], km, self.kid[h], self.kc[h],
+                              self.v_codes[h], vm, self.vid[h], self.vc[h],
                               self.k_bits, self.v_bits, self.group)
 
     def gpu_segment(self, cent_dtype=torch.bfloat16, head_map=None, device="cuda"):
@@ -78,10 +80,13 @@ class Cache:
                 t = t.index_select(0, idx)
             return t.contiguous()
 
+        def meta(m):
+            return None if m is None else up(m.view(np.int16)).view(torch.uint16)
+
         return kvc.Segment(
-            k_codes=up(self.k_codes), k_meta=up(self.k_meta.view(np.int16)).view(torch.uint16),
+            k_codes=up(self.k_codes), k_meta=meta(self.k_meta),
             k_ids=up(self.kid.astype(np.uint8)), k_cent=up(self.kc, cent_dtype),
-            v_codes=up(self.v_codes), v_meta=up(self.v_meta.view(np.int16)).view(torch.uint16),
+            v_codes=up(self.v_codes), v_meta=meta(self.v_meta),
             v_ids=up(self.vid.astype(np.uint8)), v_cent=up(self.vc, cent_dtype),
             k_bits=self.k_bits, v_bits=self.v_bits, group=self.group, rank=self.rank)
 

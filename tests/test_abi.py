@@ -100,7 +100,17 @@ def test_attend_validation(lib):
     assert _attend(lib, [_seg(k_bits=3)]) == INV
     assert _attend(lib, [_seg(group=24)]) == INV
     assert _attend(lib, [_seg(rank=32)]) == INV
-    assert _attend(lib, [_seg(), _seg(v_bits=4)]) == UNS     # segments must share codec parameters
+    # segments of different codecs are attended in one launch per codec and merged;
+    # a workspace of 0 bytes stops the call before any launch
+    assert _attend(lib, [_seg(), _seg(v_bits=4)], wsb=0) == WS
+    arr = (_lib.KvcSegment * 2)(_seg(n_tokens=9360), _seg(n_tokens=1560, k_bits=4, v_bits=4))
+    rows = 12 * 4680                                          # two partial results, then the merge
+    assert lib.kvc_attend_workspace_bytes(12, 4680, 128, 1, arr, 2) == \
+        2 * rows * 128 * 4 + 2 * rows * 4 + 2 * _tables(12, 16, 128)
+    raw = _seg(k_bits=16, v_bits=16, k_meta=None, v_meta=None)
+    assert _attend(lib, [raw], wsb=0) == WS                   # 16-bit residual segments need no metadata
+    assert _attend(lib, [_seg(k_bits=16, v_bits=2)]) == UNS   # 16-bit K needs 16-bit V
+    assert _attend(lib, [raw], qdt=0) == UNS                  # fp32 queries read 2/4-bit codes only
     assert _attend(lib, [_seg(k_codes=None)]) == INV
     assert _attend(lib, [_seg()] * 25) == UNS                 # more segments than one launch walks
     assert _attend(lib, [_seg(cent_dtype=0)]) == UNS          # bf16 queries with fp32 centres

@@ -43,7 +43,8 @@ def _bf16_tokens(H, N, d, seed, scale=1.0, outliers=True):
 @pytest.mark.parametrize("d,bits,group,dtype", [
     (128, 2, 16, torch.bfloat16), (128, 4, 32, torch.bfloat16), (128, 2, 32, torch.bfloat16),
     (128, 4, 16, torch.bfloat16), (64, 2, 16, torch.bfloat16), (64, 4, 32, torch.bfloat16),
-    (64, 4, 32, torch.float32), (128, 2, 16, torch.float32)])
+    (64, 4, 32, torch.float32), (128, 2, 16, torch.float32),
+    (128, 16, 16, torch.bfloat16), (64, 16, 32, torch.float32), (128, 16, 16, torch.float32)])
 def test_encode_bit_exact(d, bits, group, dtype):
     H, N, C = 3, 1037, 37
     x = _bf16_tokens(H, N, d, 1).to(dtype)
@@ -70,7 +71,10 @@ def test_encode_bit_exact(d, bits, group, dtype):
                                   ids=torch.from_numpy(ids.astype(np.uint8)).to(DEV))
     torch.cuda.synchronize()
     assert np.array_equal(codes.cpu().numpy(), ref_codes)
-    assert np.array_equal(meta.cpu().numpy(), ref_meta)
+    if bits == 16:                                  # fp16 residuals carry no metadata
+        assert meta is None and ref_meta is None
+    else:
+        assert np.array_equal(meta.cpu().numpy(), ref_meta)
 
 
 @pytest.mark.parametrize("rank,bits,group", [(32, 2, 16), (32, 4, 16), (64, 4, 32), (64, 2, 32)])
@@ -240,6 +244,32 @@ def test_attend_split_history():
     cache = _cache(H, N, d, 64, 4, 4, 32, 40)
     q = _bf16_tokens(H, n_q, d, 41, outliers=False)
     _attend_check(q, [cache], what="split")
+
+
+def test_attend_16bit_residual_segment():
+    # fp16 residuals (no quantizer): k_hat = fp16(r + c) with one rounding
+    H, d, n_q = 2, 128, 300
+    cache = _cache(H, 777, d, 32, 16, 16, 16, 45)
+    q = _bf16_tokens(H, n_q, d, 46, outliers=False)
+    _attend_check(q, [cache], what="16-bit")
+
+
+def test_attend_mixed_codecs_one_call():
+    # an anchor frame at 4 bits, the history at 2 bits, a raw 16-bit segment, a
+    # second 2-bit run: one launch per codec, merged by LSE
+    H, d, n_q = 2, 128, 333
+    caches = [_cache(H, 1560, d, 64, 4, 4, 16, 47), _cache(H, 3000, d, 64, 2, 2, 16, 48),
+              _cache(H, 200, d, 16, 16, 16, 16, 49), _cache(H, 450, d, 32, 2, 2, 16, 50)]
+    q = _bf16_tokens(H, n_q, d, 51, outliers=False)
+    _attend_check(q, caches, what="mixed codecs")
+
+
+def test_attend_mixed_codecs_split():
+    # one query block: each codec's history is also split across workgroups
+    H, d, n_q = 1, 128, 200
+    caches = [_cache(H, 4100, d, 64, 2, 4, 16, 52), _cache(H, 1560, d, 64, 4, 4, 32, 53)]
+    q = _bf16_tokens(H, n_q, d, 54, outliers=False)
+    _attend_check(q, caches, what="mixed codecs split")
 
 
 def test_attend_empty_history():
