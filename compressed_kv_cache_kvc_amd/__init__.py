@@ -13,6 +13,8 @@ Entry points (names follow the C ABI):
   lse_merge(outs, lses)                     -> (out, lse)
   assign_qsac(x, centroids, w, n_cand, group) -> ids          (query-aware key assignment)
   query_stats(q, w, n_prev)                 -> w              (running E[q_c^2], in place)
+  route_frames(n_frames, n_recent, ...)     -> [bool]         (full-dim frames of a history)
+  anchor_bits(k_bits, v_bits)               -> int            (anchor precision)
 """
 from __future__ import annotations
 
@@ -26,7 +28,7 @@ from . import _lib
 from ._lib import KvcSegment
 
 __all__ = ["KvcError", "Segment", "fit_assign", "encode", "attend", "attend_lowdim", "lse_merge",
-           "assign_qsac", "query_stats", "library", "version"]
+           "assign_qsac", "query_stats", "route_frames", "anchor_bits", "library", "version"]
 
 
 class KvcError(RuntimeError):
@@ -142,6 +144,19 @@ def query_stats(q: torch.Tensor, w: Optional[torch.Tensor] = None, n_prev: int =
     _need(w, "w", q.device, torch.float32, (H, d))
     _check(library().kvc_query_stats(H, n_q, d, _dtype_code(q), _ptr(q), n_prev, _ptr(w), _stream(q.device)))
     return w
+
+
+# ------------------------------------------------------------------------------ routing
+def route_frames(n_frames: int, n_recent: int, period: int = 0, n_sink: int = 0,
+                 all_full_until: int = 0) -> list:
+    """Per latent frame (oldest first): True when read at full dimension."""
+    buf = (ctypes.c_uint8 * max(1, n_frames))()
+    _check(library().kvc_route_frames(n_frames, n_recent, period, n_sink, all_full_until, buf))
+    return [bool(buf[f]) for f in range(n_frames)]
+
+
+def anchor_bits(k_bits: int, v_bits: int) -> int:
+    return int(library().kvc_anchor_bits(k_bits, v_bits))
 
 
 # ------------------------------------------------------------------------------ encode

@@ -17,7 +17,7 @@ EXPORTS = [
     "kvc_encode", "kvc_encode_workspace_bytes",
     "kvc_attend", "kvc_attend_workspace_bytes",
     "kvc_attend_lowdim", "kvc_attend_lowdim_workspace_bytes",
-    "kvc_lse_merge", "kvc_assign_qsac", "kvc_query_stats",
+    "kvc_lse_merge", "kvc_assign_qsac", "kvc_query_stats", "kvc_route_frames", "kvc_anchor_bits",
     "kvc_status_string", "kvc_last_error", "kvc_version",
 ]
 
@@ -59,6 +59,8 @@ _SIGS = {
                                      _vp]),
     "kvc_assign_qsac": (ctypes.c_int, [_i32, _i64, _i32, ctypes.c_int, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp]),
     "kvc_query_stats": (ctypes.c_int, [_i32, _i64, _i32, ctypes.c_int, _vp, _i64, _vp, _vp]),
+    "kvc_route_frames": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _vp]),
+    "kvc_anchor_bits": (_i32, [_i32, _i32]),
     "kvc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kvc_last_error": (ctypes.c_char_p, []),
     "kvc_version": (ctypes.c_char_p, []),

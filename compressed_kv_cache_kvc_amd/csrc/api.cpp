@@ -323,6 +323,25 @@ kvc_status kvc_query_stats(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_
   }
 }
 
+// ------------------------------------------------------------------------------ routing
+kvc_status kvc_route_frames(int32_t n_frames, int32_t n_recent, int32_t period, int32_t n_sink,
+                            int32_t all_full_until, uint8_t* full_dim) {
+  KVC_REQUIRE(n_frames >= 0 && n_recent >= 0 && period >= 0 && n_sink >= 0 && all_full_until >= 0,
+              KVC_ERR_INVALID_ARG, "frame counts must be >= 0");
+  KVC_REQUIRE(n_frames == 0 || full_dim != nullptr, KVC_ERR_INVALID_ARG, "full_dim is NULL");
+  for (int32_t f = 0; f < n_frames; ++f) {
+    const bool full = n_frames <= all_full_until || f >= n_frames - n_recent || f < n_sink ||
+                      (period > 0 && f % period == 0);
+    full_dim[f] = full ? 1 : 0;
+  }
+  return ok();
+}
+
+int32_t kvc_anchor_bits(int32_t k_bits, int32_t v_bits) {
+  int32_t b = k_bits > v_bits ? k_bits : v_bits;
+  return b > 4 ? b : 4;
+}
+
 // ------------------------------------------------------------------------------ encode
 size_t kvc_encode_workspace_bytes(int32_t heads, int64_t n_tokens, int32_t dim, int32_t n_centroids,
                                   int32_t ids_given) {

@@ -136,6 +136,17 @@ kvc_status kvc_assign_qsac(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dty
 kvc_status kvc_query_stats(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype,
                            const void* q, int64_t n_prev, float* w, hipStream_t stream);
 
+/* Frame routing of mixed-dimensional attention (NanoKV, Figure 4 and appendix
+ * Table 7): frame f of a history of n_frames latent frames (0 = oldest) is read
+ * at full dimension (full_dim[f] = 1) when n_frames <= all_full_until, or f >=
+ * n_frames - n_recent, or f < n_sink, or period > 0 and f % period == 0 (one
+ * anchor per `period` older frames, the first of each window); otherwise through
+ * the reduced maps (0).  Host memory; no GPU work. */
+kvc_status kvc_route_frames(int32_t n_frames, int32_t n_recent, int32_t period, int32_t n_sink,
+                            int32_t all_full_until, uint8_t* full_dim);
+/* Anchor precision (TempoKV, section 3.3 and Table 7): b_a = max(4, b_K, b_V). */
+int32_t kvc_anchor_bits(int32_t k_bits, int32_t v_bits);
+
 /* Encode tokens against their centres (TempoKV, section 3.1 Eq. 1 and section
  * 3.3 Eq. 2).  Per token: r = fl32(x - c[id]); with a basis, r is replaced by
  * its coefficients a_k = sum_i fl32(U[i][k] * r[i]) accumulated in fp32 over
