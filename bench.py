@@ -43,6 +43,13 @@ def parse():
                     help="re-assign the keys after the fit with the query-aware assignment (QuantWM section 4.1) "
                          "over M candidates, weighted by the statistics of the previous chunks' queries, and "
                          "update those statistics after the attention (self_forcing_layer, streaming); 0 = off")
+    ap.add_argument("--route", default="", metavar="R,P,S,A",
+                    help="larger_backbone: read at full dimension the R most recent latent frames, one anchor "
+                         "per P older frames, the S oldest frames, or every frame while the history has at most "
+                         "A frames (NanoKV appendix Table 7); the rest through the rank-r maps")
+    ap.add_argument("--anchor", action="store_true",
+                    help="larger_backbone: code the oldest frame, when read at full dimension, at "
+                         "max(4, k_bits, v_bits) bits (TempoKV section 3.3)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the warmup, run one plain fp32 negation of MIB MiB (reads and writes MIB MiB) so "
                          "that a hardware-counter run can scale its byte counters against a kernel of known traffic")
@@ -221,6 +228,7 @@ class LargerBackbone(Workload):
         self.kf, self.kr = self.k[:, :F].contiguous(), self.k[:, F:].contiguous()
         self.vf, self.vr = self.v[:, :F].contiguous(), self.v[:, F:].contiguous()
         self.attn_flops = 4.0 * H * cfg.n_q * R * cfg.dim + 4.0 * H * cfg.n_q * F * r + 4.0 * H * cfg.n_q * cfg.dim * r
+        self.full_tokens, self.low_tokens = R, F
         self.enc_tokens = H * N
         self.enc_bytes = sum(H * N * (cfg.dim * 2 + 1) for _ in range(2)) + \
             H * R * (cfg.dim * (cfg.k_bits + cfg.v_bits) // 8 + 8 * cfg.dim // cfg.group) + \
@@ -248,6 +256,79 @@ class LargerBackbone(Workload):
         o1, l1 = kvc.attend(self.q, [recent])
         e3 = self.ev()
         o2, l2 = kvc.attend_lowdim(self.q, self.Uk, self.Uv, [far])
+        e4 = self.ev()
+        out, lse = kvc.lse_merge([o1, o2], [l1, l2])
+        e5 = self.ev()
+        self.mark("fit", e0, e1)
+        self.mark("encode", e1, e2)
+        self.mark("attend", e2, e3)
+        self.mark("attend_lowdim", e3, e4)
+        self.mark("lse_merge", e4, e5)
+        return out
+
+
+class RoutedBackbone(LargerBackbone):
+    """larger_backbone with frame routing (NanoKV appendix Table 7): the latent
+    frames chosen by the rule (recent frames, a sink, periodic anchors) are read
+    at full dimension, the others through the rank-r maps; with --anchor the
+    oldest frame, when read at full dimension, is coded at b_a = max(4, b_K, b_V)
+    bits (TempoKV section 3.3).  Full-dimensional runs of different codecs go to
+    one attention call (one launch per codec), the reduced runs to the low-dim
+    call, and the two results are merged by LSE."""
+
+    def __init__(self, cfg, dev, route, anchor):
+        super().__init__(cfg, dev)
+        import compressed_kv_cache_kvc_amd as kvc
+        H, S = cfg.heads, cfg.frame_tokens
+        n_frames = cfg.hist // S
+        mask = kvc.route_frames(n_frames, *route)
+        self.runs = []                 # (first token, end token, full, anchor)
+        f = 0
+        while f < n_frames:
+            e = f
+            while e < n_frames and mask[e] == mask[f]:
+                e += 1
+            if mask[f] and anchor and f == 0:
+                self.runs.append((0, S, True, True))
+                if e > 1:
+                    self.runs.append((S, e * S, True, False))
+            else:
+                self.runs.append((f * S, e * S, mask[f], False))
+            f = e
+        self.anchor_bits = kvc.anchor_bits(cfg.k_bits, cfg.v_bits)
+        full = sum(b - a for a, b, fu, _ in self.runs if fu)
+        low = cfg.hist - full
+        r = cfg.rank
+        self.full_tokens, self.low_tokens = full, low
+        self.attn_flops = 4.0 * H * cfg.n_q * full * cfg.dim + 4.0 * H * cfg.n_q * low * r + \
+            (4.0 * H * cfg.n_q * cfg.dim * r if low else 0.0)
+        self.slices = [(self.k[:, a:b].contiguous(), self.v[:, a:b].contiguous()) for a, b, _, _ in self.runs]
+        self.route, self.anchor = route, anchor
+
+    def step(self):
+        import compressed_kv_cache_kvc_amd as kvc
+        cfg = self.cfg
+        kc, vc = self.kc0.clone(), self.vc0.clone()
+        e0 = self.ev()
+        kid, vid = self.both(lambda: kvc.fit_assign(self.k, kc, n_iter=cfg.n_iter),
+                             lambda: kvc.fit_assign(self.v, vc, n_iter=cfg.n_iter))
+        e1 = self.ev()
+        full_segs, low_segs = [], []
+        for (a, b, full, anc), (ks, vs) in zip(self.runs, self.slices):
+            ki, vi = kid[:, a:b].contiguous(), vid[:, a:b].contiguous()
+            kb, vb = (self.anchor_bits, self.anchor_bits) if anc else (cfg.k_bits, cfg.v_bits)
+            if full:
+                kco, kme, _ = kvc.encode(ks, kc, kb, cfg.group, ids=ki)
+                vco, vme, _ = kvc.encode(vs, vc, vb, cfg.group, ids=vi)
+                full_segs.append(kvc.Segment(kco, kme, ki, kc, vco, vme, vi, vc, kb, vb, cfg.group))
+            else:
+                kco, kme, _ = kvc.encode(ks, kc, kb, cfg.group, ids=ki, basis=self.Uk)
+                vco, vme, _ = kvc.encode(vs, vc, vb, cfg.group, ids=vi, basis=self.Uv)
+                low_segs.append(kvc.Segment(kco, kme, ki, kc, vco, vme, vi, vc, kb, vb, cfg.group, rank=cfg.rank))
+        e2 = self.ev()
+        o1, l1 = kvc.attend(self.q, full_segs)
+        e3 = self.ev()
+        o2, l2 = kvc.attend_lowdim(self.q, self.Uk, self.Uv, low_segs)
         e4 = self.ev()
         out, lse = kvc.lse_merge([o1, o2], [l1, l2])
         e5 = self.ev()
@@ -305,8 +386,10 @@ class Streaming(Workload):
         self.qsac = m
 
 
-def make_workload(cfg, dev):
+def make_workload(cfg, dev, route=None, anchor=False):
     if cfg.name == "larger_backbone":
+        if route is not None or anchor:
+            return RoutedBackbone(cfg, dev, route or (cfg.recent // cfg.frame_tokens, 0, 0, 0), anchor)
         return LargerBackbone(cfg, dev)
     if cfg.name == "streaming":
         return Streaming(cfg, dev)
@@ -416,7 +499,12 @@ def main():
     torch.cuda.set_device(dev)
     kvc.library()
     cfg = synth.get_config(args.workload)
-    w = make_workload(cfg, dev)
+    route = tuple(int(v) for v in args.route.split(",")) if args.route else None
+    if route is not None and len(route) != 4:
+        raise SystemExit("--route takes RECENT,PERIOD,SINK,ALL_FULL_UNTIL")
+    if (route is not None or args.anchor) and cfg.name != "larger_backbone":
+        raise SystemExit("--route and --anchor apply to the larger_backbone workload")
+    w = make_workload(cfg, dev, route, args.anchor)
     if args.qsac:
         if not hasattr(w, "enable_qsac"):
             raise SystemExit("--qsac covers the single-segment workloads (self_forcing_layer, streaming, tiny)")
@@ -452,7 +540,7 @@ def main():
 
     # roofline of the full-dim attention kernel (the dominant launch)
     if cfg.name == "larger_backbone":
-        fl = 4.0 * cfg.heads * cfg.n_q * cfg.recent * cfg.dim
+        fl = 4.0 * cfg.heads * cfg.n_q * w.full_tokens * cfg.dim
         launches = 1
     elif cfg.name == "streaming":
         fl = w.attn_flops
@@ -491,14 +579,19 @@ def main():
                      "lse_merge": round(phases.get("lse_merge", 0.0) / K, 4)},
         "roofline": roofline,
     }
+    if isinstance(w, RoutedBackbone):
+        line["config"]["route"] = list(w.route)
+        line["config"]["anchor_bits"] = w.anchor_bits if w.anchor else None
+        line["config"]["full_dim_tokens"] = w.full_tokens
+        line["config"]["far"] = w.low_tokens
     if cfg.name == "larger_backbone" and lowdim_ms > 0:
         # the far part is bound by the softmax's vector work rather than the
         # matrix cores: one exponential per score; the reference rate is one
         # exponential per lane and clock (256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz)
-        scores = float(cfg.heads) * cfg.n_q * cfg.far
+        scores = float(cfg.heads) * cfg.n_q * w.low_tokens
         exp_peak = 256 * 4 * 16 * 2.4e9
         line["lowdim"] = {"ms": round(lowdim_ms, 4),
-                          "TFLOP/s": round((4.0 * cfg.heads * cfg.n_q * cfg.far * cfg.rank
+                          "TFLOP/s": round((4.0 * cfg.heads * cfg.n_q * w.low_tokens * cfg.rank
                                             + 4.0 * cfg.heads * cfg.n_q * cfg.dim * cfg.rank) / (lowdim_ms * 1e-3) / 1e12, 2),
                           "scores_per_s": round(scores / (lowdim_ms * 1e-3), 1),
                           "exp_peak_per_s": exp_peak,

@@ -241,6 +241,68 @@ def test_larger_backbone_recent_far_merge():
         check_attention(om[h][rows], lm[h][rows], o_ref, l_ref, f"larger_backbone merged head {h}")
 
 
+def test_larger_backbone_routed_frames_with_anchor():
+    """Routing of NanoKV appendix Table 7 (4 recent frames, one anchor per 16 older
+    frames) on the larger backbone's 21 frames, the oldest frame coded at
+    b_a = max(4, b_K, b_V) bits: the full-dimensional frames (two codecs) go to one
+    attention call, the other 15 to the low-dim call, then the LSE merge."""
+    from oracle.routing import anchor_bits, route_frames
+    cfg = synth.get_config("larger_backbone")
+    n_src, S = 2, cfg.frame_tokens
+    n_frames = cfg.hist // S
+    mask = kvc().route_frames(n_frames, 4, 16)
+    assert mask == route_frames(n_frames, 4, 16)
+    ba = kvc().anchor_bits(cfg.k_bits, cfg.v_bits)
+    assert ba == anchor_bits(cfg.k_bits, cfg.v_bits) == 4
+    Uk = synth.orthonormal_basis(n_src, cfg.dim, cfg.rank, synth.seed_for(cfg.seed, 0, 0, 2)).numpy()
+    Uv = synth.orthonormal_basis(n_src, cfg.dim, cfg.rank, synth.seed_for(cfg.seed, 0, 1, 2)).numpy()
+    k = synth.AR1Stream(cfg, "k", heads=n_src).tokens(cfg.hist)
+    v = synth.AR1Stream(cfg, "v", heads=n_src).tokens(cfg.hist)
+    kn, vn = np32(k), np32(v)
+    kc = np32(synth.forgy_init(k, cfg.n_centroids, 3))
+    vc = np32(synth.forgy_init(v, cfg.n_centroids, 4))
+    kid, vid = nearest_ids(kn, kc), nearest_ids(vn, vc)
+    full, low = [], []
+    f = 0
+    while f < n_frames:
+        e = f
+        while e < n_frames and mask[e] == mask[f]:
+            e += 1
+        a, b = f * S, e * S
+        if mask[f]:
+            if f == 0:                               # the anchor frame, then the rest of the run
+                full.append(Cache(kn[:, :S], vn[:, :S], kc, vc, kid[:, :S], vid[:, :S], ba, ba, cfg.group))
+                a = S
+            if b > a:
+                full.append(Cache(kn[:, a:b], vn[:, a:b], kc, vc, kid[:, a:b], vid[:, a:b], cfg.k_bits, cfg.v_bits,
+                                  cfg.group))
+        else:
+            low.append(Cache(kn[:, a:b], vn[:, a:b], kc, vc, kid[:, a:b], vid[:, a:b], cfg.k_bits, cfg.v_bits,
+                             cfg.group, Uk, Uv))
+        f = e
+    assert len(full) == 2 and len(low) == 1          # anchor frame 0; frames 16-20; frames 1-15
+    head_map = [h % n_src for h in range(cfg.heads)]
+    q = _queries_tiled(cfg, head_map).to(DEV)
+    idx = torch.as_tensor(head_map, device=DEV)
+    Ukd = torch.from_numpy(Uk).to(DEV).index_select(0, idx).contiguous()
+    Uvd = torch.from_numpy(Uv).to(DEV).index_select(0, idx).contiguous()
+    o1, l1 = kvc().attend(q, [c.gpu_segment(head_map=head_map) for c in full])
+    o2, l2 = kvc().attend_lowdim(q, Ukd, Uvd, [c.gpu_segment(head_map=head_map) for c in low])
+    om, lm = kvc().lse_merge([o1, o2], [l1, l2])
+    torch.cuda.synchronize()
+    rows = _rows(cfg.n_q, cfg.seed)
+    hs = [0, 1, 39]
+    sub = [head_map[h] for h in hs]
+    qc = q[hs].cpu()
+    om, lm = om.cpu().numpy(), lm.cpu().numpy()
+    for h, s in zip(hs, sub):
+        qs = np32(qc[hs.index(h)])[rows]
+        a = oracle.attend(qs, [c.oracle_segment(s) for c in full])
+        b = oracle.attend_lowdim(qs, Uk[s], Uv[s], [c.oracle_segment(s) for c in low])
+        o_ref, l_ref = oracle.lse_merge([a[0], b[0]], [a[1], b[1]])
+        check_attention(om[h][rows], lm[h][rows], o_ref, l_ref, f"routed larger_backbone head {h}")
+
+
 def _u16(t, idx):
     """Rows of a uint16 GPU tensor as numpy (torch has no uint16 indexing on the GPU)."""
     return t.view(torch.int16)[idx].cpu().numpy().view(np.uint16)
