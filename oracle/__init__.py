@@ -19,7 +19,8 @@ video generation):
 * QuantWM (2609.26425), section 4.1 (k-means assignment of each token to its
   nearest centre, then quantization of the residual; QSAC, the query-aware
   choice among the nearest centres, Eqs. 6-12, and its cold start in the
-  appendix);
+  appendix; section 4.2, PSAC, the compensation of the remaining key error
+  along the principal query directions);
 * NanoKV (2611.06377), Table 4 (256 centres each for K and V, two k-means
   iterations, one residual stage), Table 5 caption (centres fitted separately
   for K and V) and Figure 4 (mixed-dimensional attention: reduce the queries,
@@ -51,3 +52,4 @@ from .codec import (  # noqa: F401
 )
 from .attention import attend, attend_lowdim, lse_merge, Segment  # noqa: F401
 from .qsac import assign_qsac, query_stats  # noqa: F401
+from .psac import attend_psac, psac_basis, psac_coeffs, query_moments  # noqa: F401
