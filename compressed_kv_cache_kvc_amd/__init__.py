@@ -15,6 +15,8 @@ Entry points (names follow the C ABI):
   query_stats(q, w, n_prev)                 -> w              (running E[q_c^2], in place)
   route_frames(n_frames, n_recent, ...)     -> [bool]         (full-dim frames of a history)
   anchor_bits(k_bits, v_bits)               -> int            (anchor precision)
+  query_moments(q, m, n_prev) / psac_basis(m) / psac_coeffs(...) / attend_psac(q, u, segs, coefs)
+                                            (principal-subspace logit compensation)
 """
 from __future__ import annotations
 
@@ -28,7 +30,8 @@ from . import _lib
 from ._lib import KvcSegment
 
 __all__ = ["KvcError", "Segment", "fit_assign", "encode", "attend", "attend_lowdim", "lse_merge",
-           "assign_qsac", "query_stats", "route_frames", "anchor_bits", "library", "version"]
+           "assign_qsac", "query_stats", "route_frames", "anchor_bits", "query_moments", "psac_basis",
+           "psac_coeffs", "attend_psac", "library", "version"]
 
 
 class KvcError(RuntimeError):
@@ -269,6 +272,80 @@ def attend(q: torch.Tensor, segments: Sequence[Segment], out: Optional[torch.Ten
     ws = _workspace(wsb, q.device)
     _check(lib.kvc_attend(H, n_q, d, _dtype_code(q), _ptr(q), arr, len(segments), _ptr(out), _ptr(lse),
                           _ptr(ws), wsb, _stream(q.device)))
+    return out, lse
+
+
+# ------------------------------------------------------------------------------ logit compensation
+PSAC_RANK = 8
+
+
+def query_moments(q: torch.Tensor, m: Optional[torch.Tensor] = None, n_prev: int = 0) -> torch.Tensor:
+    """Running second-moment matrices [H, d, d] fp32 of the queries q [H, n_q, d]
+    (updated in place; allocated when None, with n_prev = 0)."""
+    _need(q, "q")
+    H, n_q, d = q.shape
+    if m is None:
+        if n_prev:
+            raise ValueError("n_prev > 0 needs the previous moments m")
+        m = torch.empty(H, d, d, dtype=torch.float32, device=q.device)
+    _need(m, "m", q.device, torch.float32, (H, d, d))
+    _check(library().kvc_query_moments(H, n_q, d, _dtype_code(q), _ptr(q), n_prev, _ptr(m), _stream(q.device)))
+    return m
+
+
+def psac_basis(m: torch.Tensor, n_iter: int = 32, u_prev: Optional[torch.Tensor] = None):
+    """Top-8 eigenvectors u [H, d, 8] fp32 and eigenvalues [H, 8] of m [H, d, d]."""
+    _need(m, "m", dtype=torch.float32)
+    H, d, _ = m.shape
+    u = torch.empty(H, d, PSAC_RANK, dtype=torch.float32, device=m.device)
+    lam = torch.empty(H, PSAC_RANK, dtype=torch.float32, device=m.device)
+    if u_prev is not None:
+        _need(u_prev, "u_prev", m.device, torch.float32, (H, d, PSAC_RANK))
+    _check(library().kvc_psac_basis(H, d, _ptr(m), PSAC_RANK, n_iter, _ptr(u_prev), _ptr(u), _ptr(lam),
+                                    _stream(m.device)))
+    return u, lam
+
+
+def psac_coeffs(x: torch.Tensor, centroids: torch.Tensor, ids: torch.Tensor, codes: torch.Tensor,
+                meta: torch.Tensor, bits: int, group: int, u: torch.Tensor) -> torch.Tensor:
+    """Kept coefficients [H, N, 8] fp16 (as uint16 bits) of the keys' remaining
+    quantization error along u [H, d, 8]."""
+    _need(x, "x")
+    H, N, d = x.shape
+    C = centroids.shape[1]
+    _need(centroids, "centroids", x.device, x.dtype, (H, C, d))
+    _need(ids, "ids", x.device, torch.uint8, (H, N))
+    _need(codes, "codes", x.device, torch.uint8)
+    _need(meta, "meta", x.device, torch.uint16)
+    _need(u, "u", x.device, torch.float32, (H, d, PSAC_RANK))
+    coef = torch.empty(H, N, PSAC_RANK, dtype=torch.uint16, device=x.device)
+    _check(library().kvc_psac_coeffs(H, N, d, _dtype_code(x), _ptr(x), C, _ptr(centroids), _ptr(ids), _ptr(codes),
+                                     _ptr(meta), bits, group, _ptr(u), PSAC_RANK, _ptr(coef), _stream(x.device)))
+    return coef
+
+
+def attend_psac(q: torch.Tensor, u: torch.Tensor, segments: Sequence[Segment], coefs: Sequence[torch.Tensor],
+                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """attend() with every logit corrected by (u^T q) . coef (one coefficient
+    tensor [H, n, 8] per segment)."""
+    _need(q, "q")
+    H, n_q, d = q.shape
+    _need(u, "u", q.device, torch.float32, (H, d, PSAC_RANK))
+    if len(coefs) != len(segments):
+        raise ValueError("one coefficient tensor per segment")
+    for s, c in zip(segments, coefs):
+        _need(c, "coef", q.device, torch.uint16, (H, s.n_tokens, PSAC_RANK))
+    out = out if out is not None else torch.empty(H, n_q, d, dtype=torch.float32, device=q.device)
+    lse = lse if lse is not None else torch.empty(H, n_q, dtype=torch.float32, device=q.device)
+    _need(out, "out", q.device, torch.float32, (H, n_q, d))
+    _need(lse, "lse", q.device, torch.float32, (H, n_q))
+    arr = _seg_array(segments)
+    cp = (ctypes.c_void_p * max(1, len(coefs)))(*[c.data_ptr() for c in coefs])
+    lib = library()
+    wsb = lib.kvc_attend_psac_workspace_bytes(H, n_q, d, _dtype_code(q), arr, len(segments))
+    ws = _workspace(wsb, q.device)
+    _check(lib.kvc_attend_psac(H, n_q, d, _dtype_code(q), _ptr(q), _ptr(u), PSAC_RANK, arr, cp, len(segments),
+                               _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream(q.device)))
     return out, lse
 
 

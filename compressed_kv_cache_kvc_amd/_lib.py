@@ -18,6 +18,7 @@ EXPORTS = [
     "kvc_attend", "kvc_attend_workspace_bytes",
     "kvc_attend_lowdim", "kvc_attend_lowdim_workspace_bytes",
     "kvc_lse_merge", "kvc_assign_qsac", "kvc_query_stats", "kvc_route_frames", "kvc_anchor_bits",
+    "kvc_query_moments", "kvc_psac_basis", "kvc_psac_coeffs", "kvc_attend_psac", "kvc_attend_psac_workspace_bytes",
     "kvc_status_string", "kvc_last_error", "kvc_version",
 ]
 
@@ -60,6 +61,13 @@ _SIGS = {
     "kvc_assign_qsac": (ctypes.c_int, [_i32, _i64, _i32, ctypes.c_int, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp]),
     "kvc_query_stats": (ctypes.c_int, [_i32, _i64, _i32, ctypes.c_int, _vp, _i64, _vp, _vp]),
     "kvc_route_frames": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _vp]),
+    "kvc_query_moments": (ctypes.c_int, [_i32, _i64, _i32, ctypes.c_int, _vp, _i64, _vp, _vp]),
+    "kvc_psac_basis": (ctypes.c_int, [_i32, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "kvc_psac_coeffs": (ctypes.c_int, [_i32, _i64, _i32, ctypes.c_int, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32,
+                                       _vp, _i32, _vp, _vp]),
+    "kvc_attend_psac": (ctypes.c_int, [_i32, _i64, _i32, ctypes.c_int, _vp, _vp, _i32, ctypes.POINTER(KvcSegment),
+                                       ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _sz, _vp]),
+    "kvc_attend_psac_workspace_bytes": (_sz, [_i32, _i64, _i32, ctypes.c_int, ctypes.POINTER(KvcSegment), _i32]),
     "kvc_anchor_bits": (_i32, [_i32, _i32]),
     "kvc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kvc_last_error": (ctypes.c_char_p, []),

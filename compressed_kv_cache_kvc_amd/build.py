@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvc.so")
 
-SOURCES = ["api.cpp", "encode.hip", "assign.hip", "attend.hip", "merge.hip", "qsac.hip"]
+SOURCES = ["api.cpp", "encode.hip", "assign.hip", "attend.hip", "merge.hip", "qsac.hip", "psac.hip"]
 
 COMMON = [
     "-x", "hip", "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

@@ -72,7 +72,7 @@ CodecKey codec_of(const kvc_segment& s) {
 // of first appearance).  Without allow_mixed every segment must share one codec.
 kvc_status check_segments(int32_t heads, int32_t dim, const kvc_segment* segs, int32_t n_segs,
                           int32_t want_rank, bool allow_mixed, kvc::SegList* out, CodecKey* codecs,
-                          int* n_codecs, int* codec_of_seg) {
+                          int* n_codecs, int* codec_of_seg, const uint16_t* const* psac_coefs = nullptr) {
   KVC_REQUIRE(n_segs >= 0, KVC_ERR_INVALID_ARG, "n_segs < 0");
   KVC_REQUIRE(n_segs == 0 || segs != nullptr, KVC_ERR_INVALID_ARG, "segs is NULL");
   KVC_REQUIRE(n_segs <= kvc::kMaxSegs, KVC_ERR_UNSUPPORTED, "at most %d segments per call", kvc::kMaxSegs);
@@ -132,6 +132,12 @@ kvc_status check_segments(int32_t heads, int32_t dim, const kvc_segment* segs, i
     d.v_cent = s.v_cent;
     d.k_tab = nullptr;
     d.v_tab = nullptr;
+    d.psac = nullptr;
+    if (psac_coefs != nullptr) {
+      KVC_REQUIRE(!raw, KVC_ERR_UNSUPPORTED, "segment %d: the logit compensation reads 2/4-bit keys only", i);
+      KVC_PTR(psac_coefs[i], true, "segment compensation coefficients");
+      d.psac = psac_coefs[i];
+    }
     out->total_tiles += tiles_of(s.n_tokens);
   }
   (void)heads;
@@ -409,9 +415,10 @@ size_t kvc_attend_workspace_bytes(int32_t heads, int64_t n_q, int32_t dim, kvc_d
   return split_bytes(heads, n_q, dim, parts) + table_bytes(heads, dim, segs, n_segs);
 }
 
-kvc_status kvc_attend(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype, const void* q,
-                      const kvc_segment* segs, int32_t n_segs, float* out, float* lse, void* ws,
-                      size_t ws_bytes, hipStream_t stream) {
+namespace {
+kvc_status attend_impl(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype, const void* q,
+                       const kvc_segment* segs, int32_t n_segs, float* out, float* lse, void* ws, size_t ws_bytes,
+                       hipStream_t stream, const float* u_psac, const uint16_t* const* psac_coefs) {
   try {
     KVC_REQUIRE(heads >= 0 && n_q >= 0, KVC_ERR_INVALID_ARG, "heads and n_q must be >= 0");
     KVC_REQUIRE(dim == 64 || dim == 128, KVC_ERR_INVALID_ARG, "dim must be 64 or 128");
@@ -421,12 +428,17 @@ kvc_status kvc_attend(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype
     int n_codecs = 0;
     int codec_of_seg[kvc::kMaxSegs];
     kvc_status st = check_segments(heads, dim, segs, n_segs, 0, /*allow_mixed=*/true, &sl, codecs, &n_codecs,
-                                   codec_of_seg);
+                                   codec_of_seg, psac_coefs);
     if (st != KVC_OK) return st;
     const bool work = heads > 0 && n_q > 0;
     KVC_PTR(q, work, "q");
     KVC_PTR(out, work, "out");
     KVC_PTR(lse, work, "lse");
+    if (u_psac != nullptr) {
+      KVC_PTR(u_psac, work, "u");
+      KVC_REQUIRE(dim == 128 && q_dtype == KVC_BF16, KVC_ERR_UNSUPPORTED,
+                  "the logit compensation needs dim 128 and bf16 queries");
+    }
     if (!work) return ok();
     KVC_REQUIRE(heads <= 65535 && (n_q + 255) / 256 * heads <= (int64_t(1) << 27), KVC_ERR_UNSUPPORTED,
                 "at most 65535 heads and 2^27 blocks of 256 queries per call");
@@ -490,7 +502,7 @@ kvc_status kvc_attend(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype
       float* po = parts > 1 ? part_out + slot * rows * dim : out;
       float* pl = parts > 1 ? part_lse + slot * rows : lse;
       e = kvc::launch_attend(heads, n_q, dim, q_dtype, q, g, codecs[ci].kb, codecs[ci].vb, codecs[ci].g,
-                             codecs[ci].cdt, split_of[ci], po, pl, stream);
+                             codecs[ci].cdt, split_of[ci], po, pl, stream, u_psac);
       if (e != hipSuccess) return hip_status(e, "attend");
       slot += split_of[ci];
     }
@@ -501,6 +513,94 @@ kvc_status kvc_attend(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype
     return ok();
   } catch (...) {
     return fail(KVC_ERR_HIP, "unexpected exception in kvc_attend");
+  }
+}
+}  // namespace
+
+kvc_status kvc_attend(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype, const void* q,
+                      const kvc_segment* segs, int32_t n_segs, float* out, float* lse, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  return attend_impl(heads, n_q, dim, q_dtype, q, segs, n_segs, out, lse, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+// ------------------------------------------------------------------------------ logit compensation
+kvc_status kvc_attend_psac(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype, const void* q,
+                           const float* u, int32_t r, const kvc_segment* segs, const uint16_t* const* coefs,
+                           int32_t n_segs, float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  KVC_REQUIRE(r == kvc::kPsacRank, KVC_ERR_UNSUPPORTED, "the compensation rank must be %d", kvc::kPsacRank);
+  KVC_REQUIRE(n_segs == 0 || coefs != nullptr, KVC_ERR_INVALID_ARG, "coefs is NULL");
+  KVC_REQUIRE(u != nullptr || heads == 0 || n_q == 0, KVC_ERR_INVALID_ARG, "u is NULL");
+  return attend_impl(heads, n_q, dim, q_dtype, q, segs, n_segs, out, lse, ws, ws_bytes, stream, u, coefs);
+}
+
+size_t kvc_attend_psac_workspace_bytes(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype,
+                                       const kvc_segment* segs, int32_t n_segs) {
+  return kvc_attend_workspace_bytes(heads, n_q, dim, q_dtype, segs, n_segs);
+}
+
+kvc_status kvc_query_moments(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype, const void* q,
+                             int64_t n_prev, float* m, hipStream_t stream) {
+  try {
+    KVC_REQUIRE(heads >= 0 && n_q >= 0 && n_prev >= 0, KVC_ERR_INVALID_ARG, "heads, n_q and n_prev must be >= 0");
+    KVC_REQUIRE(heads <= 65535, KVC_ERR_UNSUPPORTED, "at most 65535 heads per call");
+    KVC_REQUIRE(dim == 64 || dim == 128, KVC_ERR_INVALID_ARG, "dim must be 64 or 128");
+    KVC_REQUIRE(valid_dtype(q_dtype), KVC_ERR_INVALID_ARG, "bad dtype");
+    const bool work = heads > 0 && n_q > 0;
+    KVC_PTR(q, work, "q");
+    KVC_PTR(m, work, "m");
+    if (!work) return ok();
+    return hip_status(kvc::launch_query_moments(heads, n_q, dim, q_dtype, q, n_prev, m, stream), "query moments");
+  } catch (...) {
+    return fail(KVC_ERR_HIP, "unexpected exception in kvc_query_moments");
+  }
+}
+
+kvc_status kvc_psac_basis(int32_t heads, int32_t dim, const float* m, int32_t r, int32_t n_iter,
+                          const float* u_prev, float* u, float* lam, hipStream_t stream) {
+  try {
+    KVC_REQUIRE(heads >= 0 && n_iter >= 0, KVC_ERR_INVALID_ARG, "heads and n_iter must be >= 0");
+    KVC_REQUIRE(dim == 64 || dim == 128, KVC_ERR_INVALID_ARG, "dim must be 64 or 128");
+    KVC_REQUIRE(r == kvc::kPsacRank, KVC_ERR_UNSUPPORTED, "the compensation rank must be %d", kvc::kPsacRank);
+    const bool work = heads > 0;
+    KVC_PTR(m, work, "m");
+    KVC_PTR(u, work, "u");
+    KVC_PTR(lam, work, "lam");
+    if (u_prev) KVC_PTR(u_prev, work, "u_prev");
+    if (!work) return ok();
+    return hip_status(kvc::launch_psac_basis(heads, dim, m, n_iter, u_prev, u, lam, stream), "psac basis");
+  } catch (...) {
+    return fail(KVC_ERR_HIP, "unexpected exception in kvc_psac_basis");
+  }
+}
+
+kvc_status kvc_psac_coeffs(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt, const void* x,
+                           int32_t n_centroids, const void* centroids, const uint8_t* ids, const uint8_t* codes,
+                           const uint16_t* meta, int32_t bits, int32_t group, const float* u, int32_t r,
+                           uint16_t* coef, hipStream_t stream) {
+  try {
+    KVC_REQUIRE(heads >= 0 && n_tokens >= 0, KVC_ERR_INVALID_ARG, "heads and n_tokens must be >= 0");
+    KVC_REQUIRE(dim == 64 || dim == 128, KVC_ERR_INVALID_ARG, "dim must be 64 or 128");
+    KVC_REQUIRE(valid_dtype(dt), KVC_ERR_INVALID_ARG, "bad dtype");
+    KVC_REQUIRE(n_centroids >= 1 && n_centroids <= 256, KVC_ERR_INVALID_ARG, "n_centroids must be in [1, 256]");
+    KVC_REQUIRE(bits == 2 || bits == 4, KVC_ERR_UNSUPPORTED, "bits must be 2 or 4");
+    KVC_REQUIRE(group > 0 && dim % group == 0, KVC_ERR_INVALID_ARG, "group must divide dim");
+    KVC_REQUIRE(group == 16 || group == 32, KVC_ERR_UNSUPPORTED, "group must be 16 or 32");
+    KVC_REQUIRE(r == kvc::kPsacRank, KVC_ERR_UNSUPPORTED, "the compensation rank must be %d", kvc::kPsacRank);
+    KVC_REQUIRE(heads <= 65535, KVC_ERR_UNSUPPORTED, "at most 65535 heads per call");
+    const bool work = heads > 0 && n_tokens > 0;
+    KVC_PTR(x, work, "x");
+    KVC_PTR(centroids, work, "centroids");
+    KVC_PTR(ids, work, "ids");
+    KVC_PTR(codes, work, "codes");
+    KVC_PTR(meta, work, "meta");
+    KVC_PTR(u, work, "u");
+    KVC_PTR(coef, work, "coef");
+    if (!work) return ok();
+    return hip_status(kvc::launch_psac_coeffs(heads, n_tokens, dim, dt, x, n_centroids, centroids, ids, codes, meta,
+                                              bits, group, u, coef, stream),
+                      "psac coefficients");
+  } catch (...) {
+    return fail(KVC_ERR_HIP, "unexpected exception in kvc_psac_coeffs");
   }
 }
 

@@ -55,6 +55,7 @@ struct AttendParams {
   float* out;             // [n_split][H][n_q][DOUT]
   float* lse;             // [n_split][H][n_q]
   const float* basis_v;   // low-dim: [H][DOUT][DQ]
+  const float* u_psac;    // logit compensation: [H][DQ][8] principal query directions
 };
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -181,9 +182,10 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 template <int DQ, bool LOWDIM>
 constexpr bool kSeqSchedule = LOWDIM && DQ == 32;
 
-template <int DQ, int KB, int VB, int G, bool LOWDIM, int DOUT>
+template <int DQ, int KB, int VB, int G, bool LOWDIM, int DOUT, bool PSAC = false>
 __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void attend_kernel(AttendParams p, SegList segs) {
   constexpr bool SEQ = kSeqSchedule<DQ, LOWDIM>;
+  static_assert(!PSAC || (!LOWDIM && !SEQ), "logit compensation: full-dimensional path only");
   constexpr int NK = SEQ ? 5 : 4;  // K tile buffers
   constexpr int KC = DQ / 16;     // k-chunks of the QK^T product
   constexpr int NDB = DQ / 32;    // 32-row blocks of O^T
@@ -269,6 +271,7 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
     const uint8_t *k_codes, *v_codes;
     const uint32_t *k_meta, *v_meta;
     const uint16_t *k_tab, *v_tab;
+    const uint16_t* psac;
   };
   auto span_load = [&](Span& c, int si) {
     c.si = si;
@@ -294,6 +297,7 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
     const int64_t hc = int64_t(h) * s.n_centroids * DQ;
     c.k_tab = s.k_tab + hc;
     c.v_tab = s.v_tab + hc;
+    if constexpr (PSAC) c.psac = s.psac + hn * 8;
   };
   auto ids_seek = [&](IdCur& c, int t) {
     while (t >= c.s.tile_end) ids_load(c, c.s.si + 1);
@@ -319,6 +323,7 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
   code_t<VNB> vc_r{};
   // metadata words (scale | zero << 16); 16-bit residuals keep (1, 0)
   uint32_t km_r = KB == 16 ? 0x3c00u : 0u, vm_r = VB == 16 ? 0x3c00u : 0u;
+  uint4 pc_r = make_uint4(0, 0, 0, 0);   // kept key-error coefficients of the token (dg == 7 lanes)
   uint32_t kcw[CWD], vcw[CWD];
 
   auto load_ids = [&](const IdCur& c, int t, int& ki, int& vi) {
@@ -330,6 +335,8 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
     const uint32_t j = row_of(c.s, t);
     kc_r = load_code_bits<KNB>(c.k_codes + (j * uint32_t(DQ * KB / 8) + uint32_t(dg * KNB)));
     vc_r = load_code_bits<VNB>(c.v_codes + (j * uint32_t(DQ * VB / 8) + uint32_t(dg * VNB)));
+    if constexpr (PSAC)
+      if (dg == 7) pc_r = *reinterpret_cast<const uint4*>(c.psac + j * 8u);
     if constexpr (KB != 16) km_r = c.k_meta[j * uint32_t(DQ / G) + uint32_t((dg * CH) / G)];
     if constexpr (VB != 16) vm_r = c.v_meta[j * uint32_t(DQ / G) + uint32_t((dg * CH) / G)];
     const uint16_t* kp = c.k_tab + (uint32_t(ki) * DQ + dg * CH);
@@ -374,6 +381,9 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
       static_assert(CH == 4, "channels per thread");
       reinterpret_cast<uint2*>(kdst)[0] = make_uint2(kw[0], kw[1]);
     }
+    // the token's compensation coefficients go to the row's 8 padding columns
+    if constexpr (PSAC)
+      if (dg == 7) *reinterpret_cast<uint4*>(&sK[kbuf][dk * ROWK + DQ]) = pc_r;
     // values: (q*s + z) and the centre add in packed fp16 (two roundings; an
     // error in a value moves only its own share of the output)
     const CodePairs<VB, CH> vq(vc_r);
@@ -402,6 +412,37 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
 
   auto clamp_t = [&](int t) { return t < t_end ? t : t_end - 1; };
 
+  // Logit compensation (kept key error along the principal query directions): the
+  // B operand holds U^T q (8 values, fp16) in k = 0..7 and zeros in k = 8..15; the A
+  // operand is the key rows' 8 coefficients in their padding columns (the upper
+  // half lanes read the same finite values, multiplied by those zeros).
+  f16x8 qpf = as_f16x8(make_uint4(0, 0, 0, 0));
+  if constexpr (PSAC) {
+    if (q_ok && half == 0) {
+      const uint16_t* qrow = p.q + (int64_t(h) * p.n_q + qi) * DQ;
+      const float* U = p.u_psac + int64_t(h) * DQ * 8;
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < DQ; ++c) {
+        const float qc = __uint_as_float(uint32_t(qrow[c]) << 16);
+        const float4 u0 = *reinterpret_cast<const float4*>(U + c * 8);
+        const float4 u1 = *reinterpret_cast<const float4*>(U + c * 8 + 4);
+        acc[0] = fmaf(u0.x, qc, acc[0]); acc[1] = fmaf(u0.y, qc, acc[1]);
+        acc[2] = fmaf(u0.z, qc, acc[2]); acc[3] = fmaf(u0.w, qc, acc[3]);
+        acc[4] = fmaf(u1.x, qc, acc[4]); acc[5] = fmaf(u1.y, qc, acc[5]);
+        acc[6] = fmaf(u1.z, qc, acc[6]); acc[7] = fmaf(u1.w, qc, acc[7]);
+      }
+      qpf = as_f16x8(make_uint4(pack_f16x2(acc[0], acc[1]), pack_f16x2(acc[2], acc[3]),
+                                pack_f16x2(acc[4], acc[5]), pack_f16x2(acc[6], acc[7])));
+    }
+  }
+  auto psac_qk = [&](int kbuf_, f32x16 (&sacc)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const f16x8 a = as_f16x8(*reinterpret_cast<const uint4*>(&sK[kbuf_][(kb * 32 + col) * ROWK + DQ]));
+      sacc[kb] = mfma32h(a, qpf, sacc[kb]);
+    }
+  };
+
   // S^T = K_hat Q^T of the K tile in buffer kb_, keys [0, 32) and [32, 64)
   auto qk = [&](int kb_, f32x16 (&sacc)[2]) {
 #pragma unroll
@@ -415,6 +456,7 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
         const f16x8 a = as_f16x8(*reinterpret_cast<const uint4*>(&sK[kb_][(kb * 32 + col) * ROWK + kc * 16 + half * 8]));
         sacc[kb] = mfma32h(a, qf[kc], sacc[kb]);
       }
+    if constexpr (PSAC) psac_qk(kb_, sacc);
   };
 
   // mask the keys past the end of the segment, raise the reference maximum when
@@ -567,6 +609,8 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
         } else if ((j & 3) == 3) {
           reinterpret_cast<uint4*>(kdst)[j >> 2] = make_uint4(kw[j - 3], kw[j - 2], kw[j - 1], kw[j]);
         }
+        if constexpr (PSAC)
+          if (j == CH / 2 - 1 && dg == 7) *reinterpret_cast<uint4*>(&sK[kstore][dk * ROWK + DQ]) = pc_r;
       } else {
         const int jj = j - CH / 2;
         vw[jj] = as_u32(__builtin_elementwise_fma(vq.pair(jj), vs, vz) + as_h2(vcw[jj]));
@@ -604,6 +648,7 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
         for (int u = 0; u < PPM; ++u) exp_pair(i * PPM + u);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if constexpr (PSAC) psac_qk(kread, nxt);
     }
     l_run += psum;
 #pragma unroll
@@ -826,17 +871,17 @@ __global__ __launch_bounds__(256) void centre_tables_kernel(TableJobs jobs) {
                               pack_f16x2(bf16_lo(w.z), bf16_lo(w.w)), pack_f16x2(bf16_hi(w.z), bf16_hi(w.w)));
 }
 
-template <int DQ, bool LOWDIM, int DOUT>
+template <int DQ, bool LOWDIM, int DOUT, bool PSAC = false>
 hipError_t pick_bits(const AttendParams& p, const SegList& segs, int kb, int vb, int g, hipStream_t st) {
   const dim3 grid(unsigned((p.n_q + 255) / 256) * unsigned(p.heads) * unsigned(p.n_split));
-#define KVC_CASE(KB_, VB_, G_)                                                                               \
-  if (kb == KB_ && vb == VB_ && g == G_) {                                                                   \
-    hipLaunchKernelGGL((attend_kernel<DQ, KB_, VB_, G_, LOWDIM, DOUT>), grid, dim3(512), 0, st, p, segs); \
-    return hipGetLastError();                                                                                \
+#define KVC_CASE(KB_, VB_, G_)                                                                                     \
+  if (kb == KB_ && vb == VB_ && g == G_) {                                                                         \
+    hipLaunchKernelGGL((attend_kernel<DQ, KB_, VB_, G_, LOWDIM, DOUT, PSAC>), grid, dim3(512), 0, st, p, segs); \
+    return hipGetLastError();                                                                                      \
   }
   KVC_CASE(2, 2, 16) KVC_CASE(2, 4, 16) KVC_CASE(4, 2, 16) KVC_CASE(4, 4, 16)
   KVC_CASE(2, 2, 32) KVC_CASE(2, 4, 32) KVC_CASE(4, 2, 32) KVC_CASE(4, 4, 32)
-  if constexpr (!LOWDIM) {
+  if constexpr (!LOWDIM && !PSAC) {
     KVC_CASE(16, 16, 16)     // 16-bit residual segments (no groups; G is nominal)
   }
 #undef KVC_CASE
@@ -864,7 +909,7 @@ hipError_t pick_f32(const float* q, int64_t n_q, int heads, const SegList& segs,
 
 hipError_t launch_attend(int heads, int64_t n_q, int dim, kvc_dtype q_dtype, const void* q, const SegList& segs,
                          int k_bits, int v_bits, int group, kvc_dtype cdt, int n_split, float* out, float* lse,
-                         hipStream_t st) {
+                         hipStream_t st, const float* u_psac) {
   if (heads == 0 || n_q == 0) return hipSuccess;
   if (segs.total_tiles == 0) {
     // empty history: out = 0, lse = -inf, through the merge kernel with one -inf part
@@ -885,7 +930,12 @@ hipError_t launch_attend(int heads, int64_t n_q, int dim, kvc_dtype q_dtype, con
   p.out = out;
   p.lse = lse;
   p.basis_v = nullptr;
+  p.u_psac = u_psac;
   if (cdt != KVC_BF16 && segs.total_tiles > 0) return hipErrorInvalidValue;
+  if (u_psac != nullptr && segs.total_tiles > 0) {
+    if (dim != 128) return hipErrorInvalidValue;
+    return pick_bits<128, false, 128, true>(p, segs, k_bits, v_bits, group, st);
+  }
   if (dim == 128) return pick_bits<128, false, 128>(p, segs, k_bits, v_bits, group, st);
   if (dim == 64) return pick_bits<64, false, 64>(p, segs, k_bits, v_bits, group, st);
   return hipErrorInvalidValue;
@@ -952,6 +1002,7 @@ hipError_t launch_attend_lowdim(int heads, int64_t n_q, int dim, int rank, const
   p.out = out;
   p.lse = lse;
   p.basis_v = basis_v;
+  p.u_psac = nullptr;
   if (dim != 128) return hipErrorInvalidValue;
   if (rank == 32) return pick_bits<32, true, 128>(p, segs, k_bits, v_bits, group, st);
   if (rank == 64) return pick_bits<64, true, 128>(p, segs, k_bits, v_bits, group, st);

@@ -30,6 +30,8 @@ struct SegDev {
   // the centres themselves (full dim) or their projections (low dim)
   const uint16_t* k_tab;
   const uint16_t* v_tab;
+  // kept key-error coefficients of the logit compensation [heads][n][8] fp16, or NULL
+  const uint16_t* psac;
 };
 
 struct SegList {
@@ -59,6 +61,16 @@ constexpr int kListChunk = 16384;      // tokens per member-list chunk (ids stag
 hipError_t launch_assign_qsac(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C,
                               const void* cent, const float* w, int n_cand, int group, uint8_t* ids,
                               hipStream_t st);
+// Logit compensation: running query second-moment matrices [heads][dim][dim], their
+// top-kPsacRank eigenvectors [heads][dim][kPsacRank] (+ eigenvalues), and the kept
+// key-error coefficients [heads][n][kPsacRank] fp16.
+hipError_t launch_query_moments(int heads, int64_t n_q, int dim, kvc_dtype dt, const void* q, int64_t n_prev,
+                                float* m, hipStream_t st);
+hipError_t launch_psac_basis(int heads, int dim, const float* m, int n_iter, const float* u_prev, float* u,
+                             float* lam, hipStream_t st);
+hipError_t launch_psac_coeffs(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C, const void* cent,
+                              const uint8_t* ids, const uint8_t* codes, const uint16_t* meta, int bits, int group,
+                              const float* u, uint16_t* coef, hipStream_t st);
 // Running per-channel second moments of the queries (w updated in place).
 hipError_t launch_query_stats(int heads, int64_t n_q, int dim, kvc_dtype dt, const void* q, int64_t n_prev,
                               float* w, hipStream_t st);
@@ -71,9 +83,12 @@ hipError_t launch_lse_merge_strided(int heads, int64_t n_q, int dim, int n_parts
 
 // Full-dim attention.  If n_split > 1, writes partial (out, lse) for split s at
 // part_out + s*heads*n_q*dim and part_lse + s*heads*n_q.
+// u_psac: NULL, or [heads][dim][kPsacRank] fp32 principal query directions; then
+// every segment carries its kept key-error coefficients (SegDev::psac).
 hipError_t launch_attend(int heads, int64_t n_q, int dim, kvc_dtype q_dtype, const void* q,
                          const SegList& segs, int k_bits, int v_bits, int group, kvc_dtype cdt,
-                         int n_split, float* out, float* lse, hipStream_t st);
+                         int n_split, float* out, float* lse, hipStream_t st, const float* u_psac = nullptr);
+constexpr int kPsacRank = 8;           // kept directions of the logit compensation
 
 hipError_t launch_project_queries(int heads, int64_t n_q, int dim, int rank, const void* q,
                                   const float* basis, uint16_t* q_proj, hipStream_t st);

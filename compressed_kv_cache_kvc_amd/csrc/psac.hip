@@ -1,0 +1,314 @@
+// Principal-subspace logit compensation of the remaining key error (PSAC;
+// QuantWM, section 4.2, Eqs. 13-17): the queries' second-moment matrix
+// M = E[q q^T], its top-r eigenvectors U_r (the principal query subspace), and the
+// kept coefficients C = (K - K_hat_0) U_r of each key's quantization error.  The
+// attention kernel adds (U_r^T q) . c to every logit (attend.hip).
+#include "kvc_internal.h"
+#include "dev_common.h"
+#include "mfma.h"
+
+namespace kvc {
+namespace {
+
+// M <- (n_prev * M + sum_i q_i q_i^T) / (n_prev + n_q) for one 32 x 32 tile of
+// one head: 256 threads, thread t owns row 32*bi + t/8 and columns 32*bj +
+// 4*(t%8) .. +3; the queries pass through LDS 64 rows at a time, and each output
+// sums over the queries in increasing order (fp32 multiply-adds).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void query_moments_kernel(const T* __restrict__ q, int64_t n_q, int64_t n_prev,
+                                                            float* __restrict__ m) {
+  constexpr int NT = D / 32;
+  __shared__ float sa[64][33], sb[64][33];
+  const int h = blockIdx.y;
+  const int bi = blockIdx.x / NT, bj = blockIdx.x % NT;
+  const int t = threadIdx.x;
+  const int row = t / 8, c0 = 4 * (t % 8);
+  const T* qh = q + int64_t(h) * n_q * D;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t i0 = 0; i0 < n_q; i0 += 64) {
+    __syncthreads();
+    // 64 rows x 32 channels of each block: 2048 values, 8 per thread
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int e = t + 256 * k;
+      const int r = e / 32, c = e % 32;
+      const int64_t qi = i0 + r;
+      float a = 0.f, b = 0.f;
+      if (qi < n_q) {
+        const T* rowp = qh + qi * D;
+        if constexpr (sizeof(T) == 2) {
+          a = __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(rowp)[bi * 32 + c]) << 16);
+          b = __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(rowp)[bj * 32 + c]) << 16);
+        } else {
+          a = reinterpret_cast<const float*>(rowp)[bi * 32 + c];
+          b = reinterpret_cast<const float*>(rowp)[bj * 32 + c];
+        }
+      }
+      sa[r][c] = a;
+      sb[r][c] = b;
+    }
+    __syncthreads();
+    const int nr = n_q - i0 < 64 ? int(n_q - i0) : 64;
+    for (int r = 0; r < nr; ++r) {
+      const float a = sa[r][row];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = fmaf(a, sb[r][c0 + k], acc[k]);
+    }
+  }
+  float* mh = m + int64_t(h) * D * D;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float* dst = mh + int64_t(bi * 32 + row) * D + bj * 32 + c0 + k;
+    double tot = double(acc[k]);
+    if (n_prev > 0) tot += double(*dst) * double(n_prev);
+    *dst = float(tot / double(n_prev + n_q));
+  }
+}
+
+// Eigen-decomposition of the symmetric R x R matrix a (row-major, overwritten)
+// by cyclic Jacobi rotations; eigenvectors in the columns of v.  One thread.
+template <int R>
+__device__ void jacobi_eig(float (&a)[R][R], float (&v)[R][R]) {
+  for (int i = 0; i < R; ++i)
+    for (int j = 0; j < R; ++j) v[i][j] = i == j ? 1.f : 0.f;
+  for (int sweep = 0; sweep < 30; ++sweep) {
+    float off = 0.f;
+    for (int i = 0; i < R; ++i)
+      for (int j = i + 1; j < R; ++j) off += a[i][j] * a[i][j];
+    if (off < 1e-30f) break;
+    for (int p = 0; p < R; ++p)
+      for (int qq = p + 1; qq < R; ++qq) {
+        if (a[p][qq] == 0.f) continue;
+        // rotation that zeroes a[p][qq] (the standard symmetric Schur step)
+        const float theta = 0.5f * (a[qq][qq] - a[p][p]) / a[p][qq];
+        const float tt = (theta >= 0.f ? 1.f : -1.f) / (fabsf(theta) + sqrtf(theta * theta + 1.f));
+        const float c = 1.f / sqrtf(tt * tt + 1.f), s = tt * c;
+        for (int k = 0; k < R; ++k) {
+          const float akp = a[k][p], akq = a[k][qq];
+          a[k][p] = c * akp - s * akq;
+          a[k][qq] = s * akp + c * akq;
+        }
+        for (int k = 0; k < R; ++k) {
+          const float apk = a[p][k], aqk = a[qq][k];
+          a[p][k] = c * apk - s * aqk;
+          a[qq][k] = s * apk + c * aqk;
+        }
+        for (int k = 0; k < R; ++k) {
+          const float vkp = v[k][p], vkq = v[k][qq];
+          v[k][p] = c * vkp - s * vkq;
+          v[k][qq] = s * vkp + c * vkq;
+        }
+      }
+  }
+}
+
+// Top-R eigenvectors of one head's M by subspace iteration: V <- orth(M V),
+// n_iter times (modified Gram-Schmidt by one wavefront), then Rayleigh-Ritz:
+// the R x R matrix V^T M V is diagonalized and V rotated onto its eigenvectors,
+// largest eigenvalue first; each column's largest component is made positive.
+// The start is u_prev (warm) or a fixed dense pattern.
+template <int D, int R>
+__global__ __launch_bounds__(256) void psac_basis_kernel(const float* __restrict__ m, int n_iter,
+                                                         const float* __restrict__ u_prev, float* __restrict__ u,
+                                                         float* __restrict__ lam) {
+  __shared__ float sm[D][D + 1];
+  __shared__ float sv[D][R], sw[D][R];
+  __shared__ float st[R][R];
+  const int h = blockIdx.x;
+  const int t = threadIdx.x;
+  const float* mh = m + int64_t(h) * D * D;
+  for (int e = t; e < D * D; e += 256) sm[e / D][e % D] = mh[e];
+  for (int e = t; e < D * R; e += 256) {
+    const int i = e / R, k = e % R;
+    sv[i][k] = u_prev ? u_prev[int64_t(h) * D * R + e]
+                      : __sinf(0.37f * float(i + 1) * float(k + 1) + 0.11f * float(k)) + (i == k ? 1.f : 0.f);
+  }
+  __syncthreads();
+  auto multiply = [&]() {                     // sw = M sv
+    for (int e = t; e < D * R; e += 256) {
+      const int i = e / R, k = e % R;
+      float acc = 0.f;
+      for (int j = 0; j < D; ++j) acc = fmaf(sm[i][j], sv[j][k], acc);
+      sw[i][k] = acc;
+    }
+    __syncthreads();
+  };
+  auto orthonormalize = [&]() {               // sv = columns of sw, Gram-Schmidt (wave 0)
+    if (t < 64) {
+      for (int k = 0; k < R; ++k) {
+        for (int j = 0; j < k; ++j) {
+          float d = 0.f;
+          for (int i = t; i < D; i += 64) d += sv[i][j] * sw[i][k];
+          for (int o = 32; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
+          for (int i = t; i < D; i += 64) sw[i][k] -= d * sv[i][j];
+        }
+        float nn = 0.f;
+        for (int i = t; i < D; i += 64) nn += sw[i][k] * sw[i][k];
+        for (int o = 32; o >= 1; o >>= 1) nn += __shfl_xor(nn, o, 64);
+        const float inv = nn > 0.f ? 1.f / sqrtf(nn) : 0.f;
+        for (int i = t; i < D; i += 64) sv[i][k] = sw[i][k] * inv;
+      }
+    }
+    __syncthreads();
+  };
+  // orthonormal start
+  for (int e = t; e < D * R; e += 256) sw[e / R][e % R] = sv[e / R][e % R];
+  __syncthreads();
+  orthonormalize();
+  for (int it = 0; it < n_iter; ++it) {
+    multiply();
+    orthonormalize();
+  }
+  // Rayleigh-Ritz
+  multiply();
+  if (t < R * R) {
+    const int a = t / R, b = t % R;
+    float acc = 0.f;
+    for (int i = 0; i < D; ++i) acc = fmaf(sv[i][a], sw[i][b], acc);
+    st[a][b] = acc;
+  }
+  __syncthreads();
+  __shared__ float sy[R][R];
+  __shared__ int sorder[R];
+  if (t == 0) {
+    float a[R][R], y[R][R];
+    for (int i = 0; i < R; ++i)
+      for (int j = 0; j < R; ++j) a[i][j] = 0.5f * (st[i][j] + st[j][i]);
+    jacobi_eig<R>(a, y);
+    int order[R];
+    for (int i = 0; i < R; ++i) order[i] = i;
+    for (int i = 0; i < R; ++i)                       // by eigenvalue, largest first
+      for (int j = i + 1; j < R; ++j)
+        if (a[order[j]][order[j]] > a[order[i]][order[i]]) { const int x = order[i]; order[i] = order[j]; order[j] = x; }
+    for (int i = 0; i < R; ++i) {
+      sorder[i] = order[i];
+      lam[int64_t(h) * R + i] = a[order[i]][order[i]];
+      for (int j = 0; j < R; ++j) sy[j][i] = y[j][order[i]];
+    }
+  }
+  __syncthreads();
+  for (int e = t; e < D * R; e += 256) {       // U = V Y
+    const int i = e / R, k = e % R;
+    float acc = 0.f;
+    for (int j = 0; j < R; ++j) acc = fmaf(sv[i][j], sy[j][k], acc);
+    sw[i][k] = acc;
+  }
+  __syncthreads();
+  if (t < R) {                                 // sign: the largest component positive
+    int arg = 0;
+    float best = -1.f;
+    for (int i = 0; i < D; ++i)
+      if (fabsf(sw[i][t]) > best) { best = fabsf(sw[i][t]); arg = i; }
+    const float sg = sw[arg][t] < 0.f ? -1.f : 1.f;
+    for (int i = 0; i < D; ++i) u[int64_t(h) * D * R + i * R + t] = sg * sw[i][t];
+  }
+}
+
+// C = (x - x_hat_0) U_r per token: x_hat_0 = c[id] + q*s + z (fp32), the error's
+// coefficients summed over the channels in increasing order, stored as fp16.
+// One thread per token; U_r of the head in LDS.
+template <typename T, int D, int G, int BITS>
+__global__ __launch_bounds__(256) void psac_coeffs_kernel(const T* __restrict__ x, const T* __restrict__ cent,
+                                                          const uint8_t* __restrict__ ids,
+                                                          const uint8_t* __restrict__ codes,
+                                                          const uint32_t* __restrict__ meta, int C, int64_t n,
+                                                          const float* __restrict__ u, uint16_t* __restrict__ coef) {
+  constexpr int R = kPsacRank;
+  __shared__ float su[D][R];
+  const int h = blockIdx.y;
+  for (int e = threadIdx.x; e < D * R; e += 256) su[e / R][e % R] = u[int64_t(h) * D * R + e];
+  __syncthreads();
+  const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (j >= n) return;
+  const int64_t tok = int64_t(h) * n + j;
+  const int id = ids[tok];
+  const T* xr = x + tok * D;
+  const T* cr = cent + (int64_t(h) * C + id) * D;
+  const uint8_t* qr = codes + tok * (D * BITS / 8);
+  const uint32_t* mr = meta + tok * (D / G);
+  float acc[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) acc[k] = 0.f;
+  for (int g = 0; g < D / G; ++g) {
+    const uint32_t mw = mr[g];
+    const float s = f16_bits_to_f32(mw & 0xffffu), z = f16_bits_to_f32(mw >> 16);
+    for (int i = 0; i < G; i += 8) {
+      float xv[8], cv[8];
+      load_row<8>(xr + g * G + i, xv);
+      load_row<8>(cr + g * G + i, cv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = g * G + i + e;
+        const uint32_t qv = (uint32_t(qr[(c * BITS) / 8]) >> ((c * BITS) % 8)) & ((1u << BITS) - 1u);
+        const float xh = cv[e] + fmaf(float(qv), s, z);
+        const float err = xv[e] - xh;
+#pragma unroll
+        for (int k = 0; k < R; ++k) acc[k] = fmaf(err, su[c][k], acc[k]);
+      }
+    }
+  }
+  uint32_t w[R / 2];
+#pragma unroll
+  for (int k = 0; k < R / 2; ++k) w[k] = pack_f16x2(acc[2 * k], acc[2 * k + 1]);
+  *reinterpret_cast<uint4*>(coef + tok * R) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <typename T, int D>
+hipError_t coeffs_bits(int heads, int64_t n, const void* x, const void* cent, const uint8_t* ids,
+                       const uint8_t* codes, const uint16_t* meta, int C, int bits, int group, const float* u,
+                       uint16_t* coef, hipStream_t st) {
+  const dim3 grid(unsigned((n + 255) / 256), unsigned(heads));
+#define KVC_COEF(G_, B_)                                                                                        \
+  if (group == G_ && bits == B_) {                                                                              \
+    hipLaunchKernelGGL((psac_coeffs_kernel<T, D, G_, B_>), grid, dim3(256), 0, st, static_cast<const T*>(x),    \
+                       static_cast<const T*>(cent), ids, codes, reinterpret_cast<const uint32_t*>(meta), C, n, u, \
+                       coef);                                                                                   \
+    return hipGetLastError();                                                                                   \
+  }
+  KVC_COEF(16, 2) KVC_COEF(16, 4) KVC_COEF(32, 2) KVC_COEF(32, 4)
+#undef KVC_COEF
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_query_moments(int heads, int64_t n_q, int dim, kvc_dtype dt, const void* q, int64_t n_prev,
+                                float* m, hipStream_t st) {
+  if (heads == 0 || n_q == 0) return hipSuccess;
+  const int nt = dim / 32;
+  const dim3 grid(unsigned(nt * nt), unsigned(heads));
+#define KVC_MOM(T, D) \
+  hipLaunchKernelGGL((query_moments_kernel<T, D>), grid, dim3(256), 0, st, static_cast<const T*>(q), n_q, n_prev, m)
+  if (dt == KVC_BF16) {
+    if (dim == 128) KVC_MOM(bf16_t, 128); else KVC_MOM(bf16_t, 64);
+  } else {
+    if (dim == 128) KVC_MOM(float, 128); else KVC_MOM(float, 64);
+  }
+#undef KVC_MOM
+  return hipGetLastError();
+}
+
+hipError_t launch_psac_basis(int heads, int dim, const float* m, int n_iter, const float* u_prev, float* u,
+                             float* lam, hipStream_t st) {
+  if (heads == 0) return hipSuccess;
+  if (dim == 128)
+    hipLaunchKernelGGL((psac_basis_kernel<128, kPsacRank>), dim3(unsigned(heads)), dim3(256), 0, st, m, n_iter,
+                       u_prev, u, lam);
+  else
+    hipLaunchKernelGGL((psac_basis_kernel<64, kPsacRank>), dim3(unsigned(heads)), dim3(256), 0, st, m, n_iter,
+                       u_prev, u, lam);
+  return hipGetLastError();
+}
+
+hipError_t launch_psac_coeffs(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C, const void* cent,
+                              const uint8_t* ids, const uint8_t* codes, const uint16_t* meta, int bits, int group,
+                              const float* u, uint16_t* coef, hipStream_t st) {
+  if (heads == 0 || n == 0) return hipSuccess;
+  if (dt == KVC_BF16 && dim == 128) return coeffs_bits<bf16_t, 128>(heads, n, x, cent, ids, codes, meta, C, bits, group, u, coef, st);
+  if (dt == KVC_BF16 && dim == 64) return coeffs_bits<bf16_t, 64>(heads, n, x, cent, ids, codes, meta, C, bits, group, u, coef, st);
+  if (dt == KVC_F32 && dim == 128) return coeffs_bits<float, 128>(heads, n, x, cent, ids, codes, meta, C, bits, group, u, coef, st);
+  if (dt == KVC_F32 && dim == 64) return coeffs_bits<float, 64>(heads, n, x, cent, ids, codes, meta, C, bits, group, u, coef, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvc

@@ -136,6 +136,38 @@ kvc_status kvc_assign_qsac(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dty
 kvc_status kvc_query_stats(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype,
                            const void* q, int64_t n_prev, float* w, hipStream_t stream);
 
+/* Principal-subspace logit compensation, PSAC (QuantWM, section 4.2, Eqs. 13-17;
+ * r = 8 kept directions).
+ * kvc_query_moments: running second-moment matrices of the queries,
+ *   M <- (n_prev * M + sum_i q_i q_i^T) / (n_prev + n_q); q [heads][n_q][dim],
+ *   m [heads][dim][dim] fp32 in/out (ignored on input when n_prev = 0).
+ * kvc_psac_basis: the r eigenvectors of the largest eigenvalues of each M, as
+ *   u [heads][dim][r] fp32 (column k = k-th largest; its largest component
+ *   positive) and lam [heads][r]; subspace iteration (n_iter products with M and
+ *   re-orthonormalization, then Rayleigh-Ritz), started from u_prev when given.
+ * kvc_psac_coeffs: kept coefficients of the keys' remaining quantization error,
+ *   coef [heads][n][r] fp16 = (x - (c[id] + q*s + z)) u, from the same x,
+ *   centroids, ids, codes and meta (2/4-bit, group 16/32) that kvc_encode used.
+ * kvc_attend_psac: kvc_attend with every logit corrected by (u^T q) . coef_j,
+ *   i.e. attention on k_hat_j + u u^T (k_j - k_hat_j); coefs is a HOST array of
+ *   n_segs device pointers (one per segment, [heads][n_tokens][r] fp16); dim 128,
+ *   bf16 queries, 2/4-bit segments.  Workspace as for kvc_attend. */
+kvc_status kvc_query_moments(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype,
+                             const void* q, int64_t n_prev, float* m, hipStream_t stream);
+kvc_status kvc_psac_basis(int32_t heads, int32_t dim, const float* m, int32_t r, int32_t n_iter,
+                          const float* u_prev, float* u, float* lam, hipStream_t stream);
+kvc_status kvc_psac_coeffs(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt,
+                           const void* x, int32_t n_centroids, const void* centroids,
+                           const uint8_t* ids, const uint8_t* codes, const uint16_t* meta,
+                           int32_t bits, int32_t group, const float* u, int32_t r,
+                           uint16_t* coef, hipStream_t stream);
+kvc_status kvc_attend_psac(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype,
+                           const void* q, const float* u, int32_t r, const kvc_segment* segs,
+                           const uint16_t* const* coefs, int32_t n_segs, float* out, float* lse,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+size_t kvc_attend_psac_workspace_bytes(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype,
+                                       const kvc_segment* segs, int32_t n_segs);
+
 /* Frame routing of mixed-dimensional attention (NanoKV, Figure 4 and appendix
  * Table 7): frame f of a history of n_frames latent frames (0 = oldest) is read
  * at full dimension (full_dim[f] = 1) when n_frames <= all_full_until, or f >=
