@@ -43,6 +43,10 @@ def parse():
                     help="re-assign the keys after the fit with the query-aware assignment (QuantWM section 4.1) "
                          "over M candidates, weighted by the statistics of the previous chunks' queries, and "
                          "update those statistics after the attention (self_forcing_layer, streaming); 0 = off")
+    ap.add_argument("--psac", action="store_true",
+                    help="self_forcing_layer, streaming: compensate the keys' remaining error along the top-8 "
+                         "directions of the earlier queries (QuantWM section 4.2): kept coefficients after the "
+                         "encode, compensated attention, then the query moments and the basis updated")
     ap.add_argument("--route", default="", metavar="R,P,S,A",
                     help="larger_backbone: read at full dimension the R most recent latent frames, one anchor "
                          "per P older frames, the S oldest frames, or every frame while the history has at most "
@@ -69,6 +73,9 @@ class Workload:
         self.events = []
         self.side = None
         self.qsac = 0                 # candidates of the query-aware key assignment (0: plain ids)
+        self.psac = False             # logit compensation of the remaining key error
+        self.mq = None                # running query second moments [H, d, d]
+        self.u = None                 # principal query directions [H, d, 8]
         self.wq = None                # running query statistics [H, d] fp32
         self.n_seen = 0               # queries folded into wq
 
@@ -126,7 +133,38 @@ def fit_encode_pair(w, k, kc0, v, vc0, n_iter=2):
     vco, vme, _ = kvc.encode(v, vc, cfg.v_bits, cfg.group, ids=vid)
     e2 = w.ev()
     w.mark("encode", e1, e2)
+    if w.psac and w.u is not None:
+        w.coef = kvc.psac_coeffs(k, kc, kid, kco, kme, cfg.k_bits, cfg.group, w.u)
+        e3 = w.ev()
+        w.mark("psac_coeffs", e2, e3)
     return (kco, kme, kid, kc), (vco, vme, vid, vc)
+
+
+def attend_step(w, q, segs, coefs):
+    """The attention call of a step (compensated when PSAC is on and a basis exists)."""
+    import compressed_kv_cache_kvc_amd as kvc
+    e0 = w.ev()
+    if w.psac and w.u is not None:
+        out, lse = kvc.attend_psac(q, w.u, segs, coefs)
+    else:
+        out, lse = kvc.attend(q, segs)
+    e1 = w.ev()
+    w.mark("attend", e0, e1)
+    return out, lse
+
+
+def update_psac_basis(w, q):
+    """Fold the chunk's queries into the second moments and refresh the basis
+    (warm start from the previous one)."""
+    import compressed_kv_cache_kvc_amd as kvc
+    e0 = w.ev()
+    w.mq = kvc.query_moments(q, w.mq, n_prev=w.n_seen_m)
+    e1 = w.ev()
+    w.u, _ = kvc.psac_basis(w.mq, n_iter=4 if w.u is not None else 32, u_prev=w.u)
+    e2 = w.ev()
+    w.mark("query_moments", e0, e1)
+    w.mark("psac_basis", e1, e2)
+    w.n_seen_m += q.shape[1]
 
 
 def update_query_stats(w, q):
@@ -174,6 +212,12 @@ class SingleLayer(Workload):
             (kcodes, kmeta, kid, kc), (vcodes, vmeta, vid, vc) = fit_encode_pair(
                 self, self.k, self.kc0, self.v, self.vc0, n_iter=cfg.n_iter)
             segs = [kvc.Segment(kcodes, kmeta, kid, kc, vcodes, vmeta, vid, vc, cfg.k_bits, cfg.v_bits, cfg.group)]
+            if self.psac:
+                out, lse = attend_step(self, self.q, segs, [self.coef])
+                update_psac_basis(self, self.q)
+                if self.qsac:
+                    update_query_stats(self, self.q)
+                return out
         else:
             # one centre table per head over the whole history; each history
             # segment is encoded from its own slice (segments are attention splits)
@@ -198,6 +242,17 @@ class SingleLayer(Workload):
         if self.qsac:
             update_query_stats(self, self.q)
         return out
+
+    def enable_psac(self):
+        """Logit compensation; moments and basis start from a previous chunk's queries."""
+        import compressed_kv_cache_kvc_amd as kvc
+        if len(self.bounds) != 2 or self.cfg.dtype != "bf16":
+            raise SystemExit("--psac covers the single-segment bf16 workloads (self_forcing_layer, streaming)")
+        self.psac = True
+        prev = self.synth.queries(self.cfg, device=self.dev, stream_id=2)
+        self.mq = kvc.query_moments(prev)
+        self.u, _ = kvc.psac_basis(self.mq, n_iter=32)
+        self.n_seen_m = prev.shape[1]
 
     def enable_qsac(self, m):
         """Query-aware key assignment; the statistics start from a previous chunk's queries."""
@@ -370,17 +425,30 @@ class Streaming(Workload):
         out = None
         if self.qsac:                 # each rollout starts cold: unit weights for the first chunk
             self.wq, self.n_seen = None, 0
+        if self.psac:                 # cold start: no compensation until queries have been seen
+            self.mq, self.u, self.n_seen_m = None, None, 0
+        coefs = []
         for (k, v, q, kc0, vc0) in self.chunks:
             (kcodes, kmeta, kid, kc), (vcodes, vmeta, vid, vc) = fit_encode_pair(self, k, kc0, v, vc0,
                                                                                  n_iter=cfg.n_iter)
             segs.append(kvc.Segment(kcodes, kmeta, kid, kc, vcodes, vmeta, vid, vc, cfg.k_bits, cfg.v_bits, cfg.group))
-            e0 = self.ev()
-            out, lse = kvc.attend(q, segs)
-            e1 = self.ev()
-            self.mark("attend", e0, e1)
+            if self.psac:
+                # one basis per rollout, fixed after the first chunk (the cold start);
+                # the first chunk keeps zero coefficients (no compensation)
+                coefs.append(self.coef if self.u is not None else
+                             self.torch.zeros(cfg.heads, k.shape[1], 8, dtype=self.torch.uint16, device=self.dev))
+                out, lse = attend_step(self, q, segs, coefs) if self.u is not None else attend_step(self, q, segs, None)
+                if self.u is None:
+                    update_psac_basis(self, q)
+            else:
+                out, lse = attend_step(self, q, segs, None)
             if self.qsac:
                 update_query_stats(self, q)
         return out
+
+    def enable_psac(self):
+        self.psac = True
+        self.n_seen_m = 0
 
     def enable_qsac(self, m):
         self.qsac = m
@@ -505,6 +573,10 @@ def main():
     if (route is not None or args.anchor) and cfg.name != "larger_backbone":
         raise SystemExit("--route and --anchor apply to the larger_backbone workload")
     w = make_workload(cfg, dev, route, args.anchor)
+    if args.psac:
+        if not hasattr(w, "enable_psac"):
+            raise SystemExit("--psac covers the single-segment workloads (self_forcing_layer, streaming)")
+        w.enable_psac()
     if args.qsac:
         if not hasattr(w, "enable_qsac"):
             raise SystemExit("--qsac covers the single-segment workloads (self_forcing_layer, streaming, tiny)")
@@ -596,6 +668,10 @@ def main():
                           "scores_per_s": round(scores / (lowdim_ms * 1e-3), 1),
                           "exp_peak_per_s": exp_peak,
                           "exp_bound_frac": round(scores / (lowdim_ms * 1e-3) / exp_peak, 4)}
+    if w.psac:
+        for name in ("psac_coeffs", "query_moments", "psac_basis"):
+            line["phase_ms"][name] = round(phases.get(name, 0.0) / K, 4)
+        line["psac"] = {"rank": 8, "attention_includes_compensation": True}
     if w.qsac:
         # keys re-assigned per step: H*N tokens (all chunks for streaming); the
         # weighted distances are 2*C*d FLOP per token, the tokens are read once

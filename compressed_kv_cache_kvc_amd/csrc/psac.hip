@@ -11,7 +11,7 @@ namespace kvc {
 namespace {
 
 // M <- (n_prev * M + sum_i q_i q_i^T) / (n_prev + n_q) for one 32 x 32 tile of
-// one head: 256 threads, thread t owns row 32*bi + t/8 and columns 32*bj +
+// one head (fp32 queries): 256 threads, thread t owns row 32*bi + t/8 and columns 32*bj +
 // 4*(t%8) .. +3; the queries pass through LDS 64 rows at a time, and each output
 // sums over the queries in increasing order (fp32 multiply-adds).
 template <typename T, int D>
@@ -65,6 +65,64 @@ __global__ __launch_bounds__(256) void query_moments_kernel(const T* __restrict_
   }
 }
 
+// bf16 queries: the 32 x 32 tile (bi, bj) of sum_i q_i q_i^T on the matrix cores,
+// one wavefront per tile: A = Q^T rows (channels 32*bi ..), B = Q columns
+// (channels 32*bj ..), the contraction over 16 queries per
+// v_mfma_f32_32x32x16_bf16 (products of bf16 values are exact in fp32).  The
+// queries pass through LDS 64 at a time (zero rows past the end).
+template <int D>
+__global__ __launch_bounds__(64) void query_moments_mfma_kernel(const bf16_t* __restrict__ q, int64_t n_q,
+                                                                int64_t n_prev, float* __restrict__ m) {
+  constexpr int NT = D / 32;
+  constexpr int ROW = 40;                      // 32 channels + padding, 16-byte aligned rows
+  __shared__ __attribute__((aligned(16))) uint16_t sa[64 * ROW], sb[64 * ROW];
+  const int h = blockIdx.y;
+  const int bi = blockIdx.x / NT, bj = blockIdx.x % NT;
+  const int lane = threadIdx.x;
+  const uint16_t* qh = reinterpret_cast<const uint16_t*>(q) + int64_t(h) * n_q * D;
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  for (int64_t i0 = 0; i0 < n_q; i0 += 64) {
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {              // 64 rows x 4 chunks of 8 channels, per slice
+      const int e = lane + 64 * k;
+      const int r = e / 4, c8 = (e % 4) * 8;
+      uint4 wa = make_uint4(0, 0, 0, 0), wb = make_uint4(0, 0, 0, 0);
+      if (i0 + r < n_q) {
+        wa = *reinterpret_cast<const uint4*>(qh + (i0 + r) * D + bi * 32 + c8);
+        wb = *reinterpret_cast<const uint4*>(qh + (i0 + r) * D + bj * 32 + c8);
+      }
+      *reinterpret_cast<uint4*>(&sa[r * ROW + c8]) = wa;
+      *reinterpret_cast<uint4*>(&sb[r * ROW + c8]) = wb;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {           // 16 queries per product
+      uint32_t a[4], b[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r0 = kk * 16 + 8 * (lane / 32) + 2 * e;
+        a[e] = uint32_t(sa[r0 * ROW + lane % 32]) | (uint32_t(sa[(r0 + 1) * ROW + lane % 32]) << 16);
+        b[e] = uint32_t(sb[r0 * ROW + lane % 32]) | (uint32_t(sb[(r0 + 1) * ROW + lane % 32]) << 16);
+      }
+      acc = mfma32(as_bf16x8(make_uint4(a[0], a[1], a[2], a[3])), as_bf16x8(make_uint4(b[0], b[1], b[2], b[3])), acc);
+    }
+  }
+  // lane: column j = lane % 32, rows i = 8*(v/4) + 4*(lane/32) + v%4
+  float* mh = m + int64_t(h) * D * D;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int i = bi * 32 + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
+    const int j = bj * 32 + lane % 32;
+    float* dst = mh + int64_t(i) * D + j;
+    double tot = double(acc[v]);
+    if (n_prev > 0) tot += double(*dst) * double(n_prev);
+    *dst = float(tot / double(n_prev + n_q));
+  }
+}
+
 // Eigen-decomposition of the symmetric R x R matrix a (row-major, overwritten)
 // by cyclic Jacobi rotations; eigenvectors in the columns of v.  One thread.
 template <int R>
@@ -72,10 +130,12 @@ __device__ void jacobi_eig(float (&a)[R][R], float (&v)[R][R]) {
   for (int i = 0; i < R; ++i)
     for (int j = 0; j < R; ++j) v[i][j] = i == j ? 1.f : 0.f;
   for (int sweep = 0; sweep < 30; ++sweep) {
-    float off = 0.f;
-    for (int i = 0; i < R; ++i)
+    float off = 0.f, diag = 0.f;
+    for (int i = 0; i < R; ++i) {
+      diag += a[i][i] * a[i][i];
       for (int j = i + 1; j < R; ++j) off += a[i][j] * a[i][j];
-    if (off < 1e-30f) break;
+    }
+    if (off <= 1e-14f * diag) break;          // off-diagonal at fp32 rounding level
     for (int p = 0; p < R; ++p)
       for (int qq = p + 1; qq < R; ++qq) {
         if (a[p][qq] == 0.f) continue;
@@ -280,7 +340,12 @@ hipError_t launch_query_moments(int heads, int64_t n_q, int dim, kvc_dtype dt, c
 #define KVC_MOM(T, D) \
   hipLaunchKernelGGL((query_moments_kernel<T, D>), grid, dim3(256), 0, st, static_cast<const T*>(q), n_q, n_prev, m)
   if (dt == KVC_BF16) {
-    if (dim == 128) KVC_MOM(bf16_t, 128); else KVC_MOM(bf16_t, 64);
+    if (dim == 128)
+      hipLaunchKernelGGL((query_moments_mfma_kernel<128>), grid, dim3(64), 0, st, static_cast<const bf16_t*>(q), n_q,
+                         n_prev, m);
+    else
+      hipLaunchKernelGGL((query_moments_mfma_kernel<64>), grid, dim3(64), 0, st, static_cast<const bf16_t*>(q), n_q,
+                         n_prev, m);
   } else {
     if (dim == 128) KVC_MOM(float, 128); else KVC_MOM(float, 64);
   }
