@@ -135,13 +135,14 @@ struct CodePairs<16, CH> {
   }
 };
 
-// (fp16(t0 + c.lo), fp16(t1 + c.hi)) for fp32 t and a packed fp16 pair c, each with
-// a single rounding: v_fma_mix{lo,hi}_f16 with fp32 sources t and 1.0 and the fp16
-// source c, computed in fp32 and rounded once to the destination half.
-__device__ __forceinline__ uint32_t round_add_f16x2(float t0, float t1, uint32_t c) {
+// (fp16(c.lo * sc + t0), fp16(c.hi * sc + t1)) for fp32 t and sc and a packed fp16
+// pair c, each with a single rounding: v_fma_mix{lo,hi}_f16 with the fp16 source c
+// and the fp32 sources sc and t, computed in fp32 and rounded once to the
+// destination half.
+__device__ __forceinline__ uint32_t round_add_f16x2(float t0, float t1, uint32_t c, float sc) {
   uint32_t r;
-  asm("v_fma_mixlo_f16 %0, %1, 1.0, %2 op_sel_hi:[0,0,1]" : "=&v"(r) : "v"(t0), "v"(c));
-  asm("v_fma_mixhi_f16 %0, %1, 1.0, %2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(r) : "v"(t1), "v"(c));
+  asm("v_fma_mixlo_f16 %0, %2, %3, %1 op_sel_hi:[1,0,0]" : "=&v"(r) : "v"(t0), "v"(c), "v"(sc));
+  asm("v_fma_mixhi_f16 %0, %2, %3, %1 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(r) : "v"(t1), "v"(c), "v"(sc));
   return r;
 }
 
@@ -224,7 +225,10 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
   const bool q_ok = qi < p.n_q;
 
   // B operand Q^T in fp16, channels in tile order: bf16 queries convert exactly
-  // inside the fp16 range; reduced queries arrive in fp16 and tile order already
+  // inside the fp16 range; reduced queries arrive in fp16 and tile order already.
+  // The factor c = log2(e)/sqrt(d) goes into the key tile (inside its one fp16
+  // rounding), so that the score products are base-2 exponents already.
+  const float c_sc = p.scale_log2;
   f16x8 qf[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
@@ -359,17 +363,17 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
   auto zero2 = [](uint32_t m) { return as_h2(__builtin_amdgcn_perm(m, m, 0x03020302u)); };
 
   auto store_tile = [&](int kbuf, int vbuf) {
-    // keys: q*s + z in fp32 (exact but for one fp32 rounding), then one rounding of
-    // the sum with the centre to fp16; the key tile's rounding error moves every
-    // logit, so keys get the single-rounding form
+    // keys, scaled by c: c*(q*s + z) in fp32 (q*(c*s) + c*z), then one rounding of
+    // the sum with c times the centre to fp16; the key tile's rounding error moves
+    // every logit, so keys get the single-rounding form
     const CodePairs<KB, CH> kq(kc_r);
     const h2 km = as_h2(km_r);
-    const float ks = float(km[0]), kz = float(km[1]);
+    const float ks = float(km[0]) * c_sc, kz = float(km[1]) * c_sc;
     uint32_t kw[CH / 2];
 #pragma unroll
     for (int j = 0; j < CH / 2; ++j) {
       const h2 c = kq.pair(j);
-      kw[j] = round_add_f16x2(fmaf(float(c[0]), ks, kz), fmaf(float(c[1]), ks, kz), kcw[j]);
+      kw[j] = round_add_f16x2(fmaf(float(c[0]), ks, kz), fmaf(float(c[1]), ks, kz), kcw[j], c_sc);
     }
     uint16_t* kdst = &sK[kbuf][dk * ROWK + dg * CH];
     if constexpr (CH == 16) {
@@ -402,7 +406,9 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
     }
   };
 
-  float m_run = -INFINITY;        // reference maximum of the row, log2 units
+  // reference maximum of the row (log2 units), a sum of two fp16 values hi + lo
+  // that enters the scores through the bias product below; set from the first tile
+  float m_run = 0.f;
   float l_run = 0.f;              // this lane's share of the running sum
   f32x16 o[NDB];
 #pragma unroll
@@ -412,10 +418,17 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
 
   auto clamp_t = [&](int t) { return t < t_end ? t : t_end - 1; };
 
-  // Logit compensation (kept key error along the principal query directions): the
-  // B operand holds U^T q (8 values, fp16) in k = 0..7 and zeros in k = 8..15; the A
-  // operand is the key rows' 8 coefficients in their padding columns (the upper
-  // half lanes read the same finite values, multiplied by those zeros).
+  // Bias product: one more v_mfma_f32_32x32x16_f16 per 32 keys subtracts the
+  // reference maximum from the scores.  Upper-half lanes (k = 8..15) hold 1, 1 in the
+  // A operand and -m_hi, -m_lo of the lane's query in the B operand.  With logit
+  // compensation (kept key error along the principal query directions) the
+  // lower-half lanes (k = 0..7) hold the key rows' 8 coefficients (A, from the K
+  // row's padding columns) and c * U^T q (B, fp32 then fp16); otherwise their B
+  // entries are zero.
+  __shared__ __attribute__((aligned(16))) uint32_t sOne[4];
+  if (PSAC && tid == 0) {
+    sOne[0] = 0x3c003c00u; sOne[1] = 0u; sOne[2] = 0u; sOne[3] = 0u;
+  }
   f16x8 qpf = as_f16x8(make_uint4(0, 0, 0, 0));
   if constexpr (PSAC) {
     if (q_ok && half == 0) {
@@ -431,19 +444,25 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
         acc[4] = fmaf(u1.x, qc, acc[4]); acc[5] = fmaf(u1.y, qc, acc[5]);
         acc[6] = fmaf(u1.z, qc, acc[6]); acc[7] = fmaf(u1.w, qc, acc[7]);
       }
-      qpf = as_f16x8(make_uint4(pack_f16x2(acc[0], acc[1]), pack_f16x2(acc[2], acc[3]),
-                                pack_f16x2(acc[4], acc[5]), pack_f16x2(acc[6], acc[7])));
+      qpf = as_f16x8(make_uint4(pack_f16x2(c_sc * acc[0], c_sc * acc[1]), pack_f16x2(c_sc * acc[2], c_sc * acc[3]),
+                                pack_f16x2(c_sc * acc[4], c_sc * acc[5]), pack_f16x2(c_sc * acc[6], c_sc * acc[7])));
     }
   }
-  auto psac_qk = [&](int kbuf_, f32x16 (&sacc)[2]) {
+  f16x8 qbias = qpf;                                         // B operand of the bias product
+  const f16x8 a_one = as_f16x8(make_uint4(0x3c003c00u, 0u, 0u, 0u));
+  auto bias_qk = [&](int kbuf_, f32x16 (&sacc)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const f16x8 a = as_f16x8(*reinterpret_cast<const uint4*>(&sK[kbuf_][(kb * 32 + col) * ROWK + DQ]));
-      sacc[kb] = mfma32h(a, qpf, sacc[kb]);
+      f16x8 a = a_one;
+      if constexpr (PSAC) {
+        const uint32_t* src = half ? sOne : reinterpret_cast<const uint32_t*>(&sK[kbuf_][(kb * 32 + col) * ROWK + DQ]);
+        a = as_f16x8(*reinterpret_cast<const uint4*>(src));
+      }
+      sacc[kb] = mfma32h(a, qbias, sacc[kb]);
     }
   };
 
-  // S^T = K_hat Q^T of the K tile in buffer kb_, keys [0, 32) and [32, 64)
+  // S^T = c K_hat Q^T - m of the K tile in buffer kb_, keys [0, 32) and [32, 64)
   auto qk = [&](int kb_, f32x16 (&sacc)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -456,12 +475,11 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
         const f16x8 a = as_f16x8(*reinterpret_cast<const uint4*>(&sK[kb_][(kb * 32 + col) * ROWK + kc * 16 + half * 8]));
         sacc[kb] = mfma32h(a, qf[kc], sacc[kb]);
       }
-    if constexpr (PSAC) psac_qk(kb_, sacc);
+    bias_qk(kb_, sacc);
   };
 
-  // mask the keys past the end of the segment, raise the reference maximum when
-  // the tile exceeds it by more than 2^8 (rescaling the output accumulator)
-  auto softmax_prep = [&](f32x16 (&sacc)[2], int nvalid) {
+  // mask the keys past the end of the segment
+  auto mask_tail = [&](f32x16 (&sacc)[2], int nvalid) {
     if (nvalid < 64) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -470,25 +488,6 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
           const int key = kb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
           if (key >= nvalid) sacc[kb][v] = -INFINITY;
         }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-    // the other half of the row sits in lane l ^ 32
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2;
-    const bool raise = mx > m_run + 8.f;
-    if (__any(raise)) {
-      const float m_new = raise ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int b = 0; b < NDB; ++b)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[b][v] *= alpha;
     }
   };
 
@@ -576,19 +575,67 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
     }
     span_seek(cur_comp, t);
     const int nvalid_left = cur_comp.n_tokens - (t - cur_comp.tile_begin) * 64;
-    if constexpr (!SEQ) softmax_prep(cur, nvalid_left >= 64 ? 64 : nvalid_left);
+    if constexpr (!SEQ) mask_tail(cur, nvalid_left >= 64 ? 64 : nvalid_left);
 
-    // tile t's exponentials, one pair of scores at a time, as fp16 probabilities;
-    // the row sum is taken over the same rounded values
+    // tile t's exponentials (the scores are c*q.k - m already), one pair at a time,
+    // as fp16 probabilities; the row sum is taken over the same rounded values
     uint32_t pw[16];
     float psum = 0.f;
     const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
     auto exp_pair = [&](int k) {
       const int kb = k >> 3, v = 2 * (k & 7);
-      const float e0 = __builtin_amdgcn_exp2f(fmaf(cur[kb][v], p.scale_log2, -m_run));
-      const float e1 = __builtin_amdgcn_exp2f(fmaf(cur[kb][v + 1], p.scale_log2, -m_run));
+      const float e0 = __builtin_amdgcn_exp2f(cur[kb][v]);
+      const float e1 = __builtin_amdgcn_exp2f(cur[kb][v + 1]);
       pw[k] = pack_f16x2(e0, e1);
       psum = __builtin_amdgcn_fdot2(as_h2(pw[k]), ones, psum, false);
+    };
+    // The reference maximum is raised lazily: a tile whose probabilities (against
+    // the current m) sum to more than 2^8 in some row, and the first tile, take this
+    // branch, which moves m of every row to the tile's maximum where that lies above
+    // m (the first tile: always), shifts the scores of this tile and of the next
+    // (already formed with the old m), rescales the output accumulator and the sum,
+    // and recomputes the exponentials.  A row's probabilities are thus at most 2^8
+    // each, so fp16 holds them.
+    auto rescale = [&](bool first) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, cur[kb][v]);
+      // the other half of the row sits in lane l ^ 32
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const float target = m_run + (first ? (mx > -INFINITY ? mx : 0.f) : (mx > 0.f ? mx : 0.f));
+      const _Float16 m_hi = (_Float16)target;
+      const _Float16 m_lo = (_Float16)(target - (float)m_hi);
+      const float m_new = (float)m_hi + (float)m_lo;
+      const float delta = m_new - m_run;
+      if (!first) {
+        const float alpha = __builtin_amdgcn_exp2f(-delta);
+        l_run *= alpha;
+#pragma unroll
+        for (int b = 0; b < NDB; ++b)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[b][v] *= alpha;
+      }
+      m_run = m_new;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) cur[kb][v] -= delta;
+      if constexpr (!SEQ) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) nxt[kb][v] -= delta;
+      }
+      if (half) {
+        const h2 nm = {(_Float16)(-m_hi), (_Float16)(-m_lo)};
+        qbias = as_f16x8(make_uint4(as_u32(nm), 0u, 0u, 0u));
+      }
+      psum = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) exp_pair(k);
     };
     f16x8 pf[4];
 
@@ -602,7 +649,7 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
                        h2 vz) {
       if (j < CH / 2) {
         const h2 c = kq.pair(j);
-        kw[j] = round_add_f16x2(fmaf(float(c[0]), ks, kz), fmaf(float(c[1]), ks, kz), kcw[j]);
+        kw[j] = round_add_f16x2(fmaf(float(c[0]), ks, kz), fmaf(float(c[1]), ks, kz), kcw[j], c_sc);
         uint16_t* kdst = &sK[kstore][dk * ROWK + dg * CH];
         if constexpr (CH == 4) {
           if (j == 1) reinterpret_cast<uint2*>(kdst)[0] = make_uint2(kw[0], kw[1]);
@@ -633,7 +680,8 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
         else
           cur[i & 1] = mfma32h(fr[i & 3], qf[i >> 1], cur[i & 1]);
       }
-      softmax_prep(cur, nvalid_left >= 64 ? 64 : nvalid_left);
+      bias_qk(kbuf, cur);
+      mask_tail(cur, nvalid_left >= 64 ? 64 : nvalid_left);
 #pragma unroll
       for (int k = 0; k < 16; ++k) exp_pair(k);
     } else {
@@ -648,15 +696,16 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
         for (int u = 0; u < PPM; ++u) exp_pair(i * PPM + u);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (PSAC) psac_qk(kread, nxt);
+      bias_qk(kread, nxt);
     }
+    if (__any(!(psum <= 256.f)) || t == t_begin) rescale(t == t_begin);
     l_run += psum;
 #pragma unroll
     for (int c = 0; c < 4; ++c) pf[c] = as_f16x8(make_uint4(pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]));
 
     const CodePairs<KB, CH> kq(kc_r);
     const h2 kmh = as_h2(km_r);
-    const float ks = float(kmh[0]), kz = float(kmh[1]);
+    const float ks = float(kmh[0]) * c_sc, kz = float(kmh[1]) * c_sc;
     const CodePairs<VB, CH> vq(vc_r);
     const h2 vs = scale2(vm_r), vz = zero2(vm_r);
 #pragma unroll
