@@ -1,19 +1,30 @@
 // Nearest-centre assignment (QuantWM, section 4.1: each token goes to its nearest
 // centroid) and the k-means centre update (NanoKV, Table 4: two K-means iterations).
 //
-// bf16 tokens: the scores s_c = ||c||^2 - 2 x.c of a 32-centre by 32-token tile
-// come from v_mfma_f32_32x32x16_bf16 (products of bf16 values are exact in fp32;
-// the accumulator starts at ||c||^2 and the token fragment is pre-scaled by -2,
-// which is exact).  Each lane keeps the best score, its index and the second-best
-// score.  When the top-2 gap is not larger than a bound on the fp32 rounding error
-// of the scores, the token is re-scored exactly: fp64 sums of (x_i - c_i)^2 over
-// all centres, ties to the lowest index.  fp32 tokens always take that fp64 path.
+// bf16 tokens: the nearest centre maximises t_c = x.c - ||c||^2 / 2, which is
+// -1/2 times ||c||^2 - 2 x.c (||x - c||^2 less the token's own norm).  The scores
+// of a 32-centre by 32-token tile come from v_mfma_f32_32x32x16_bf16 (products of
+// bf16 values are exact in fp32; the accumulator starts at -||c||^2 / 2, an exact
+// halving, and the token fragment is the raw token, so every intermediate is
+// exactly -1/2 of the one for ||c||^2 - 2 x.c and so is its rounding error).  Each
+// lane keeps the best score, its index and the second-best score.  When the top-2
+// gap is not larger than a bound on the fp32 rounding error of the scores, the
+// token is re-scored exactly: fp64 sums of (x_i - c_i)^2 over all centres, ties to
+// the lowest index.  fp32 tokens always take that fp64 path.
 #include "kvc_internal.h"
 #include "dev_common.h"
 #include "mfma.h"
 
 namespace kvc {
 namespace {
+
+// acc + lo^2 + hi^2 for the two bf16 values of a word (v_dot2_f32_bf16: the
+// products are exact in fp32)
+__device__ __forceinline__ float sq2_bf16(uint32_t w, float acc) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const b2 v = __builtin_bit_cast(b2, w);
+  return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+}
 
 // Exact fp64 squared distance between a token row (global) and a centre row.
 template <typename T, int D>
@@ -69,10 +80,6 @@ __global__ __launch_bounds__(256) void assign_exact_kernel(const T* __restrict__
   if (lane == 0) ids[int64_t(h) * n + j] = static_cast<uint8_t>(bi);
 }
 
-__device__ __forceinline__ uint32_t scale_m2_bf16x2(uint32_t w) {
-  // multiply both bf16 halves by -2 (exact for finite values away from the range limits)
-  return pack_bf16x2(-2.f * bf16_lo(w), -2.f * bf16_hi(w));
-}
 
 template <int D>
 __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ cent,
@@ -114,10 +121,10 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
     }
   }
   __syncthreads();
-  // ||c||^2 in fp32, channels in order (one fused multiply-add each); padding rows
-  // score +inf
+  // -||c||^2 / 2 with ||c||^2 in fp32, channel pairs in order (v_dot2_f32_bf16);
+  // padding rows score -inf
   {
-    float sn = INFINITY;
+    float sn = -INFINITY;
     if (tid < C) {
       sn = 0.f;
 #pragma unroll
@@ -126,21 +133,21 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
         const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          sn = fmaf(bf16_lo(ww[i]), bf16_lo(ww[i]), sn);
-          sn = fmaf(bf16_hi(ww[i]), bf16_hi(ww[i]), sn);
+          sn = sq2_bf16(ww[i], sn);
         }
       }
+      sn *= -0.5f;
     }
     if (tid < rows) sN[tid] = sn;
   }
   __syncthreads();
-  float cmax = 0.f;
-  for (int c = lane; c < C; c += 64) cmax = fmaxf(cmax, sN[c]);
+  float cmax = 0.f;                    // max ||c||^2
+  for (int c = lane; c < C; c += 64) cmax = fmaxf(cmax, -2.f * sN[c]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, off, 64));
 
   for (int round = 0; round < kAssignRounds; ++round) {
-  // token fragments (B operand), pre-scaled by -2, and ||x||^2
+  // token fragments (B operand) and ||x||^2
   const int64_t tok0 = (int64_t(blockIdx.x) * kAssignRounds + round) * 256 + wave * 64;
   if (tok0 >= n) break;                // wave-uniform; no barrier follows
   bf16x8 xb[2][KC];
@@ -157,16 +164,16 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        s = fmaf(bf16_lo(ww[i]), bf16_lo(ww[i]), s);
-        s = fmaf(bf16_hi(ww[i]), bf16_hi(ww[i]), s);
+        s = sq2_bf16(ww[i], s);
       }
-      xb[cb][kc] = as_bf16x8(make_uint4(scale_m2_bf16x2(w.x), scale_m2_bf16x2(w.y), scale_m2_bf16x2(w.z),
-                                        scale_m2_bf16x2(w.w)));
+      xb[cb][kc] = as_bf16x8(w);
     }
     xx[cb] = s + __shfl_xor(s, 32, 64);
   }
 
-  float b1[2] = {INFINITY, INFINITY}, b2[2] = {INFINITY, INFINITY};
+  // best and second-best score per token; the index of the best is kept without
+  // this lane's row offset 4*half (a wave-uniform code, added after the scan)
+  float b1[2] = {-INFINITY, -INFINITY}, b2[2] = {-INFINITY, -INFINITY};
   int i1[2] = {0, 0};
   for (int blk = 0; blk < nblk; ++blk) {
     f32x16 nc;
@@ -182,40 +189,45 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
       acc0 = mfma32(a, xb[0][kc], acc0);
       acc1 = mfma32(a, xb[1][kc], acc1);
     }
+    // strictly greater: on equal scores the earlier (lower) centre stays; the
+    // second best is the median of (best, second, new)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int cidx = blk * 32 + 8 * (v / 4) + 4 * half + (v % 4);
+      const int code = blk * 32 + 8 * (v / 4) + (v % 4);
       {
-        const float s = acc0[v];
-        const bool lt = s < b1[0];
-        b2[0] = fminf(b2[0], fmaxf(b1[0], s));
-        b1[0] = lt ? s : b1[0];
-        i1[0] = lt ? cidx : i1[0];
+        const float sc = acc0[v];
+        const bool gt = sc > b1[0];
+        b2[0] = __builtin_amdgcn_fmed3f(b1[0], b2[0], sc);
+        b1[0] = gt ? sc : b1[0];
+        i1[0] = gt ? code : i1[0];
       }
       {
-        const float s = acc1[v];
-        const bool lt = s < b1[1];
-        b2[1] = fminf(b2[1], fmaxf(b1[1], s));
-        b1[1] = lt ? s : b1[1];
-        i1[1] = lt ? cidx : i1[1];
+        const float sc = acc1[v];
+        const bool gt = sc > b1[1];
+        b2[1] = __builtin_amdgcn_fmed3f(b1[1], b2[1], sc);
+        b1[1] = gt ? sc : b1[1];
+        i1[1] = gt ? code : i1[1];
       }
     }
   }
+  i1[0] += 4 * half;
+  i1[1] += 4 * half;
 
-  const float err_scale = float(4 * D + 8) * 5.9604645e-08f;  // (4D + 8) * 2^-24
+  // bound on the rounding error of ||c||^2 - 2 x.c, halved for the scores used here
+  const float err_scale = float(4 * D + 8) * 5.9604645e-08f * 0.5f;  // (4D + 8) * 2^-24 / 2
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const float ob1 = __shfl_xor(b1[cb], 32, 64);
     const float ob2 = __shfl_xor(b2[cb], 32, 64);
     const int oi1 = __shfl_xor(i1[cb], 32, 64);
-    const float nb2 = fminf(fmaxf(b1[cb], ob1), fminf(b2[cb], ob2));
-    const bool other = ob1 < b1[cb] || (ob1 == b1[cb] && oi1 < i1[cb]);
+    const float nb2 = fmaxf(fminf(b1[cb], ob1), fmaxf(b2[cb], ob2));
+    const bool other = ob1 > b1[cb] || (ob1 == b1[cb] && oi1 < i1[cb]);
     const float nb1 = other ? ob1 : b1[cb];
     int id = other ? oi1 : i1[cb];
     const int64_t tok = tok0 + cb * 32 + col;
     const bool valid = tok < n;
     const float thr = err_scale * (xx[cb] + 2.f * cmax);
-    const bool flag = valid && half == 0 && !(nb2 - nb1 > thr);  // also catches NaN
+    const bool flag = valid && half == 0 && !(nb1 - nb2 > thr);  // also catches NaN
     uint64_t mask = __ballot(flag);
     if (mask) {
       // The true nearest centre of a flagged token is among the centres whose
@@ -223,7 +235,7 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
       // by scoring this token half once more, then re-scored exactly (fp64,
       // dimensions spread over the lanes, a fixed reduction order), ties to the
       // lowest index.
-      const float lim = nb1 + thr;
+      const float lim = nb1 - thr;
       uint32_t cm[8];                 // candidate bits of block blk: 16 per lane
 #pragma unroll
       for (int blk = 0; blk < 8; ++blk) cm[blk] = 0;
@@ -241,7 +253,7 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
         }
         uint32_t bits = 0;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) bits |= (acc[v] <= lim ? 1u : 0u) << v;
+        for (int v = 0; v < 16; ++v) bits |= (acc[v] >= lim ? 1u : 0u) << v;
 #pragma unroll
         for (int q = 0; q < 8; ++q)
           if (q == blk) cm[q] = bits;
