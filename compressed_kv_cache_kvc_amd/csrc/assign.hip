@@ -88,6 +88,7 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
   constexpr int KC = D / 16;
   __shared__ __attribute__((aligned(16))) uint16_t sC[256 * ROWP];
   __shared__ __attribute__((aligned(16))) float sN[256];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[4][D];   // a flagged token's row, per wavefront
 
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
@@ -213,8 +214,13 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
   i1[0] += 4 * half;
   i1[1] += 4 * half;
 
-  // bound on the rounding error of ||c||^2 - 2 x.c, halved for the scores used here
-  const float err_scale = float(4 * D + 8) * 5.9604645e-08f * 0.5f;  // (4D + 8) * 2^-24 / 2
+  // Bound on the difference of the rounding errors of two scores.  A score sums
+  // D exact products and -n_c/2 in fp32 (in any order: at most D roundings), and
+  // n_c = ||c||^2 itself comes from at most D roundings, so
+  // |err(t_c)| <= g (n_c + ||x|| sqrt(n_c)) with g = D 2^-24 (1 + 2^-16), using
+  // |x.c| <= ||x|| ||c||; a gap of two scores is then off by at most
+  // 2 g (cmax + ||x|| sqrt(cmax)), below (2D + 4) 2^-24 (cmax + ||x|| sqrt(cmax)).
+  const float err_scale = float(2 * D + 4) * 5.9604645e-08f;   // (2D + 4) * 2^-24
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const float ob1 = __shfl_xor(b1[cb], 32, 64);
@@ -226,7 +232,7 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
     int id = other ? oi1 : i1[cb];
     const int64_t tok = tok0 + cb * 32 + col;
     const bool valid = tok < n;
-    const float thr = err_scale * (xx[cb] + 2.f * cmax);
+    const float thr = err_scale * (cmax + sqrtf(xx[cb] * cmax));
     const bool flag = valid && half == 0 && !(nb1 - nb2 > thr);  // also catches NaN
     uint64_t mask = __ballot(flag);
     if (mask) {
@@ -239,24 +245,35 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
       uint32_t cm[8];                 // candidate bits of block blk: 16 per lane
 #pragma unroll
       for (int blk = 0; blk < 8; ++blk) cm[blk] = 0;
-      for (int blk = 0; blk < nblk; ++blk) {
-        f32x16 acc;
+      // two blocks at a time (two independent accumulation chains); the second of
+      // a pair past the last block reads rows of the 256-row table that are never
+      // used and is discarded
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const float4 t = *reinterpret_cast<const float4*>(&sN[blk * 32 + 8 * g4 + 4 * half]);
-          acc[4 * g4 + 0] = t.x; acc[4 * g4 + 1] = t.y; acc[4 * g4 + 2] = t.z; acc[4 * g4 + 3] = t.w;
+      for (int bp = 0; bp < 4; ++bp) {
+        if (2 * bp >= nblk) break;
+        f32x16 acc[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const float4 t = *reinterpret_cast<const float4*>(&sN[(2 * bp + u) * 32 + 8 * g4 + 4 * half]);
+            acc[u][4 * g4 + 0] = t.x; acc[u][4 * g4 + 1] = t.y; acc[u][4 * g4 + 2] = t.z; acc[u][4 * g4 + 3] = t.w;
+          }
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const bf16x8 a = as_bf16x8(
+                *reinterpret_cast<const uint4*>(&sC[((2 * bp + u) * 32 + col) * ROWP + kc * 16 + half * 8]));
+            acc[u] = mfma32(a, xb[cb][kc], acc[u]);
+          }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          uint32_t bits = 0;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) bits |= (acc[u][v] >= lim ? 1u : 0u) << v;
+          if (2 * bp + u < nblk) cm[2 * bp + u] = bits;
         }
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&sC[(blk * 32 + col) * ROWP + kc * 16 + half * 8]));
-          acc = mfma32(a, xb[cb][kc], acc);
-        }
-        uint32_t bits = 0;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) bits |= (acc[v] >= lim ? 1u : 0u) << v;
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (q == blk) cm[q] = bits;
       }
       constexpr int PERL = D / 64;    // dimensions per lane in the exact re-scoring
       while (mask) {
@@ -264,20 +281,24 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
         mask &= mask - 1;
         const int64_t t = tok0 + cb * 32 + b;
         const bf16_t* xr = x + (int64_t(h) * n + t) * D;
+        // the token's row from the two lanes that hold it (fragments of 8
+        // dimensions), through this wavefront's LDS row (LDS operations of one
+        // wavefront complete in order)
+        if (col == b) {
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc)
+            *reinterpret_cast<uint4*>(&sX[wave][kc * 16 + half * 8]) = as_uint4(xb[cb][kc]);
+        }
         double xd[PERL];
 #pragma unroll
-        for (int i = 0; i < PERL; ++i)
-          xd[i] = double(__uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(xr)[lane * PERL + i]) << 16));
+        for (int i = 0; i < PERL; ++i) xd[i] = double(__uint_as_float(uint32_t(sX[wave][lane * PERL + i]) << 16));
         double best = INFINITY;
         int bi = 0x7fffffff;
-        for (int blk = 0; blk < nblk; ++blk) {
-          uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-          for (int q = 0; q < 8; ++q)
-            if (q == blk) {
-              w0 = __builtin_amdgcn_readlane(cm[q], b);
-              w1 = __builtin_amdgcn_readlane(cm[q], b + 32);
-            }
+        for (int blk = 0; blk < 8; ++blk) {
+          if (blk >= nblk) break;
+          const uint32_t w0 = __builtin_amdgcn_readlane(cm[blk], b);
+          const uint32_t w1 = __builtin_amdgcn_readlane(cm[blk], b + 32);
           uint32_t both = w0 | (w1 << 16);   // bit v: row 8*(v/4) + v%4 (+4 for the high half)
           while (both) {
             const int bit = __builtin_ctz(both);
