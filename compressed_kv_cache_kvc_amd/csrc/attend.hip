@@ -478,16 +478,16 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
     bias_qk(kb_, sacc);
   };
 
-  // mask the keys past the end of the segment
+  // mask the keys past the end of the segment: this lane's rows are 4*half +
+  // (its register rows), tested against a wave-uniform mask of the valid keys
   auto mask_tail = [&](f32x16 (&sacc)[2], int nvalid) {
     if (nvalid < 64) {
+      const uint64_t mine = ((uint64_t(1) << nvalid) - 1) >> (4 * half);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = kb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
-          if (key >= nvalid) sacc[kb][v] = -INFINITY;
-        }
+        for (int v = 0; v < 16; ++v)
+          if (!((mine >> (kb * 32 + 8 * (v / 4) + (v % 4))) & 1)) sacc[kb][v] = -INFINITY;
     }
   };
 
@@ -562,10 +562,13 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
       const uint2 lo = lds_read_tr16(base), hi = lds_read_tr16(base + 8 * ROWV);
       return as_f16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
     };
-    f16x8 fr[4];
-    fr[0] = frag(0);
-    fr[1] = frag(1);
-    fr[2] = frag(2);
+    // operand reads run FA products ahead of their use (a ring of FA + 1
+    // fragments); with logit compensation two, which leaves the registers for
+    // the token's kept coefficients
+    constexpr int FA = PSAC ? 2 : 3, FR = FA + 1;
+    f16x8 fr[FR];
+#pragma unroll
+    for (int f = 0; f < FA; ++f) fr[f] = frag(f);
     {
       const int t3 = clamp_t(t + 3), t4 = clamp_t(t + 4);
       data_seek(cur_data, t3);
@@ -674,11 +677,11 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
       // tile t's scores, then its softmax and exponentials
 #pragma unroll
       for (int i = 0; i < NQK; ++i) {
-        fr[(i + 3) & 3] = frag(i + 3);
+        fr[(i + FA) % FR] = frag(i + FA);
         if (i < 2)
-          cur[i] = mfma32h(fr[i & 3], qf[0], f32x16{});
+          cur[i] = mfma32h(fr[i % FR], qf[0], f32x16{});
         else
-          cur[i & 1] = mfma32h(fr[i & 3], qf[i >> 1], cur[i & 1]);
+          cur[i & 1] = mfma32h(fr[i % FR], qf[i >> 1], cur[i & 1]);
       }
       bias_qk(kbuf, cur);
       mask_tail(cur, nvalid_left >= 64 ? 64 : nvalid_left);
@@ -687,11 +690,11 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
     } else {
 #pragma unroll
       for (int i = 0; i < NQK; ++i) {
-        fr[(i + 3) & 3] = frag(i + 3);
+        fr[(i + FA) % FR] = frag(i + FA);
         if (i < 2)
-          nxt[i] = mfma32h(fr[i & 3], qf[0], f32x16{});
+          nxt[i] = mfma32h(fr[i % FR], qf[0], f32x16{});
         else
-          nxt[i & 1] = mfma32h(fr[i & 3], qf[i >> 1], nxt[i & 1]);
+          nxt[i & 1] = mfma32h(fr[i % FR], qf[i >> 1], nxt[i & 1]);
 #pragma unroll
         for (int u = 0; u < PPM; ++u) exp_pair(i * PPM + u);
         __builtin_amdgcn_sched_barrier(0);
@@ -710,8 +713,8 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
     const h2 vs = scale2(vm_r), vz = zero2(vm_r);
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
-      if (NQK + i + 3 < NQK + NPV) fr[(NQK + i + 3) & 3] = frag(NQK + i + 3);
-      o[i % NDB] = mfma32h(fr[(NQK + i) & 3], pf[i / NDB], o[i % NDB]);
+      if (NQK + i + FA < NQK + NPV) fr[(NQK + i + FA) % FR] = frag(NQK + i + FA);
+      o[i % NDB] = mfma32h(fr[(NQK + i) % FR], pf[i / NDB], o[i % NDB]);
 #pragma unroll
       for (int u = 0; u < IPM; ++u) dq_item(i * IPM + u, kq, ks, kz, vq, vs, vz);
       __builtin_amdgcn_sched_barrier(0);
