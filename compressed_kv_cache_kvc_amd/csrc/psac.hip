@@ -65,28 +65,43 @@ __global__ __launch_bounds__(256) void query_moments_kernel(const T* __restrict_
   }
 }
 
-// bf16 queries: the 32 x 32 tile (bi, bj) of sum_i q_i q_i^T on the matrix cores,
-// one wavefront per tile: A = Q^T rows (channels 32*bi ..), B = Q columns
-// (channels 32*bj ..), the contraction over 16 queries per
-// v_mfma_f32_32x32x16_bf16 (products of bf16 values are exact in fp32).  The
-// queries pass through LDS 64 at a time (zero rows past the end).
+// bf16 queries: the 32 x 32 tile (bi, bj) of sum_i q_i q_i^T on the matrix cores:
+// A = Q^T rows (channels 32*bi ..), B = Q columns (channels 32*bj ..), the
+// contraction over 16 queries per v_mfma_f32_32x32x16_bf16 (products of bf16
+// values are exact in fp32).  Eight wavefronts per tile, each walking its own
+// blocks of 64 queries (block w, w + 8, ...) through its own LDS rows (32
+// channels, 64 B, so the transposing reads of 4 rows hit distinct banks) with no
+// barrier in the loop; the operands come from ds_read_b64_tr_b16, A and B in the
+// same query order.  The eight partial tiles are added in wavefront order.
+typedef short mom_s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) mom_s16x4 mom_lds_s16x4;
+__device__ __forceinline__ uint2 mom_read_tr16(const uint16_t* p) {
+  const mom_s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((mom_lds_s16x4*)(const_cast<uint16_t*>(p)));
+  return __builtin_bit_cast(uint2, v);
+}
+
 template <int D>
-__global__ __launch_bounds__(64) void query_moments_mfma_kernel(const bf16_t* __restrict__ q, int64_t n_q,
-                                                                int64_t n_prev, float* __restrict__ m) {
+__global__ __launch_bounds__(512) void query_moments_mfma_kernel(const bf16_t* __restrict__ q, int64_t n_q,
+                                                                 int64_t n_prev, float* __restrict__ m) {
   constexpr int NT = D / 32;
-  constexpr int ROW = 40;                      // 32 channels + padding, 16-byte aligned rows
-  __shared__ __attribute__((aligned(16))) uint16_t sa[64 * ROW], sb[64 * ROW];
+  constexpr int W = 8;                         // wavefronts per tile
+  __shared__ __attribute__((aligned(16))) uint16_t sa[W][64 * 32], sb[W][64 * 32];
+  __shared__ float red[W][16][64];             // partial tiles, [wave][v][lane]
   const int h = blockIdx.y;
   const int bi = blockIdx.x / NT, bj = blockIdx.x % NT;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint16_t* qh = reinterpret_cast<const uint16_t*>(q) + int64_t(h) * n_q * D;
   f32x16 acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-  for (int64_t i0 = 0; i0 < n_q; i0 += 64) {
-    __syncthreads();
+  // transposing reads: lane s supplies query row 4*(s >> 5) + ((s >> 2) & 3) (+8
+  // for the second read, +16*kk per product) and channels 16*((s >> 4) & 1) +
+  // 4*(s & 3) .. +3; lane l receives channel l % 32 of its 4 queries
+  const int trow = 4 * (lane >> 5) + ((lane >> 2) & 3);
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  for (int64_t i0 = int64_t(w) * 64; i0 < n_q; i0 += W * 64) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {              // 64 rows x 4 chunks of 8 channels, per slice
+    for (int k = 0; k < 4; ++k) {              // 64 rows x 4 chunks of 8 channels
       const int e = lane + 64 * k;
       const int r = e / 4, c8 = (e % 4) * 8;
       uint4 wa = make_uint4(0, 0, 0, 0), wb = make_uint4(0, 0, 0, 0);
@@ -94,30 +109,33 @@ __global__ __launch_bounds__(64) void query_moments_mfma_kernel(const bf16_t* __
         wa = *reinterpret_cast<const uint4*>(qh + (i0 + r) * D + bi * 32 + c8);
         wb = *reinterpret_cast<const uint4*>(qh + (i0 + r) * D + bj * 32 + c8);
       }
-      *reinterpret_cast<uint4*>(&sa[r * ROW + c8]) = wa;
-      *reinterpret_cast<uint4*>(&sb[r * ROW + c8]) = wb;
+      *reinterpret_cast<uint4*>(&sa[w][r * 32 + c8]) = wa;
+      *reinterpret_cast<uint4*>(&sb[w][r * 32 + c8]) = wb;
     }
-    __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {           // 16 queries per product
-      uint32_t a[4], b[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r0 = kk * 16 + 8 * (lane / 32) + 2 * e;
-        a[e] = uint32_t(sa[r0 * ROW + lane % 32]) | (uint32_t(sa[(r0 + 1) * ROW + lane % 32]) << 16);
-        b[e] = uint32_t(sb[r0 * ROW + lane % 32]) | (uint32_t(sb[(r0 + 1) * ROW + lane % 32]) << 16);
-      }
-      acc = mfma32(as_bf16x8(make_uint4(a[0], a[1], a[2], a[3])), as_bf16x8(make_uint4(b[0], b[1], b[2], b[3])), acc);
+      const uint16_t* pa = &sa[w][(kk * 16 + trow) * 32 + tcol];
+      const uint16_t* pb = &sb[w][(kk * 16 + trow) * 32 + tcol];
+      const uint2 alo = mom_read_tr16(pa), ahi = mom_read_tr16(pa + 8 * 32);
+      const uint2 blo = mom_read_tr16(pb), bhi = mom_read_tr16(pb + 8 * 32);
+      acc = mfma32(as_bf16x8(make_uint4(alo.x, alo.y, ahi.x, ahi.y)),
+                   as_bf16x8(make_uint4(blo.x, blo.y, bhi.x, bhi.y)), acc);
     }
   }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) red[w][v][lane] = acc[v];
+  __syncthreads();
+  if (w != 0) return;
   // lane: column j = lane % 32, rows i = 8*(v/4) + 4*(lane/32) + v%4
   float* mh = m + int64_t(h) * D * D;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
+    double tot = 0.0;
+#pragma unroll
+    for (int u = 0; u < W; ++u) tot += double(red[u][v][lane]);
     const int i = bi * 32 + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
     const int j = bj * 32 + lane % 32;
     float* dst = mh + int64_t(i) * D + j;
-    double tot = double(acc[v]);
     if (n_prev > 0) tot += double(*dst) * double(n_prev);
     *dst = float(tot / double(n_prev + n_q));
   }
@@ -341,10 +359,10 @@ hipError_t launch_query_moments(int heads, int64_t n_q, int dim, kvc_dtype dt, c
   hipLaunchKernelGGL((query_moments_kernel<T, D>), grid, dim3(256), 0, st, static_cast<const T*>(q), n_q, n_prev, m)
   if (dt == KVC_BF16) {
     if (dim == 128)
-      hipLaunchKernelGGL((query_moments_mfma_kernel<128>), grid, dim3(64), 0, st, static_cast<const bf16_t*>(q), n_q,
+      hipLaunchKernelGGL((query_moments_mfma_kernel<128>), grid, dim3(512), 0, st, static_cast<const bf16_t*>(q), n_q,
                          n_prev, m);
     else
-      hipLaunchKernelGGL((query_moments_mfma_kernel<64>), grid, dim3(64), 0, st, static_cast<const bf16_t*>(q), n_q,
+      hipLaunchKernelGGL((query_moments_mfma_kernel<64>), grid, dim3(512), 0, st, static_cast<const bf16_t*>(q), n_q,
                          n_prev, m);
   } else {
     if (dim == 128) KVC_MOM(float, 128); else KVC_MOM(float, 64);
