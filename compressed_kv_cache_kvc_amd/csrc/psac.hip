@@ -142,35 +142,45 @@ __global__ __launch_bounds__(512) void query_moments_mfma_kernel(const bf16_t* _
 }
 
 // Eigen-decomposition of the symmetric R x R matrix a (row-major, overwritten)
-// by cyclic Jacobi rotations; eigenvectors in the columns of v.  One thread.
+// by cyclic Jacobi rotations; eigenvectors in the columns of v.  One thread; the
+// index loops are unrolled so that a and v stay in registers.
 template <int R>
 __device__ void jacobi_eig(float (&a)[R][R], float (&v)[R][R]) {
+#pragma unroll
   for (int i = 0; i < R; ++i)
+#pragma unroll
     for (int j = 0; j < R; ++j) v[i][j] = i == j ? 1.f : 0.f;
   for (int sweep = 0; sweep < 30; ++sweep) {
     float off = 0.f, diag = 0.f;
+#pragma unroll
     for (int i = 0; i < R; ++i) {
       diag += a[i][i] * a[i][i];
+#pragma unroll
       for (int j = i + 1; j < R; ++j) off += a[i][j] * a[i][j];
     }
     if (off <= 1e-14f * diag) break;          // off-diagonal at fp32 rounding level
+#pragma unroll
     for (int p = 0; p < R; ++p)
+#pragma unroll
       for (int qq = p + 1; qq < R; ++qq) {
         if (a[p][qq] == 0.f) continue;
         // rotation that zeroes a[p][qq] (the standard symmetric Schur step)
         const float theta = 0.5f * (a[qq][qq] - a[p][p]) / a[p][qq];
         const float tt = (theta >= 0.f ? 1.f : -1.f) / (fabsf(theta) + sqrtf(theta * theta + 1.f));
         const float c = 1.f / sqrtf(tt * tt + 1.f), s = tt * c;
+#pragma unroll
         for (int k = 0; k < R; ++k) {
           const float akp = a[k][p], akq = a[k][qq];
           a[k][p] = c * akp - s * akq;
           a[k][qq] = s * akp + c * akq;
         }
+#pragma unroll
         for (int k = 0; k < R; ++k) {
           const float apk = a[p][k], aqk = a[qq][k];
           a[p][k] = c * apk - s * aqk;
           a[qq][k] = s * apk + c * aqk;
         }
+#pragma unroll
         for (int k = 0; k < R; ++k) {
           const float vkp = v[k][p], vkq = v[k][qq];
           v[k][p] = c * vkp - s * vkq;
@@ -178,6 +188,26 @@ __device__ void jacobi_eig(float (&a)[R][R], float (&v)[R][R]) {
         }
       }
   }
+}
+
+// Sum of a float over the 64 lanes, the same in every lane, in a fixed order:
+// neighbours (DPP quad permutations), the other half of each group of 8 and of
+// each row of 16 (DPP mirrors), then across rows and halves (permlane swaps).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += dpp_f32<0xB1>(v);     // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(v);     // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141>(v);    // row_half_mirror
+  v += dpp_f32<0x140>(v);    // row_mirror
+  {
+    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
 // Top-R eigenvectors of one head's M by subspace iteration: V <- orth(M V),
@@ -190,24 +220,41 @@ __global__ __launch_bounds__(256) void psac_basis_kernel(const float* __restrict
                                                          const float* __restrict__ u_prev, float* __restrict__ u,
                                                          float* __restrict__ lam) {
   __shared__ float sm[D][D + 1];
-  __shared__ float sv[D][R], sw[D][R];
+  __shared__ __attribute__((aligned(16))) float sv[D][R], sw[D][R];
   __shared__ float st[R][R];
   const int h = blockIdx.x;
   const int t = threadIdx.x;
   const float* mh = m + int64_t(h) * D * D;
-  for (int e = t; e < D * D; e += 256) sm[e / D][e % D] = mh[e];
+  {                                           // M into LDS: all loads issued first
+    constexpr int PER = D * D / 4 / 256;
+    float4 w[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) w[k] = reinterpret_cast<const float4*>(mh)[t + 256 * k];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = 4 * (t + 256 * k);
+      sm[e / D][e % D] = w[k].x; sm[e / D][e % D + 1] = w[k].y;
+      sm[e / D][e % D + 2] = w[k].z; sm[e / D][e % D + 3] = w[k].w;
+    }
+  }
   for (int e = t; e < D * R; e += 256) {
     const int i = e / R, k = e % R;
     sv[i][k] = u_prev ? u_prev[int64_t(h) * D * R + e]
                       : __sinf(0.37f * float(i + 1) * float(k + 1) + 0.11f * float(k)) + (i == k ? 1.f : 0.f);
   }
   __syncthreads();
-  auto multiply = [&]() {                     // sw = M sv
-    for (int e = t; e < D * R; e += 256) {
-      const int i = e / R, k = e % R;
-      float acc = 0.f;
-      for (int j = 0; j < D; ++j) acc = fmaf(sm[i][j], sv[j][k], acc);
-      sw[i][k] = acc;
+  auto multiply = [&]() {                     // sw = M sv: a thread per (row, 4 columns)
+    static_assert(R == 8 && D * 2 <= 256, "two threads per row");
+    if (t < 2 * D) {
+      const int i = t >> 1, k0 = (t & 1) * 4;
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+      for (int j = 0; j < D; ++j) {
+        const float mij = sm[i][j];
+        const float4 vj = *reinterpret_cast<const float4*>(&sv[j][k0]);
+        a0 = fmaf(mij, vj.x, a0); a1 = fmaf(mij, vj.y, a1);
+        a2 = fmaf(mij, vj.z, a2); a3 = fmaf(mij, vj.w, a3);
+      }
+      *reinterpret_cast<float4*>(&sw[i][k0]) = make_float4(a0, a1, a2, a3);
     }
     __syncthreads();
   };
@@ -217,12 +264,12 @@ __global__ __launch_bounds__(256) void psac_basis_kernel(const float* __restrict
         for (int j = 0; j < k; ++j) {
           float d = 0.f;
           for (int i = t; i < D; i += 64) d += sv[i][j] * sw[i][k];
-          for (int o = 32; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
+          d = wave_sum_f32(d);
           for (int i = t; i < D; i += 64) sw[i][k] -= d * sv[i][j];
         }
         float nn = 0.f;
         for (int i = t; i < D; i += 64) nn += sw[i][k] * sw[i][k];
-        for (int o = 32; o >= 1; o >>= 1) nn += __shfl_xor(nn, o, 64);
+        nn = wave_sum_f32(nn);
         const float inv = nn > 0.f ? 1.f / sqrtf(nn) : 0.f;
         for (int i = t; i < D; i += 64) sv[i][k] = sw[i][k] * inv;
       }
@@ -246,23 +293,30 @@ __global__ __launch_bounds__(256) void psac_basis_kernel(const float* __restrict
     st[a][b] = acc;
   }
   __syncthreads();
-  __shared__ float sy[R][R];
-  __shared__ int sorder[R];
-  if (t == 0) {
+  __shared__ float sy[R][R], sy0[R][R], sdiag[R];
+  if (t == 0) {                                // static indices only: a and y stay in registers
     float a[R][R], y[R][R];
+#pragma unroll
     for (int i = 0; i < R; ++i)
+#pragma unroll
       for (int j = 0; j < R; ++j) a[i][j] = 0.5f * (st[i][j] + st[j][i]);
     jacobi_eig<R>(a, y);
-    int order[R];
-    for (int i = 0; i < R; ++i) order[i] = i;
-    for (int i = 0; i < R; ++i)                       // by eigenvalue, largest first
-      for (int j = i + 1; j < R; ++j)
-        if (a[order[j]][order[j]] > a[order[i]][order[i]]) { const int x = order[i]; order[i] = order[j]; order[j] = x; }
+#pragma unroll
     for (int i = 0; i < R; ++i) {
-      sorder[i] = order[i];
-      lam[int64_t(h) * R + i] = a[order[i]][order[i]];
-      for (int j = 0; j < R; ++j) sy[j][i] = y[j][order[i]];
+      sdiag[i] = a[i][i];
+#pragma unroll
+      for (int j = 0; j < R; ++j) sy0[j][i] = y[j][i];
     }
+  }
+  __syncthreads();
+  if (t < R) {                                 // by eigenvalue, largest first (ties: lower index first)
+    const float ev = sdiag[t];
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < R; ++j) rank += (sdiag[j] > ev || (sdiag[j] == ev && j < t)) ? 1 : 0;
+    lam[int64_t(h) * R + rank] = ev;
+#pragma unroll
+    for (int j = 0; j < R; ++j) sy[j][rank] = sy0[j][t];
   }
   __syncthreads();
   for (int e = t; e < D * R; e += 256) {       // U = V Y
