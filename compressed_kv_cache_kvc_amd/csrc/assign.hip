@@ -360,111 +360,38 @@ __device__ __forceinline__ uint32_t f64_to_bits_rne(double d) {
   return (sign << SIGN_SHIFT) | bits;
 }
 
-// Member lists of the centres, in token order.  The ids of a head are taken in
-// chunks of kListChunk tokens, one workgroup of 256 threads per (chunk, head):
-// thread t counts, per centre, the ids of its kListChunk/256 consecutive tokens
-// (16-bit counts, [centre][thread] in LDS); an exclusive scan over (centre,
-// thread) in that order gives each thread its first slot per centre, and a second
-// pass over the same tokens writes their offsets inside the chunk.  Centre c's
-// members of chunk k are then list[k*kListChunk + off[k][c] ... off[k][c+1]), in
-// increasing token order (a stable counting sort).
-__global__ __launch_bounds__(256) void member_lists_kernel(const uint8_t* __restrict__ ids, int64_t n, int C,
-                                                           uint32_t* __restrict__ off, uint16_t* __restrict__ list) {
-  __shared__ __attribute__((aligned(16))) uint16_t cnt[256 * 256];   // [centre][thread]
-  __shared__ __attribute__((aligned(16))) uint8_t sid[kListChunk];     // the chunk's ids
-  __shared__ uint32_t base[257];
-  const int t = threadIdx.x;
-  const int k = blockIdx.x;
-  const int h = blockIdx.y;
-  const int64_t nk = (n + kListChunk - 1) / kListChunk;
-  const int64_t c0 = int64_t(k) * kListChunk;
-  const int len = int(n - c0 < kListChunk ? n - c0 : kListChunk);
-  const int L = (len + 255) / 256;
-  const int j0 = t * L < len ? t * L : len;
-  const int j1 = j0 + L < len ? j0 + L : len;
-  const uint8_t* idk = ids + int64_t(h) * n + c0;
-  for (int i = t; i < 256 * 256 / 8; i += 256) reinterpret_cast<uint4*>(cnt)[i] = make_uint4(0, 0, 0, 0);
-  for (int i = t; i < len; i += 256) sid[i] = idk[i];      // coalesced
-  __syncthreads();
-  for (int j = j0; j < j1; ++j) ++cnt[int(sid[j]) * 256 + t];
-  __syncthreads();
-  // row c: exclusive prefix over the threads, row total to base[c]
-  if (t < C) {
-    uint32_t run = 0;
-    uint4* row = reinterpret_cast<uint4*>(&cnt[t * 256]);
-    for (int i = 0; i < 32; ++i) {
-      uint4 w = row[i];
-      uint32_t* pw = reinterpret_cast<uint32_t*>(&w);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = pw[q] & 0xffffu, hi = pw[q] >> 16;
-        pw[q] = run | ((run + lo) << 16);
-        run += lo + hi;
-      }
-      row[i] = w;
-    }
-    base[t] = run;
-  }
-  __syncthreads();
-  // exclusive scan of the row totals: inclusive scan inside each wavefront, then
-  // the wavefront totals added in order
-  {
-    const int lane = t & 63, w = t >> 6;
-    const uint32_t v = t < C ? base[t] : 0u;
-    uint32_t inc = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t u = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += u;
-    }
-    __shared__ uint32_t wsum[4];
-    if (lane == 63) wsum[w] = inc;
-    __syncthreads();
-    uint32_t add = 0;
-    for (int i = 0; i < w; ++i) add += wsum[i];
-    if (t < C) base[t] = add + inc - v;
-    if (t == 255) base[C] = add + inc;
-  }
-  __syncthreads();
-  uint32_t* offk = off + (int64_t(h) * nk + k) * (C + 1);
-  for (int c = t; c <= C; c += 256) offk[c] = base[c];
-  uint16_t* lk = list + int64_t(h) * n + c0;
-  for (int j = j0; j < j1; ++j) {
-    const int c = sid[j];
-    const uint32_t slot = base[c] + cnt[c * 256 + t]++;
-    lk[slot] = static_cast<uint16_t>(j);
-  }
-}
-
 // One wavefront per (head, centre): the members' rows are added in fp64 in token
-// order (chunk by chunk, each member list in increasing order), BATCH row loads
-// in flight at a time.  The order of the additions is fixed, so the result is
-// deterministic; the centre becomes the mean (one fp64 division) rounded to
-// nearest even in the storage type, and a centre without members keeps its value.
+// order.  The head's ids pass through LDS in chunks of kScanChunk tokens, shared
+// by the workgroup's four wavefronts; each wavefront finds its centre's members 64
+// ids at a time (a ballot; slots in token order by mbcnt), lists up to 64 of them
+// in LDS and then adds their rows in that order with BATCH row loads in flight.
+// The order of the additions is fixed, so the result is deterministic; the centre
+// becomes the mean (one fp64 division) rounded to nearest even in the storage
+// type, and a centre without members keeps its value.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void kmeans_update_kernel(const T* __restrict__ x, T* __restrict__ cent,
-                                                            const uint32_t* __restrict__ off,
-                                                            const uint16_t* __restrict__ list, int C, int64_t n) {
+                                                            const uint8_t* __restrict__ ids, int C, int64_t n) {
   constexpr int PER = D / 64;                 // channels per lane
   constexpr int WPR = PER * int(sizeof(T)) / 4 > 0 ? PER * int(sizeof(T)) / 4 : 1;   // 32-bit words per lane and row
   constexpr int BATCH = 64 / WPR < 64 ? 64 / WPR : 64;   // rows in flight (64 registers of raw words)
+  __shared__ __attribute__((aligned(16))) uint8_t sid[kScanChunk];
+  __shared__ int slist[4][64];
   const int lane = threadIdx.x % 64;
-  const int c = blockIdx.x * 4 + threadIdx.x / 64;
+  const int wave = threadIdx.x / 64;
+  const int c = blockIdx.x * 4 + wave;
   const int h = blockIdx.y;
-  if (c >= C) return;                         // wave-uniform; the kernel has no block barrier
-  const int64_t nk = (n + kListChunk - 1) / kListChunk;
+  const bool active = c < C;                  // wave-uniform; every wavefront takes the barriers
+  const uint8_t* idh = ids + int64_t(h) * n;
   const T* xh = x + int64_t(h) * n * D + lane * PER;
   double acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.0;
-  int cnt = 0;
-  // lane's channels of a row as fp32
+  int64_t cnt = 0;
+  int nl = 0;                                 // members listed, not yet added
+  // lane's channels of a row
   auto load_raw = [&](const T* row, uint32_t (&w)[WPR]) {
     if constexpr (sizeof(T) == 2 && PER == 1) w[0] = reinterpret_cast<const uint16_t*>(row)[0];
-    else if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int q = 0; q < WPR; ++q) w[q] = reinterpret_cast<const uint32_t*>(row)[q];
-    } else {
+    else {
 #pragma unroll
       for (int q = 0; q < WPR; ++q) w[q] = reinterpret_cast<const uint32_t*>(row)[q];
     }
@@ -477,31 +404,62 @@ __global__ __launch_bounds__(256) void kmeans_update_kernel(const T* __restrict_
       return __uint_as_float(w[i]);
     }
   };
-  for (int64_t k = 0; k < nk; ++k) {
-    const uint32_t* offk = off + (int64_t(h) * nk + k) * (C + 1);
-    const int lo = int(offk[c]), hi = int(offk[c + 1]);
-    const uint16_t* lk = list + int64_t(h) * n + k * kListChunk;
-    const T* xk = xh + k * kListChunk * D;
-    cnt += hi - lo;
-    for (int s0 = lo; s0 < hi; s0 += 64) {
-      const int m = hi - s0 < 64 ? hi - s0 : 64;
-      const int mine = s0 + lane < hi ? int(lk[s0 + lane]) : 0;   // member s0 + lane of the list
-      for (int u0 = 0; u0 < m; u0 += BATCH) {
-        uint32_t w[BATCH][WPR];
+  auto flush = [&]() {                        // add the listed rows, in list order
+    for (int u0 = 0; u0 < nl; u0 += BATCH) {
+      uint32_t w[BATCH][WPR];
 #pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-          const int j = __builtin_amdgcn_readlane(mine, u0 + u < m ? u0 + u : 0);
-          load_raw(xk + int64_t(j) * D, w[u]);
+      for (int u = 0; u < BATCH; ++u) {
+        const int j = slist[wave][u0 + u < nl ? u0 + u : nl - 1];
+        load_raw(xh + int64_t(j) * D, w[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u)
+        if (u0 + u < nl) {
+#pragma unroll
+          for (int i = 0; i < PER; ++i) acc[i] = __dadd_rn(acc[i], double(value(w[u], i)));
+        }
+    }
+    nl = 0;
+  };
+  for (int64_t c0 = 0; c0 < n; c0 += kScanChunk) {
+    const int len = int(n - c0 < kScanChunk ? n - c0 : kScanChunk);
+    __syncthreads();                          // the previous chunk is scanned
+    if (((reinterpret_cast<uintptr_t>(idh + c0)) & 3) == 0) {
+      const int len4 = len / 4;
+      for (int i = threadIdx.x; i < len4; i += 256)
+        reinterpret_cast<uint32_t*>(sid)[i] = reinterpret_cast<const uint32_t*>(idh + c0)[i];
+      for (int i = 4 * len4 + threadIdx.x; i < len; i += 256) sid[i] = idh[c0 + i];
+    } else {
+      for (int i = threadIdx.x; i < len; i += 256) sid[i] = idh[c0 + i];
+    }
+    __syncthreads();
+    if (active) {
+      // four windows of 64 ids read at once, then taken in token order
+      for (int p0 = 0; p0 < len; p0 += 256) {
+        int idv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int p = p0 + 64 * k + lane;
+          idv[k] = p < len ? int(sid[p]) : -1;
         }
 #pragma unroll
-        for (int u = 0; u < BATCH; ++u)
-          if (u0 + u < m) {
-#pragma unroll
-            for (int i = 0; i < PER; ++i) acc[i] = __dadd_rn(acc[i], double(value(w[u], i)));
+        for (int k = 0; k < 4; ++k) {
+          const bool mine = idv[k] == c;
+          const uint64_t m = __ballot(mine);
+          if (m) {
+            const int tot = __popcll(m);
+            if (nl + tot > 64) flush();
+            const int rank = int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+            if (mine) slist[wave][nl + rank] = int(c0 + p0 + 64 * k + lane);
+            nl += tot;
+            cnt += tot;
           }
+        }
       }
     }
   }
+  if (!active) return;
+  flush();
   if (cnt == 0) return;                       // empty cluster keeps its centre
   T* dst = cent + (int64_t(h) * C + c) * D + lane * PER;
 #pragma unroll
@@ -545,32 +503,28 @@ hipError_t launch_assign(int heads, int64_t n, int dim, kvc_dtype dt, const void
 
 template <typename T, int D>
 hipError_t run_kmeans_update(int heads, int64_t n, const void* x, int C, void* cent, const uint8_t* ids,
-                             uint32_t* off, uint16_t* list, hipStream_t st) {
-  const int64_t nk = (n + kListChunk - 1) / kListChunk;
-  hipLaunchKernelGGL(member_lists_kernel, dim3(unsigned(nk), unsigned(heads)), dim3(256), 0, st, ids, n, C, off,
-                     list);
+                             hipStream_t st) {
   hipLaunchKernelGGL((kmeans_update_kernel<T, D>), dim3(unsigned((C + 3) / 4), unsigned(heads)), dim3(256), 0, st,
-                     static_cast<const T*>(x), static_cast<T*>(cent), off, list, C, n);
+                     static_cast<const T*>(x), static_cast<T*>(cent), ids, C, n);
   return hipGetLastError();
 }
 
 size_t kmeans_update_workspace(int heads, int64_t n, int C) {
-  const int64_t nk = (n + kListChunk - 1) / kListChunk;
-  const size_t a = (size_t(heads) * size_t(nk) * size_t(C + 1) * 4 + 255) & ~size_t(255);
-  return a + size_t(heads) * size_t(n) * 2;
+  (void)heads;
+  (void)n;
+  (void)C;
+  return 256;                                 // reserved; the update keeps its lists in LDS
 }
 
 hipError_t launch_kmeans_update(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C, void* cent,
                                 const uint8_t* ids, void* ws, hipStream_t st) {
+  (void)ws;
   if (heads == 0 || n == 0) return hipSuccess;
-  const int64_t nk = (n + kListChunk - 1) / kListChunk;
-  auto* off = static_cast<uint32_t*>(ws);
-  auto* list = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) +
-                                           ((size_t(heads) * size_t(nk) * size_t(C + 1) * 4 + 255) & ~size_t(255)));
-  if (dt == KVC_BF16 && dim == 128) return run_kmeans_update<bf16_t, 128>(heads, n, x, C, cent, ids, off, list, st);
-  if (dt == KVC_BF16 && dim == 64) return run_kmeans_update<bf16_t, 64>(heads, n, x, C, cent, ids, off, list, st);
-  if (dt == KVC_F32 && dim == 128) return run_kmeans_update<float, 128>(heads, n, x, C, cent, ids, off, list, st);
-  if (dt == KVC_F32 && dim == 64) return run_kmeans_update<float, 64>(heads, n, x, C, cent, ids, off, list, st);
+  if (n >= (int64_t(1) << 31)) return hipErrorInvalidValue;   // token indices are 32-bit in the lists
+  if (dt == KVC_BF16 && dim == 128) return run_kmeans_update<bf16_t, 128>(heads, n, x, C, cent, ids, st);
+  if (dt == KVC_BF16 && dim == 64) return run_kmeans_update<bf16_t, 64>(heads, n, x, C, cent, ids, st);
+  if (dt == KVC_F32 && dim == 128) return run_kmeans_update<float, 128>(heads, n, x, C, cent, ids, st);
+  if (dt == KVC_F32 && dim == 64) return run_kmeans_update<float, 64>(heads, n, x, C, cent, ids, st);
   return hipErrorInvalidValue;
 }
 

@@ -49,12 +49,12 @@ hipError_t launch_encode(int heads, int64_t n, int dim, kvc_dtype dt, const void
 hipError_t launch_assign(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C,
                          const void* cent, uint8_t* ids, hipStream_t st);
 constexpr int kAssignRounds = 1;       // 256-token rounds per assignment workgroup
-// k-means update (member lists + per-centre means); ws holds
-// kmeans_update_workspace(heads, n, C) bytes, 256-byte aligned.
+// k-means update (per-centre means over the members in token order); ws of
+// kmeans_update_workspace(heads, n, C) bytes is reserved (the lists live in LDS).
 hipError_t launch_kmeans_update(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C,
                                 void* cent, const uint8_t* ids, void* ws, hipStream_t st);
 size_t kmeans_update_workspace(int heads, int64_t n, int C);
-constexpr int kListChunk = 16384;      // tokens per member-list chunk (ids staged in LDS)
+constexpr int kScanChunk = 32768;      // ids per LDS chunk of the k-means update
 
 // Query-aware assignment (QSAC) of key tokens; n_cand in {1, 2, 4, 8}, group 16 or 32;
 // w [heads][dim] fp32 or NULL (all ones).

@@ -97,8 +97,7 @@ typedef struct {
  *   ids_out    [heads][n_tokens]: argmin over centres of the squared L2 distance,
  *              ties to the lowest index.
  *   ws         workspace of at least kvc_fit_assign_workspace_bytes(...) bytes
- *              (the per-centre member lists of the update: 2 bytes per token
- *              plus 4 per centre and chunk of 16384 tokens).
+ *              (256 bytes, reserved: the update keeps its member lists in LDS).
  * dim must be 64 or 128; n_centroids 1..256; n_tokens >= n_centroids is not
  * required. */
 kvc_status kvc_fit_assign(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt,
