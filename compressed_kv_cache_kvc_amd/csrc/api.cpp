@@ -248,7 +248,7 @@ const char* kvc_version(void) { return "kvc 0.1.0 (gfx950)"; }
 size_t kvc_fit_assign_workspace_bytes(int32_t heads, int64_t n_tokens, int32_t dim, int32_t n_centroids) {
   (void)dim;
   if (heads <= 0 || n_centroids <= 0) return 0;
-  // the member lists of the centre update
+  // reserved (the centre update keeps its member lists in LDS)
   return align_up(kvc::kmeans_update_workspace(heads, n_tokens > 0 ? n_tokens : 0, n_centroids));
 }
 

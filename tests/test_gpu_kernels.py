@@ -177,8 +177,8 @@ def test_fit_many_heads():
 
 
 def test_fit_long_history_member_list_chunks():
-    # 40000 tokens per head: the member lists of the centre update span three
-    # chunks of 16384 tokens, whose sums must continue in token order
+    # 40000 tokens per head: the ids of the centre update pass through LDS in two
+    # chunks of 32768 tokens, and the sums must continue across them
     # (seed 16 with these centres has no near-tie token, before or after the update)
     H, N, C, d = 1, 40000, 16, 64
     x = _bf16_tokens(H, N, d, 16)
