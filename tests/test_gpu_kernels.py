@@ -353,3 +353,71 @@ def test_lse_merge_in_place():
     for h in range(H):
         assert np.allclose(a.cpu().numpy()[h], ref[h][0], rtol=1e-5, atol=1e-6)
         assert np.allclose(b.cpu().numpy()[h], ref[h][1], rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_attend_logit_jumps(d):
+    """Logits far below the later maximum in the first tiles (the first tile sets
+    the reference), then two jumps far above the running maximum mid-history
+    (probabilities past the fp16 range before the rescale), then ordinary keys:
+    the lazily raised reference must still give the oracle's output and LSE."""
+    H, N, n_q, C = 2, 900, 200, 32
+    g = torch.Generator().manual_seed(61)
+    u = torch.randn(H, 1, d, generator=g)
+    u = u / u.norm(dim=-1, keepdim=True)            # one shared direction per head
+    q = torch.randn(H, n_q, d, generator=g) + 10.0 * u
+    k = torch.randn(H, N, d, generator=g)
+    beta = torch.zeros(N)
+    beta[:200] = -20.0                               # first tiles: logits ~ -18 below the rest
+    beta[300:311] = 40.0                             # jump: ~ +35
+    beta[700:706] = 90.0                             # second jump: ~ +80
+    k = k + beta[None, :, None] * u
+    v = torch.randn(H, N, d, generator=g)
+    q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    kn, vn = np32(k), np32(v)
+    kc = synth.forgy_init(k, C, 62)
+    vc = synth.forgy_init(v, C, 63)
+    kcn, vcn = np32(kc), np32(vc)
+    kid = np.stack([oracle.assign(kn[h], kcn[h])[0] for h in range(H)])
+    vid = np.stack([oracle.assign(vn[h], vcn[h])[0] for h in range(H)])
+    cache = Cache(kn, vn, kcn, vcn, kid, vid, 4, 4, 32)
+    # the logits of the dequantized keys do jump as intended
+    seg = cache.oracle_segment(0)
+    khat = oracle.reconstruct(seg.k_codes, seg.k_meta, seg.k_ids, seg.k_cent, 4, 32)
+    s = np32(q)[0] @ khat.T / np.sqrt(d)
+    assert s[:, 700:706].max() - s[:, :64].max() > 60 and s[:, 300:311].max() - s[:, :300].max() > 20
+    _attend_check(q, [cache], what=f"logit jumps d{d}")
+
+
+def test_attend_lowdim_logit_jumps():
+    """The rank-32 path (one tile per step) with logit jumps along a direction
+    inside the reduced key basis: the first tiles far below, then jumps of about
+    +18 log2 units (probabilities past the fp16 range before the rescale) and
+    +13.  The reduced queries are fp16, so a logit carries about 2^-12 of its own
+    size as rounding error; the largest logits here stay near 30."""
+    H, N, d, n_q, C, rank = 2, 900, 128, 200, 24, 32
+    g = torch.Generator().manual_seed(64)
+    Uk, Uv = synth.orthonormal_basis(H, d, rank, 65), synth.orthonormal_basis(H, d, rank, 66)
+    u = Uk[:, :, 0].unsqueeze(1)                     # [H, 1, d], unit length, kept by the projection
+    q = torch.randn(H, n_q, d, generator=g) + 10.0 * u
+    k = torch.randn(H, N, d, generator=g)
+    beta = torch.zeros(N)
+    beta[:200] = -20.0
+    beta[300:311] = 20.0
+    beta[700:706] = 30.0
+    k = k + beta[None, :, None] * u
+    v = torch.randn(H, N, d, generator=g)
+    q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    kn, vn = np32(k), np32(v)
+    kcn, vcn = np32(synth.forgy_init(k, C, 67)), np32(synth.forgy_init(v, C, 68))
+    kid = np.stack([oracle.assign(kn[h], kcn[h])[0] for h in range(H)])
+    vid = np.stack([oracle.assign(vn[h], vcn[h])[0] for h in range(H)])
+    cache = Cache(kn, vn, kcn, vcn, kid, vid, 2, 4, 16, Uk.numpy(), Uv.numpy())
+    out, lse = kvc().attend_lowdim(q.to(DEV), Uk.to(DEV), Uv.to(DEV), [cache.gpu_segment()])
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    qn = np32(q)
+    for h in range(H):
+        o_ref, l_ref = oracle.attend_lowdim(qn[h], Uk.numpy()[h], Uv.numpy()[h], [cache.oracle_segment(h)])
+        assert l_ref.max() > 20                         # the jumps reach the reduced logits
+        check_attention(out[h], lse[h], o_ref, l_ref, f"lowdim jumps head {h}")
