@@ -205,9 +205,14 @@ __global__ __launch_bounds__(256) void qsac_mfma_kernel(const bf16_t* __restrict
   for (int c = lane; c < C; c += 64) cmax = fmaxf(cmax, sN[c]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, off, 64));
-  // bound on |computed - exact| of a score (see the file comment): the split of
-  // w*x (2^-18), the fp32 norms and the fp32 accumulation of 2D + 1 terms
-  const float err_scale = 3.8146973e-06f + float(6 * D + 8) * 5.9604645e-08f;
+  // Bound on |computed - exact| of one score, u = 2^-24: the weighted norm takes
+  // 2D roundings (n_c (1 + 2D u)); b = fl(w*x) (u) and its hi + lo split (2^-18)
+  // perturb the cross term by (u + 2^-18) S; the 2D + 1 terms of the matrix
+  // accumulation add 2D u (n_c + 2 S); S = sum |w x mu| <= sqrt(||x||_w^2 n_c)
+  // (weights >= 0).  So |err| <= (4D + 4) u cmax + (2^-17 + (4D + 4) u)
+  // sqrt(||x||_w^2 cmax) with cmax = max_c n_c.
+  const float err_a = float(4 * D + 4) * 5.9604645e-08f;
+  const float err_b = 7.6293945e-06f + err_a;
 
   const int64_t wave_tok0 = int64_t(blockIdx.x) * 256 + wave * 64;
   for (int cb = 0; cb < 2; ++cb) {
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(256) void qsac_mfma_kernel(const bf16_t* __restrict
     for (int k = 0; k < M; ++k) cand[k] = top.i[k];
     // the set of the M nearest is certain when the (M+1)-th score is more than
     // twice the error bound above the M-th one (or there are at most M centres)
-    const float thr = err_scale * (xxw + 2.f * cmax);
+    const float thr = err_a * cmax + err_b * sqrtf(xxw * cmax);
     const bool flag = valid && C > M && !(top.s[M] - top.s[M - 1] > 2.f * thr);   // also catches NaN
     uint64_t mask = __ballot(flag && half == 0);
     if (mask) {
