@@ -158,6 +158,7 @@ __global__ __launch_bounds__(256) void qsac_mfma_kernel(const bf16_t* __restrict
   __shared__ float sN[256];
   __shared__ float sW[D];
   __shared__ float sWg[D / 16];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[4][D];   // a flagged token's row, per wavefront
 
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
@@ -324,11 +325,16 @@ __global__ __launch_bounds__(256) void qsac_mfma_kernel(const bf16_t* __restrict
       while (mask) {
         const int b = __builtin_ctzll(mask);
         mask &= mask - 1;
-        const uint16_t* xr = reinterpret_cast<const uint16_t*>(x + (int64_t(h) * n + tok0 + b) * D);
+        // the token's row from the two lanes that hold it, through this
+        // wavefront's LDS row (LDS operations of one wavefront complete in order)
+        if (col == b) {
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) *reinterpret_cast<uint4*>(&sX[wave][kc * 16 + half * 8]) = xraw[kc];
+        }
         double xd[PERL], wd[PERL];
 #pragma unroll
         for (int i = 0; i < PERL; ++i) {
-          xd[i] = double(__uint_as_float(uint32_t(xr[lane * PERL + i]) << 16));
+          xd[i] = double(__uint_as_float(uint32_t(sX[wave][lane * PERL + i]) << 16));
           wd[i] = double(sW[lane * PERL + i]);
         }
         auto exact = [&](int ci) -> double {
@@ -345,14 +351,11 @@ __global__ __launch_bounds__(256) void qsac_mfma_kernel(const bf16_t* __restrict
         TopList<double, M> ex;
         ex.init();
         int seen = 0;
-        for (int blk = 0; blk < nblk; ++blk) {
-          uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-          for (int q = 0; q < 8; ++q)
-            if (q == blk) {
-              w0 = __builtin_amdgcn_readlane(cm[q], b);
-              w1 = __builtin_amdgcn_readlane(cm[q], b + 32);
-            }
+        for (int blk = 0; blk < 8; ++blk) {
+          if (blk >= nblk) break;
+          const uint32_t w0 = __builtin_amdgcn_readlane(cm[blk], b);
+          const uint32_t w1 = __builtin_amdgcn_readlane(cm[blk], b + 32);
           uint32_t both = w0 | (w1 << 16);   // bit v: row 8*(v/4) + v%4 (+4 for the high half)
           while (both) {
             const int bit = __builtin_ctz(both);
