@@ -790,7 +790,7 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
 
 // fp32 queries: one thread per query, fp32 dequantization and softmax throughout.
 template <int D, int KB, int VB, int G>
-__global__ __launch_bounds__(64) void attend_f32_kernel(const float* __restrict__ q, int64_t n_q, int heads,
+__global__ __launch_bounds__(64) void attend_f32_kernel(const float* __restrict__ q, int64_t n_q,
                                                         SegList segs, float scale, float* __restrict__ out,
                                                         float* __restrict__ lse) {
   const int64_t qi = int64_t(blockIdx.x) * 64 + threadIdx.x;
@@ -952,7 +952,7 @@ hipError_t pick_f32(const float* q, int64_t n_q, int heads, const SegList& segs,
   const float scale = 1.0f / sqrtf(float(D));
 #define KVC_CASE(KB_, VB_, G_)                                                                                 \
   if (kb == KB_ && vb == VB_ && g == G_) {                                                                     \
-    hipLaunchKernelGGL((attend_f32_kernel<D, KB_, VB_, G_>), grid, dim3(64), 0, st, q, n_q, heads, segs, scale, out, \
+    hipLaunchKernelGGL((attend_f32_kernel<D, KB_, VB_, G_>), grid, dim3(64), 0, st, q, n_q, segs, scale, out, \
                        lse);                                                                                   \
     return hipGetLastError();                                                                                  \
   }
