@@ -197,6 +197,82 @@ def test_fit_long_history_member_list_chunks():
         assert not ((ids_g.cpu().numpy()[h] != ids1) & ~tie).any()
 
 
+def test_single_centre_fit_encode_attend():
+    # C = 1: every id is 0, the fitted centre is the mean of all tokens, and the
+    # codes and the attention follow from that one centre
+    H, N, d, n_q = 2, 777, 64, 130
+    x_k, x_v = _bf16_tokens(H, N, d, 60), _bf16_tokens(H, N, d, 61)
+    xk, xv = np32(x_k), np32(x_v)
+    cent = {}
+    for name, x, seed in (("k", x_k, 62), ("v", x_v, 63)):
+        init = synth.forgy_init(x, 1, seed)
+        cg = init.to(DEV).clone()
+        ids = kvc().fit_assign(x.to(DEV), cg, n_iter=2)
+        torch.cuda.synchronize()
+        assert not ids.cpu().numpy().any()
+        for h in range(H):
+            c2, ids2 = oracle.fit(np32(x)[h], np32(init)[h], n_iter=2, storage="bf16")
+            assert not ids2.any()
+            assert np.array_equal(np32(cg)[h].view(np.uint32), c2.view(np.uint32)), f"{name} head {h}"
+        cent[name] = np32(cg)
+    zeros = np.zeros((H, N), dtype=np.int64)
+    codes, meta, _ = kvc().encode(x_k.to(DEV), torch.from_numpy(cent["k"]).to(torch.bfloat16).to(DEV), 2, 16,
+                                  ids=torch.zeros(H, N, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    ref_codes, ref_meta = encode_heads(xk, cent["k"], zeros, 2, 16)
+    assert np.array_equal(codes.cpu().numpy(), ref_codes)
+    assert np.array_equal(meta.cpu().numpy(), ref_meta)
+    cache = Cache(xk, xv, cent["k"], cent["v"], zeros, zeros, 2, 4, 16)
+    _attend_check(_bf16_tokens(H, n_q, d, 64, outliers=False), [cache], what="one centre")
+
+
+def test_fit_duplicate_centre_stays_empty():
+    # an exact duplicate of centre 2 at index 5 draws no member in the first
+    # assignment (ties go to the lower index), so the update keeps it unchanged
+    H, N, C, d = 2, 900, 8, 128
+    x = _bf16_tokens(H, N, d, 65)
+    init = synth.forgy_init(x, C, 66)
+    init[:, 5] = init[:, 2]
+    cg = init.to(DEV).clone()
+    ids_g = kvc().fit_assign(x.to(DEV), cg, n_iter=1)
+    torch.cuda.synchronize()
+    xn, cn = np32(x), np32(init)
+    for h in range(H):
+        ids0, d1, d2 = oracle.assign(xn[h], cn[h])
+        assert not (ids0 == 5).any()
+        assert not (near_tie(d1, d2) & (d1 != d2)).any(), "near-tie in the update test input"
+        c1, ids1 = oracle.fit(xn[h], cn[h], n_iter=1, storage="bf16")
+        assert np.array_equal(c1[5].view(np.uint32), cn[h, 5].view(np.uint32))
+        assert np.array_equal(np32(cg)[h].view(np.uint32), c1.view(np.uint32)), f"head {h}"
+        _, e1, e2 = oracle.assign(xn[h], c1)
+        tie = near_tie(e1, e2) & (e1 != e2)
+        assert not ((ids_g.cpu().numpy()[h] != ids1) & ~tie).any()
+
+
+def test_zero_sizes():
+    # no tokens, no queries, no heads: every call returns without a launch
+    d = 128
+    x = torch.empty(2, 0, d, dtype=torch.bfloat16, device=DEV)
+    cent = torch.zeros(2, 4, d, dtype=torch.bfloat16, device=DEV)
+    ids = kvc().fit_assign(x, cent, n_iter=2)
+    codes, meta, ids2 = kvc().encode(x, cent, 2, 16)
+    assert tuple(ids.shape) == (2, 0) and tuple(ids2.shape) == (2, 0)
+    assert tuple(codes.shape) == (2, 0, 32) and tuple(meta.shape) == (2, 0, 8, 2)
+    assert not cent.float().cpu().numpy().any()
+    H, N = 2, 300
+    x_k = _bf16_tokens(H, N, d, 67)
+    kc = synth.forgy_init(x_k, 8, 68)
+    kn, kcn = np32(x_k), np32(kc)
+    kid = np.stack([oracle.assign(kn[h], kcn[h])[0] for h in range(H)])
+    seg = Cache(kn, kn, kcn, kcn, kid, kid, 2, 2, 16).gpu_segment()
+    out, lse = kvc().attend(torch.empty(H, 0, d, dtype=torch.bfloat16, device=DEV), [seg])
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (H, 0, d) and tuple(lse.shape) == (H, 0)
+    out, lse = kvc().attend(torch.empty(0, 5, d, dtype=torch.bfloat16, device=DEV), [])
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, 5, d)
+
+
 # ------------------------------------------------------------------------------ attention
 def _cache(H, N, d, C, kb, vb, g, seed, dtype=torch.bfloat16):
     x_k = _bf16_tokens(H, N, d, seed).to(dtype)
