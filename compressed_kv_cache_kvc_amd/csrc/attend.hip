@@ -563,9 +563,11 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
       return as_f16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
     };
     // operand reads run FA products ahead of their use (a ring of FA + 1
-    // fragments); with logit compensation two, which leaves the registers for
-    // the token's kept coefficients
-    constexpr int FA = PSAC ? 2 : 3, FR = FA + 1;
+    // fragments): four with 2-bit values in the overlapped schedule, three with
+    // wider values (whose code registers leave no room for a fifth fragment) and
+    // in the sequential schedule, two with logit compensation (the token's kept
+    // coefficients take the registers)
+    constexpr int FA = PSAC ? 2 : ((VB == 2 && !SEQ) ? 4 : 3), FR = FA + 1;
     f16x8 fr[FR];
 #pragma unroll
     for (int f = 0; f < FA; ++f) fr[f] = frag(f);
