@@ -375,7 +375,7 @@ __global__ __launch_bounds__(256) void kmeans_update_kernel(const T* __restrict_
   constexpr int WPR = PER * int(sizeof(T)) / 4 > 0 ? PER * int(sizeof(T)) / 4 : 1;   // 32-bit words per lane and row
   constexpr int BATCH = 64 / WPR < 64 ? 64 / WPR : 64;   // rows in flight (64 registers of raw words)
   __shared__ __attribute__((aligned(16))) uint8_t sid[kScanChunk];
-  __shared__ int slist[4][64];
+  __shared__ int slist[4][256];
   const int lane = threadIdx.x % 64;
   const int wave = threadIdx.x / 64;
   const int c = blockIdx.x * 4 + wave;
@@ -434,23 +434,38 @@ __global__ __launch_bounds__(256) void kmeans_update_kernel(const T* __restrict_
     }
     __syncthreads();
     if (active) {
-      // four windows of 64 ids read at once, then taken in token order
-      for (int p0 = 0; p0 < len; p0 += 256) {
-        int idv[4];
+      // Windows of 256 ids, four ids (one 32-bit word) per lane, lane l holding
+      // ids 4l..4l+3; four windows read at once, then taken in token order.  A
+      // byte equal to c is flagged exactly: with x = word ^ (c in every byte),
+      // ((x & 0x7f..) + 0x7f..) | x has its top bit clear only in zero bytes
+      // (no carry crosses a byte).  Flags past the end of the chunk are dropped.
+      const uint32_t cc = uint32_t(c) * 0x01010101u;
+      auto rank_of = [](uint64_t m) {
+        return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+      };
+      for (int p0 = 0; p0 < len; p0 += 1024) {
+        uint32_t wv[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const int p = p0 + 64 * k + lane;
-          idv[k] = p < len ? int(sid[p]) : -1;
+          const int p = p0 + 256 * k + 4 * lane;
+          wv[k] = p < len ? reinterpret_cast<const uint32_t*>(sid)[p >> 2] : 0u;
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const bool mine = idv[k] == c;
-          const uint64_t m = __ballot(mine);
-          if (m) {
-            const int tot = __popcll(m);
+          const int p = p0 + 256 * k + 4 * lane;
+          const uint32_t x = wv[k] ^ cc;
+          uint32_t z = ~(((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x) & 0x80808080u;
+          const int rem = len - p;
+          if (rem < 4) z &= rem <= 0 ? 0u : (0x80808080u >> (8 * (4 - rem)));
+          if (__ballot(z != 0u)) {
+            // members of this window: lane prefix of the per-lane counts (0..4)
+            // from three ballots of the count's bits
+            const int k1 = __popc(z);
+            const uint64_t b0 = __ballot(k1 & 1), b1 = __ballot(k1 & 2), b2 = __ballot(k1 & 4);
+            const int tot = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
             if (nl + tot > 64) flush();
-            const int rank = int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
-            if (mine) slist[wave][nl + rank] = int(c0 + p0 + 64 * k + lane);
+            int pos = nl + rank_of(b0) + 2 * rank_of(b1) + 4 * rank_of(b2);
+            for (uint32_t zz = z; zz != 0u; zz &= zz - 1u) slist[wave][pos++] = int(c0 + p + (__builtin_ctz(zz) >> 3));
             nl += tot;
             cnt += tot;
           }
