@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="self_forcing_layer",
+    ap.add_argument("--workload", default="streaming",
                     choices=["self_forcing_layer", "long_history", "larger_backbone", "streaming", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
@@ -419,9 +419,14 @@ class Streaming(Workload):
                                          for b in (cfg.k_bits, cfg.v_bits))
 
     def step(self):
+        """One rollout: for each chunk, fit + encode it into the cache (its own
+        centre tables), then attend the chunk's queries over every chunk so far.
+        The cache is the package's StreamingCache, the composition the rollout
+        parity test checks against the oracle."""
         import compressed_kv_cache_kvc_amd as kvc
+        from compressed_kv_cache_kvc_amd.streaming import StreamingCache
         cfg = self.cfg
-        segs = []
+        cache = StreamingCache(cfg.k_bits, cfg.v_bits, cfg.group, n_iter=cfg.n_iter)
         out = None
         if self.qsac:                 # each rollout starts cold: unit weights for the first chunk
             self.wq, self.n_seen = None, 0
@@ -429,19 +434,35 @@ class Streaming(Workload):
             self.mq, self.u, self.n_seen_m = None, None, 0
         coefs = []
         for (k, v, q, kc0, vc0) in self.chunks:
-            (kcodes, kmeta, kid, kc), (vcodes, vmeta, vid, vc) = fit_encode_pair(self, k, kc0, v, vc0,
-                                                                                 n_iter=cfg.n_iter)
-            segs.append(kvc.Segment(kcodes, kmeta, kid, kc, vcodes, vmeta, vid, vc, cfg.k_bits, cfg.v_bits, cfg.group))
+            e0 = self.ev()
+            kid, kc, vid, vc = cache.fit(k, v, kc0, vc0)
+            e1 = self.ev()
+            self.mark("fit", e0, e1)
+            if self.qsac:
+                kid = kvc.assign_qsac(k, kc, self.wq, self.qsac, cfg.group)
+                e1b = self.ev()
+                self.mark("qsac", e1, e1b)
+                e1 = e1b
+            seg = cache.encode(k, v, kid, kc, vid, vc)
+            e2 = self.ev()
+            self.mark("encode", e1, e2)
+            cache.push(seg)
             if self.psac:
                 # one basis per rollout, fixed after the first chunk (the cold start);
                 # the first chunk keeps zero coefficients (no compensation)
-                coefs.append(self.coef if self.u is not None else
-                             self.torch.zeros(cfg.heads, k.shape[1], 8, dtype=self.torch.uint16, device=self.dev))
-                out, lse = attend_step(self, q, segs, coefs) if self.u is not None else attend_step(self, q, segs, None)
-                if self.u is None:
+                if self.u is not None:
+                    coefs.append(kvc.psac_coeffs(k, kc, kid, seg.k_codes, seg.k_meta, cfg.k_bits, cfg.group, self.u))
+                    e3 = self.ev()
+                    self.mark("psac_coeffs", e2, e3)
+                else:
+                    coefs.append(self.torch.zeros(cfg.heads, k.shape[1], 8, dtype=self.torch.uint16, device=self.dev))
+                if self.u is not None:
+                    out, lse = attend_step(self, q, cache.segments, coefs)
+                else:
+                    out, lse = attend_step(self, q, cache.segments, None)
                     update_psac_basis(self, q)
             else:
-                out, lse = attend_step(self, q, segs, None)
+                out, lse = attend_step(self, q, cache.segments, None)
             if self.qsac:
                 update_query_stats(self, q)
         return out
@@ -467,18 +488,29 @@ def make_workload(cfg, dev, route=None, anchor=False):
 # ------------------------------------------------------------------------------ CPU oracle baseline
 def cpu_baseline(cfg, budget_s):
     """Time the oracle (as it stands) on a bounded sample of the workload: the
-    fp64 attention of all queries over the history, head after head, until the
-    time budget is spent or every sampled head is done (at most 16 heads are
-    generated).  The codes come from the oracle's own encoder (timed too) with
-    centres drawn from the tokens; ids from the expanded distance."""
+    fp64 attention of all queries over the history the timed step attends, head
+    after head, until the time budget is spent or every generated head is done.
+    The history has the workload's segment structure (streaming: the step-10
+    history of ten chunks, each with its own centre table; long history: eight
+    segments sharing one table).  The codes come from the oracle's own encoder
+    (timed too) with centres drawn from the tokens; ids from the expanded
+    distance."""
     import numpy as np
     import torch
     import oracle
     import synth
     from threadpoolctl import threadpool_info
 
-    N = cfg.chunk if cfg.name == "streaming" else (cfg.recent if cfg.name == "larger_backbone" else cfg.hist)
-    H = min(cfg.heads, 16)
+    if cfg.name == "streaming":
+        N, bounds, own_tables = cfg.hist, [cfg.chunk * i for i in range(cfg.steps + 1)], True
+        H = min(cfg.heads, 4)
+    elif cfg.name == "larger_backbone":
+        N, bounds, own_tables = cfg.recent, [0, cfg.recent], False
+        H = min(cfg.heads, 16)
+    else:
+        N = cfg.hist
+        bounds, own_tables = [N * i // cfg.n_segments for i in range(cfg.n_segments + 1)], False
+        H = min(cfg.heads, 16)
     if cfg.dtype == "f32":
         k, _ = synth.tiny_kv(cfg, "k")
         v, _ = synth.tiny_kv(cfg, "v")
@@ -502,18 +534,24 @@ def cpu_baseline(cfg, budget_s):
         if h > 0 and time.perf_counter() - wall0 > budget_s:
             break
         kn, vn = k[h].float().numpy(), v[h].float().numpy()
-        kc = kn[rng.choice(N, min(C, N), replace=False)]
-        vc = vn[rng.choice(N, min(C, N), replace=False)]
-        kid, vid = ids_of(kn, kc), ids_of(vn, vc)
-        t0 = time.perf_counter()
-        kcodes, kmeta = oracle.encode(kn, kc, kid, cfg.k_bits, cfg.group)
-        vcodes, vmeta = oracle.encode(vn, vc, vid, cfg.v_bits, cfg.group)
-        t_enc += time.perf_counter() - t0
-        n_enc += 2 * N
-        seg = oracle.Segment(kcodes, kmeta, kid, kc, vcodes, vmeta, vid, vc, cfg.k_bits, cfg.v_bits, cfg.group)
+        segs = []
+        for si, (a, b) in enumerate(zip(bounds[:-1], bounds[1:])):
+            if own_tables or si == 0:
+                base = (a, b) if own_tables else (0, N)
+                span = base[1] - base[0]
+                kc = kn[base[0]:base[1]][rng.choice(span, min(C, span), replace=False)]
+                vc = vn[base[0]:base[1]][rng.choice(span, min(C, span), replace=False)]
+            kid, vid = ids_of(kn[a:b], kc), ids_of(vn[a:b], vc)
+            t0 = time.perf_counter()
+            kcodes, kmeta = oracle.encode(kn[a:b], kc, kid, cfg.k_bits, cfg.group)
+            vcodes, vmeta = oracle.encode(vn[a:b], vc, vid, cfg.v_bits, cfg.group)
+            t_enc += time.perf_counter() - t0
+            n_enc += 2 * (b - a)
+            segs.append(oracle.Segment(kcodes, kmeta, kid, kc, vcodes, vmeta, vid, vc, cfg.k_bits, cfg.v_bits,
+                                       cfg.group))
         q = q_all[h].float().numpy()
         t0 = time.perf_counter()
-        oracle.attend(q, [seg])
+        oracle.attend(q, segs)
         t_att += time.perf_counter() - t0
         flops += 4.0 * len(q) * N * cfg.dim
         nq_total += len(q)
@@ -521,10 +559,13 @@ def cpu_baseline(cfg, budget_s):
     threads = 1
     for info in threadpool_info():
         threads = max(threads, int(info.get("num_threads", 1)))
+    hist = f"{N} history tokens in {len(bounds) - 1} segment(s)"
+    if cfg.name == "streaming":
+        hist = f"the step-{cfg.steps} history of {N} tokens in {cfg.steps} chunks with their own centre tables"
     return {
         "value": flops / t_att / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-        "sample": f"fp64 attention of {heads_done} head(s) x {nq_total // max(heads_done, 1)} queries x {N} "
-                  f"history tokens (d={cfg.dim}); oracle encode of the same heads' K and V ({n_enc} token rows)",
+        "sample": f"fp64 attention of {heads_done} head(s) x {nq_total // max(heads_done, 1)} queries over "
+                  f"{hist} (d={cfg.dim}); oracle encode of the same heads' K and V ({n_enc} token rows)",
         "encode_tokens_per_s": n_enc / t_enc if t_enc > 0 else None,
         "seconds": t_att + t_enc,
         "cpu_count_affinity": len(os.sched_getaffinity(0)),
@@ -658,10 +699,11 @@ def main():
         line["config"]["far"] = w.low_tokens
     if cfg.name == "larger_backbone" and lowdim_ms > 0:
         # the far part is bound by the softmax's vector work rather than the
-        # matrix cores: one exponential per score; the reference rate is one
-        # exponential per lane and clock (256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz)
+        # matrix cores: one exponential per score.  Transcendental instructions
+        # issue at a quarter of the fp32 vector rate: 256 CUs x 4 SIMDs x 16
+        # lanes / 4 per clock at 2.4 GHz
         scores = float(cfg.heads) * cfg.n_q * w.low_tokens
-        exp_peak = 256 * 4 * 16 * 2.4e9
+        exp_peak = 256 * 4 * 16 / 4 * 2.4e9
         line["lowdim"] = {"ms": round(lowdim_ms, 4),
                           "TFLOP/s": round((4.0 * cfg.heads * cfg.n_q * w.low_tokens * cfg.rank
                                             + 4.0 * cfg.heads * cfg.n_q * cfg.dim * cfg.rank) / (lowdim_ms * 1e-3) / 1e12, 2),

@@ -17,6 +17,7 @@ Entry points (names follow the C ABI):
   anchor_bits(k_bits, v_bits)               -> int            (anchor precision)
   query_moments(q, m, n_prev) / psac_basis(m) / psac_coeffs(...) / attend_psac(q, u, segs, coefs)
                                             (principal-subspace logit compensation)
+  streaming.StreamingCache                  (chunk-by-chunk composition: fit, encode, append, attend)
 """
 from __future__ import annotations
 

@@ -95,6 +95,9 @@ kvc_status check_segments(int32_t heads, int32_t dim, const kvc_segment* segs, i
                 "segment %d: v_bits must be 2, 4 or 16", i);
     KVC_REQUIRE(!raw || (s.k_bits == 16 && s.v_bits == 16 && want_rank == 0), KVC_ERR_UNSUPPORTED,
                 "segment %d: 16-bit residuals need k_bits = v_bits = 16 and full dimension", i);
+    // a 16-bit residual row is 2*dim <= 256 bytes: 2^24 rows keep its 32-bit offsets in range
+    KVC_REQUIRE(!raw || s.n_tokens <= (int64_t(1) << 24), KVC_ERR_UNSUPPORTED,
+                "segment %d: at most 2^24 tokens per head in a 16-bit residual segment", i);
     KVC_REQUIRE(raw || (s.group > 0 && code_dim % s.group == 0), KVC_ERR_INVALID_ARG,
                 "segment %d: group %d does not divide %d", i, s.group, code_dim);
     KVC_REQUIRE(s.n_centroids >= 1 && s.n_centroids <= 256, KVC_ERR_INVALID_ARG,
@@ -440,8 +443,10 @@ kvc_status attend_impl(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtyp
                   "the logit compensation needs dim 128 and bf16 queries");
     }
     if (!work) return ok();
-    KVC_REQUIRE(heads <= 65535 && (n_q + 255) / 256 * heads <= (int64_t(1) << 27), KVC_ERR_UNSUPPORTED,
-                "at most 65535 heads and 2^27 blocks of 256 queries per call");
+    // one workgroup of 512 work-items per (256-query block, head, history split of at
+    // most 8): the dispatch's work-item count must fit 32 bits
+    KVC_REQUIRE(heads <= 65535 && (n_q + 255) / 256 * heads <= (int64_t(1) << 20), KVC_ERR_UNSUPPORTED,
+                "at most 65535 heads and 2^20 blocks of 256 queries per call");
     for (int ci = 0; ci < n_codecs; ++ci) {
       KVC_REQUIRE(codecs[ci].g == 16 || codecs[ci].g == 32, KVC_ERR_UNSUPPORTED, "group must be 16 or 32");
       KVC_REQUIRE(q_dtype == codecs[ci].cdt, KVC_ERR_UNSUPPORTED, "queries and centres must share a dtype");
@@ -451,6 +456,7 @@ kvc_status attend_impl(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtyp
       KVC_REQUIRE(n_codecs <= 1, KVC_ERR_UNSUPPORTED, "fp32 queries need one codec for all segments");
       KVC_REQUIRE(n_codecs == 0 || codecs[0].kb != 16, KVC_ERR_UNSUPPORTED,
                   "fp32 queries do not read 16-bit residual segments");
+      KVC_REQUIRE(n_q <= (int64_t(1) << 26), KVC_ERR_UNSUPPORTED, "fp32 queries: at most 2^26 per head");
       const CodecKey c = n_codecs ? codecs[0] : CodecKey{2, 2, 16, KVC_F32};
       return hip_status(kvc::launch_attend(heads, n_q, dim, q_dtype, q, sl, c.kb, c.vb, c.g, c.cdt, 1, out, lse,
                                            stream),
@@ -607,7 +613,7 @@ kvc_status kvc_psac_coeffs(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dty
 size_t kvc_attend_lowdim_workspace_bytes(int32_t heads, int64_t n_q, int32_t dim, int32_t rank,
                                          const kvc_segment* segs, int32_t n_segs) {
   if (heads <= 0 || n_q <= 0 || dim != 128 || (rank != 32 && rank != 64)) return 0;
-  size_t b = align_up(size_t(heads) * size_t(n_q) * rank * 2);   // projected queries (fp16)
+  size_t b = align_up(size_t(heads) * size_t(n_q) * rank * 4);   // projected queries (fp16 hi + lo)
   b += table_bytes(heads, rank, segs, n_segs);                      // projected centres (fp16)
   const int s = kvc::attend_split_plan(heads, n_q, total_tiles_of(segs, n_segs), kvc::kLowdimRows);
   return b + split_bytes(heads, n_q, dim, s);
@@ -638,8 +644,10 @@ kvc_status kvc_attend_lowdim(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype 
     KVC_PTR(out, work, "out");
     KVC_PTR(lse, work, "lse");
     if (!work) return ok();
-    KVC_REQUIRE(heads <= 65535 && (n_q + 255) / 256 * heads <= (int64_t(1) << 27), KVC_ERR_UNSUPPORTED,
-                "at most 65535 heads and 2^27 blocks of 256 queries per call");
+    // one workgroup of 512 work-items per (256-query block, head, history split of at
+    // most 8): the dispatch's work-item count must fit 32 bits
+    KVC_REQUIRE(heads <= 65535 && (n_q + 255) / 256 * heads <= (int64_t(1) << 20), KVC_ERR_UNSUPPORTED,
+                "at most 65535 heads and 2^20 blocks of 256 queries per call");
     const CodecKey c = n_codecs ? codecs[0] : CodecKey{2, 2, 16, KVC_BF16};
     if (sl.total_tiles > 0) {
       KVC_REQUIRE(c.g == 16 || c.g == 32, KVC_ERR_UNSUPPORTED, "group must be 16 or 32");
@@ -652,7 +660,7 @@ kvc_status kvc_attend_lowdim(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype 
     KVC_PTR(ws, true, "ws");
     char* w = static_cast<char*>(ws);
     auto* q_proj = reinterpret_cast<uint16_t*>(w);
-    w += align_up(size_t(heads) * size_t(n_q) * rank * 2);
+    w += align_up(size_t(heads) * size_t(n_q) * rank * 4);
     hipError_t e = kvc::launch_project_queries(heads, n_q, dim, rank, q, basis_k, q_proj, stream);
     if (e != hipSuccess) return hip_status(e, "project queries");
     int di = 0;

@@ -65,7 +65,9 @@ __device__ __forceinline__ int exact_assign_token(const T* __restrict__ xr, cons
     if (d < best) { best = d; bi = c; }
   }
   wave_argmin(best, bi);
-  return bi;
+  // no finite distance (a token with a NaN or an infinite value): the lowest
+  // index, as the first minimum of an all-NaN or all-infinite row
+  return bi == 0x7fffffff ? 0 : bi;
 }
 
 // fp32 tokens: every token assigned exactly; one wave per token.
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
         }
         int e = bi;
         if (bi == 0x7fffffff)           // no candidate (non-finite scores): score every centre exactly
-          e = exact_assign_token<bf16_t, D>(xr, centh, C, lane);
+          e = exact_assign_token<bf16_t, D>(xr, centh, C, lane);   // 0 when no distance is finite
         if (lane == b) id = e;
       }
     }

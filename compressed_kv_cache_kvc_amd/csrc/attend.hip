@@ -48,6 +48,7 @@ namespace {
 
 struct AttendParams {
   const uint16_t* q;      // queries [H][n_q][DQ]: bf16 (full dim) or fp16 (reduced queries, low-dim path)
+  const uint16_t* q_lo;   // low-dim path: fp16 remainders of the reduced queries [H][n_q][DQ]
   int64_t n_q;
   int heads;
   int n_split;
@@ -230,6 +231,11 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
   // rounding), so that the score products are base-2 exponents already.
   const float c_sc = p.scale_log2;
   f16x8 qf[KC];
+  // reduced queries are a sum hi + lo of two fp16 values: one fp16 rounding of
+  // q' alone would put about 2^-12 of a logit into its error, which a logit
+  // concentrated on few coefficients does not average out; the lo part costs one
+  // more score product per k-chunk
+  f16x8 ql[LOWDIM ? KC : 1];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
     uint4 w = make_uint4(0, 0, 0, 0);
@@ -237,6 +243,10 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
     if constexpr (!LOWDIM) {
       w = make_uint4(pack_f16x2(bf16_lo(w.x), bf16_lo(w.y)), pack_f16x2(bf16_hi(w.x), bf16_hi(w.y)),
                      pack_f16x2(bf16_lo(w.z), bf16_lo(w.w)), pack_f16x2(bf16_hi(w.z), bf16_hi(w.w)));
+    } else {
+      uint4 wl = make_uint4(0, 0, 0, 0);
+      if (q_ok) wl = *reinterpret_cast<const uint4*>(p.q_lo + (int64_t(h) * p.n_q + qi) * DQ + kc * 16 + half * 8);
+      ql[kc] = as_f16x8(wl);
     }
     qf[kc] = as_f16x8(w);
   }
@@ -474,6 +484,7 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
       for (int kb = 0; kb < 2; ++kb) {
         const f16x8 a = as_f16x8(*reinterpret_cast<const uint4*>(&sK[kb_][(kb * 32 + col) * ROWK + kc * 16 + half * 8]));
         sacc[kb] = mfma32h(a, qf[kc], sacc[kb]);
+        if constexpr (LOWDIM) sacc[kb] = mfma32h(a, ql[kc], sacc[kb]);
       }
     bias_qk(kb_, sacc);
   };
@@ -684,6 +695,7 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
           cur[i] = mfma32h(fr[i % FR], qf[0], f32x16{});
         else
           cur[i & 1] = mfma32h(fr[i % FR], qf[i >> 1], cur[i & 1]);
+        cur[i & 1] = mfma32h(fr[i % FR], ql[i >> 1], cur[i & 1]);   // SEQ is a low-dim schedule
       }
       bias_qk(kbuf, cur);
       mask_tail(cur, nvalid_left >= 64 ? 64 : nvalid_left);
@@ -701,6 +713,7 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
           nxt[i] = mfma32h(fr[i % FR], qf[0], f32x16{});
         else
           nxt[i & 1] = mfma32h(fr[i % FR], qf[i >> 1], nxt[i & 1]);
+        if constexpr (LOWDIM) nxt[i & 1] = mfma32h(fr[i % FR], ql[i >> 1], nxt[i & 1]);
 #pragma unroll
         for (int u = 0; u < PPM; ++u) exp_pair(i * PPM + u);
         __builtin_amdgcn_sched_barrier(0);
@@ -790,16 +803,27 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
   if (q_ok && half == 0) p.lse[row] = l > 0.f ? (m_run + __log2f(l)) * 0.69314718055994531f : -INFINITY;
 }
 
-// fp32 queries: one thread per query, fp32 dequantization and softmax throughout.
+// fp32 queries: one wavefront per (query, head), fp32 dequantization and softmax
+// throughout.  The lanes take the keys of the history in turn (key j of a segment
+// on lane j mod 64), so that a wavefront's loads of codes, metadata and ids cover
+// consecutive tokens; each lane keeps its own running maximum, sum and output
+// row, and the 64 partial results are combined at the end (rescaled to the
+// common maximum and added across the lanes).  The query row is read from LDS
+// at one address per instruction (a broadcast).
 template <int D, int KB, int VB, int G>
-__global__ __launch_bounds__(64) void attend_f32_kernel(const float* __restrict__ q, int64_t n_q,
-                                                        SegList segs, float scale, float* __restrict__ out,
-                                                        float* __restrict__ lse) {
-  const int64_t qi = int64_t(blockIdx.x) * 64 + threadIdx.x;
+__global__ __launch_bounds__(256) void attend_f32_kernel(const float* __restrict__ q, int64_t n_q,
+                                                         SegList segs, float scale, float* __restrict__ out,
+                                                         float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(16))) float sq[4][D];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t qi = int64_t(blockIdx.x) * 4 + wave;
   const int h = blockIdx.y;
-  if (qi >= n_q) return;
-  float qv[D];
-  load_row<D>(q + (int64_t(h) * n_q + qi) * D, qv);
+  if (qi >= n_q) return;                       // wave-uniform; no barrier follows
+  const float* qr = q + (int64_t(h) * n_q + qi) * D;
+  for (int c = lane; c < D; c += 64) sq[wave][c] = qr[c];
+  __builtin_amdgcn_wave_barrier();             // LDS writes of a wavefront complete in order
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   float m = -INFINITY, l = 0.f;
   float acc[D];
 #pragma unroll
@@ -808,16 +832,17 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(const float* __restrict_
     const SegDev& s = segs.s[si];
     const float* kcent = static_cast<const float*>(s.k_cent) + int64_t(h) * s.n_centroids * D;
     const float* vcent = static_cast<const float*>(s.v_cent) + int64_t(h) * s.n_centroids * D;
-    for (int64_t j = 0; j < s.n_tokens; ++j) {
+    for (int64_t j = lane; j < s.n_tokens; j += 64) {
       const int64_t tok = int64_t(h) * s.n_tokens + j;
       const float* kc = kcent + int64_t(s.k_ids[tok]) * D;
       const uint8_t* kcode = s.k_codes + tok * (D * KB / 8);
       float dot = 0.f;
+#pragma unroll 4
       for (int i = 0; i < D; ++i) {
         const uint32_t w = s.k_meta[tok * (D / G) + i / G];
         const float code = float((kcode[i / (8 / KB)] >> (KB * (i % (8 / KB)))) & ((1 << KB) - 1));
         const float kh = kc[i] + fmaf(code, f16_bits_to_f32(w & 0xffffu), f16_bits_to_f32(w >> 16));
-        dot = fmaf(qv[i], kh, dot);
+        dot = fmaf(sq[wave][i], kh, dot);
       }
       const float sc = dot * scale;
       const float m_new = fmaxf(m, sc);
@@ -836,11 +861,24 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(const float* __restrict_
       }
     }
   }
-  float* dst = out + (int64_t(h) * n_q + qi) * D;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  // combine the lanes: common maximum, then sums of the rescaled partials
+  float mw = m;
 #pragma unroll
-  for (int i = 0; i < D; ++i) dst[i] = acc[i] * inv;
-  lse[int64_t(h) * n_q + qi] = l > 0.f ? m + logf(l) : -INFINITY;
+  for (int off = 32; off >= 1; off >>= 1) mw = fmaxf(mw, __shfl_xor(mw, off, 64));
+  const float f = (m == -INFINITY) ? 0.f : expf(m - mw);   // a lane without keys adds nothing
+  l *= f;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off, 64);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  float* dst = out + (int64_t(h) * n_q + qi) * D;
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    float a = acc[i] * f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) a += __shfl_xor(a, off, 64);
+    if (lane == (i & 63)) dst[i] = a * inv;
+  }
+  if (lane == 0) lse[int64_t(h) * n_q + qi] = l > 0.f ? mw + logf(l) : -INFINITY;
 }
 
 // Reduced queries q' = U^T q (fp32 accumulation, fp16 result in tile channel order).
@@ -879,11 +917,18 @@ __global__ __launch_bounds__(256) void project_queries_kernel(const uint16_t* __
       }
     }
   }
-  // position p holds coefficient tile_channel(p); pairs of positions per word
+  // position p holds coefficient tile_channel(p); pairs of positions per word.
+  // hi = fp16(q'), lo = fp16(q' - hi) (the difference is exact in fp32)
   uint32_t* dst = reinterpret_cast<uint32_t*>(qp + (int64_t(h) * n_q + qi) * R);
+  uint32_t* dlo = reinterpret_cast<uint32_t*>(qp + (int64_t(gridDim.y) * n_q + int64_t(h) * n_q + qi) * R);
 #pragma unroll
-  for (int p2 = 0; p2 < R / 2; ++p2)
-    dst[p2] = pack_f16x2(acc[tile_channel(2 * p2)], acc[tile_channel(2 * p2 + 1)]);
+  for (int p2 = 0; p2 < R / 2; ++p2) {
+    const float a0 = acc[tile_channel(2 * p2)], a1 = acc[tile_channel(2 * p2 + 1)];
+    const uint32_t hw = pack_f16x2(a0, a1);
+    const h2 hv = as_h2(hw);
+    dst[p2] = hw;
+    dlo[p2] = pack_f16x2(a0 - float(hv[0]), a1 - float(hv[1]));
+  }
 }
 
 // Projected centres c' = U^T c (fp32 accumulation), as an fp16 table in tile
@@ -950,13 +995,13 @@ hipError_t pick_bits(const AttendParams& p, const SegList& segs, int kb, int vb,
 template <int D>
 hipError_t pick_f32(const float* q, int64_t n_q, int heads, const SegList& segs, int kb, int vb, int g, float* out,
                     float* lse, hipStream_t st) {
-  const dim3 grid(unsigned((n_q + 63) / 64), unsigned(heads));
+  const dim3 grid(unsigned((n_q + 3) / 4), unsigned(heads));
   const float scale = 1.0f / sqrtf(float(D));
-#define KVC_CASE(KB_, VB_, G_)                                                                                 \
-  if (kb == KB_ && vb == VB_ && g == G_) {                                                                     \
-    hipLaunchKernelGGL((attend_f32_kernel<D, KB_, VB_, G_>), grid, dim3(64), 0, st, q, n_q, segs, scale, out, \
-                       lse);                                                                                   \
-    return hipGetLastError();                                                                                  \
+#define KVC_CASE(KB_, VB_, G_)                                                                                  \
+  if (kb == KB_ && vb == VB_ && g == G_) {                                                                      \
+    hipLaunchKernelGGL((attend_f32_kernel<D, KB_, VB_, G_>), grid, dim3(256), 0, st, q, n_q, segs, scale, out, \
+                       lse);                                                                                    \
+    return hipGetLastError();                                                                                   \
   }
   KVC_CASE(2, 2, 16) KVC_CASE(2, 4, 16) KVC_CASE(4, 2, 16) KVC_CASE(4, 4, 16)
   KVC_CASE(2, 2, 32) KVC_CASE(2, 4, 32) KVC_CASE(4, 2, 32) KVC_CASE(4, 4, 32)
@@ -982,6 +1027,7 @@ hipError_t launch_attend(int heads, int64_t n_q, int dim, kvc_dtype q_dtype, con
   }
   AttendParams p;
   p.q = static_cast<const uint16_t*>(q);
+  p.q_lo = nullptr;
   p.n_q = n_q;
   p.heads = heads;
   p.n_split = n_split;
@@ -1054,6 +1100,7 @@ hipError_t launch_attend_lowdim(int heads, int64_t n_q, int dim, int rank, const
   if (segs.total_tiles == 0) { k_bits = v_bits = 2; group = 16; }
   AttendParams p;
   p.q = q_proj;
+  p.q_lo = q_proj + int64_t(heads) * n_q * rank;
   p.n_q = n_q;
   p.heads = heads;
   p.n_split = n_split;

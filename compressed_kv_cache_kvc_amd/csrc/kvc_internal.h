@@ -90,6 +90,9 @@ hipError_t launch_attend(int heads, int64_t n_q, int dim, kvc_dtype q_dtype, con
                          int n_split, float* out, float* lse, hipStream_t st, const float* u_psac = nullptr);
 constexpr int kPsacRank = 8;           // kept directions of the logit compensation
 
+// Reduced queries q' = U^T q as two fp16 arrays [heads][n_q][rank] (tile channel
+// order): q_proj holds fp16(q') and q_proj + heads*n_q*rank the fp16 rounding of
+// the remainder q' - fp16(q'), so that their sum carries q' to about 2^-22.
 hipError_t launch_project_queries(int heads, int64_t n_q, int dim, int rank, const void* q,
                                   const float* basis, uint16_t* q_proj, hipStream_t st);
 hipError_t launch_project_centres(int heads, int C, int dim, int rank, kvc_dtype cdt,

@@ -99,7 +99,9 @@ typedef struct {
  *   ws         workspace of at least kvc_fit_assign_workspace_bytes(...) bytes
  *              (256 bytes, reserved: the update keeps its member lists in LDS).
  * dim must be 64 or 128; n_centroids 1..256; n_tokens >= n_centroids is not
- * required. */
+ * required.  Tokens must be finite: a token with a NaN or an infinite value has
+ * no finite distance and is assigned id 0 (its codes and the centre update are
+ * then meaningless, but every id stays a valid index). */
 kvc_status kvc_fit_assign(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt,
                           const void* x, int32_t n_centroids, void* centroids,
                           int32_t n_iters, uint8_t* ids_out,
@@ -210,9 +212,14 @@ size_t kvc_encode_workspace_bytes(int32_t heads, int64_t n_tokens, int32_t dim,
                                   int32_t n_centroids, int32_t ids_given);
 
 /* Attention of n_q queries per head over the concatenation of n_segs history
- * segments (full-dimensional codes, rank = 0): S = q . k_hat / sqrt(dim),
- * k_hat = c_K[id] + q*s + z, likewise v_hat; out = softmax(S) V_hat, lse =
- * ln sum exp(S).  No mask.  An empty history gives out = 0, lse = -inf.
+ * segments (full-dimensional codes, rank = 0), each token reconstructed on
+ * demand as its prediction plus the dequantized residual (TempoKV, section 3.3,
+ * Eq. 2, with the centre as the prediction; QuantWM, Figure 9: packed storage
+ * read back by on-demand reconstruction during streaming inference):
+ * S = q . k_hat / sqrt(dim), k_hat = c_K[id] + q*s + z, likewise v_hat;
+ * out = softmax(S) V_hat, lse = ln sum exp(S), the log-sum-exp by which parts of
+ * the history merge (NanoKV, Figure 4d).  No mask.  An empty history gives
+ * out = 0, lse = -inf.
  *   q          [heads][n_q][dim], dtype q_dtype (bf16; fp32 selects an fp32 path).
  *   segs       host array of n_segs descriptors; every segment must share the
  *              codec parameters (k_bits, v_bits, group, cent_dtype); each has its
@@ -220,8 +227,10 @@ size_t kvc_encode_workspace_bytes(int32_t heads, int64_t n_tokens, int32_t dim,
  *   out, lse   fp32 outputs.
  *   ws         at least kvc_attend_workspace_bytes(...) bytes (partial results of
  *              the split over history, merged by LSE inside the call).
- * Limits: heads <= 65535 and ceil(n_q / 256) * heads <= 2^27 (else
- * KVC_ERR_UNSUPPORTED); the same limits hold for kvc_attend_lowdim. */
+ * Limits: heads <= 65535 and ceil(n_q / 256) * heads <= 2^20; fp32 queries
+ * n_q <= 2^26; a 2/4-bit segment holds at most 2^25 tokens per head, a 16-bit
+ * residual segment at most 2^24 (else KVC_ERR_UNSUPPORTED); the same limits hold
+ * for kvc_attend_lowdim. */
 kvc_status kvc_attend(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype, const void* q,
                       const kvc_segment* segs, int32_t n_segs, float* out, float* lse,
                       void* ws, size_t ws_bytes, hipStream_t stream);

@@ -129,5 +129,27 @@ def near_tie(d1, d2, rel=1e-5):
     return (gap < rel) | (d2s == 0)
 
 
+def check_ids(ids_gpu: np.ndarray, x: np.ndarray, cent: np.ndarray, rel=1e-5, what="", ref=None):
+    """Nearest-centre ids of one head against the oracle: identical except on
+    near-ties (0 < (D2 - D1)/D2 < rel); exact ties (D1 == D2) must go to the
+    lowest index like the oracle's.  On a near-tie the GPU's id must still be a
+    valid answer: its own distance, by the plain definition in fp64, within
+    rel * D2 of the smallest.  ``ref`` may pass oracle.assign(x, cent) when it
+    is already known.  Returns (near-ties, ids that differ from the oracle's)."""
+    ids, d1, d2 = oracle.assign(x, cent) if ref is None else ref
+    exact = d1 == d2
+    tie = near_tie(d1, d2, rel) & ~exact
+    bad = (ids_gpu != ids) & ~tie
+    assert not bad.any(), f"{what}: {int(bad.sum())} ids differ outside near-ties"
+    j = np.nonzero(tie & (ids_gpu != ids))[0]
+    if len(j):
+        assert np.all((ids_gpu[j] >= 0) & (ids_gpu[j] < cent.shape[0])), f"{what}: id out of range on a near-tie"
+        diff = x[j].astype(np.float64) - cent[ids_gpu[j]].astype(np.float64)
+        dg = (diff * diff).sum(axis=1)
+        worse = dg - d1[j] > rel * d2[j]
+        assert not worse.any(), f"{what}: {int(worse.sum())} near-tie ids are not among the nearest centres"
+    return int(tie.sum()), int(len(j))
+
+
 def softmax_scale(d):
     return 1.0 / math.sqrt(d)

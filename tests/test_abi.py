@@ -111,6 +111,15 @@ def test_attend_validation(lib):
     assert _attend(lib, [raw], wsb=0) == WS                   # 16-bit residual segments need no metadata
     assert _attend(lib, [_seg(k_bits=16, v_bits=2)]) == UNS   # 16-bit K needs 16-bit V
     assert _attend(lib, [raw], qdt=0) == UNS                  # fp32 queries read 2/4-bit codes only
+    # 16-bit residual rows are 256 bytes at d = 128: at most 2^24 rows per head
+    # keep the kernel's 32-bit row offsets in range; 2/4-bit segments allow 2^25
+    big16 = _seg(k_bits=16, v_bits=16, k_meta=None, v_meta=None, n_tokens=(1 << 24) + 1)
+    assert _attend(lib, [big16], wsb=0) == UNS
+    assert "2^24" in lib.kvc_last_error().decode()
+    ok16 = _seg(k_bits=16, v_bits=16, k_meta=None, v_meta=None, n_tokens=1 << 24)
+    assert _attend(lib, [ok16], wsb=0) == WS                  # passes the limit, stops at the workspace
+    assert _attend(lib, [_seg(n_tokens=(1 << 25) + 1)], wsb=0) == UNS
+    assert _attend(lib, [_seg(n_tokens=1 << 25)], wsb=0) == WS
     assert _attend(lib, [_seg(k_codes=None)]) == INV
     assert _attend(lib, [_seg()] * 25) == UNS                 # more segments than one launch walks
     assert _attend(lib, [_seg(cent_dtype=0)]) == UNS          # bf16 queries with fp32 centres

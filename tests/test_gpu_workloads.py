@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from tests.helpers import Cache, check_attention, encode_heads, near_tie, nearest_ids, np32
+from tests.helpers import Cache, check_attention, check_ids, encode_heads, nearest_ids, np32
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -96,13 +96,20 @@ def test_tiny_whole_path():
 
 
 # ------------------------------------------------------------------------------ assignment + update, full size
-@pytest.mark.parametrize("name", ["self_forcing_layer", "streaming"])
+@pytest.mark.parametrize("name", ["self_forcing_layer", "long_history", "larger_backbone", "streaming"])
 def test_assign_and_update_full_size(name):
+    """One assignment and one Lloyd iteration over every head at the workload's
+    full size (long_history: 70200 tokens a head, so the update walks three LDS
+    chunks of ids; larger_backbone: 40 heads x 32760), checked on sampled heads:
+    ids against the oracle's assignment, and, wherever the GPU's ids equal the
+    oracle's (a near-tie resolved the other way changes the update's input),
+    the updated centres bit for bit and the ids after the update."""
+    from concurrent.futures import ThreadPoolExecutor
     cfg = synth.get_config(name)
-    N = cfg.hist if name == "self_forcing_layer" else cfg.chunk
+    N = cfg.chunk if name == "streaming" else cfg.hist
     x = synth.AR1Stream(cfg, "k", device=DEV).tokens(N)
     cent0 = synth.forgy_init(x, cfg.n_centroids, synth.seed_for(cfg.seed, 0, 0, 1))
-    sample = [0, cfg.heads // 2, cfg.heads - 1]
+    sample = [0, cfg.heads - 1] if N > 20000 else [0, cfg.heads // 2, cfg.heads - 1]
     c_g = cent0.clone()
     ids_g = kvc().fit_assign(x, c_g, n_iter=0).cpu().numpy()
     c1_g = cent0.clone()
@@ -110,20 +117,27 @@ def test_assign_and_update_full_size(name):
     torch.cuda.synchronize()
     xs, cs = np32(x[sample]), np32(cent0[sample])
     c1s = np32(c1_g[sample])
-    excl = 0
-    for i, h in enumerate(sample):
-        ids, d1, d2 = oracle.assign(xs[i], cs[i])
-        tie = near_tie(d1, d2) & (d1 != d2)
-        assert not ((ids_g[h] != ids) & ~tie).any(), f"{name} head {h}: ids differ outside near-ties"
-        excl += int(tie.sum())
-        if not tie.any():
-            c1, ids1 = oracle.fit(xs[i], cs[i], n_iter=1, storage="bf16")
-            assert np.array_equal(c1s[i].view(np.uint32), c1.view(np.uint32)), f"{name} head {h}: centres"
-            _, e1, e2 = oracle.assign(xs[i], c1)
-            tie1 = near_tie(e1, e2) & (e1 != e2)
-            assert not ((ids1_g[h] != ids1) & ~tie1).any()
-    print(f"{name}: near-ties excluded {excl} of {len(sample) * N}")
+
+    def one(i):
+        h = sample[i]
+        ref0 = oracle.assign(xs[i], cs[i])
+        tie, differ = check_ids(ids_g[h].astype(np.int64), xs[i], cs[i], what=f"{name} head {h}", ref=ref0)
+        if differ:
+            return tie, False
+        c1, ids1, hist = oracle.fit(xs[i], cs[i], n_iter=1, storage="bf16", history=True)
+        assert np.array_equal(hist[0][1], ref0[0])
+        assert np.array_equal(c1s[i].view(np.uint32), c1.view(np.uint32)), f"{name} head {h}: centres"
+        check_ids(ids1_g[h].astype(np.int64), xs[i], c1, what=f"{name} head {h} after the update")
+        return tie, True
+
+    # numpy releases the GIL inside the oracle's array operations: heads in parallel
+    with ThreadPoolExecutor(max_workers=len(sample)) as ex:
+        res = list(ex.map(one, range(len(sample))))
+    excl = sum(t for t, _ in res)
+    updated = sum(u for _, u in res)
+    print(f"{name}: near-ties excluded {excl} of {len(sample) * N}; centre updates checked on {updated} heads")
     assert excl <= 0.001 * len(sample) * N
+    assert updated >= 1
 
 
 # ------------------------------------------------------------------------------ encode, full size

@@ -235,6 +235,23 @@ def test_assign_distances_match_definition():
         assert d1[j] == pytest.approx(D[0], rel=1e-12) and d2[j] == pytest.approx(D[1], rel=1e-12)
 
 
+def test_assign_non_finite_token_takes_the_lowest_index():
+    # a token with a NaN or an infinite channel has no finite distance to any
+    # centre: the first minimum of such a row is index 0, so the id stays a valid
+    # index into the centre table (the kernels map this case to 0 as well)
+    rng = np.random.default_rng(33)
+    c = rng.standard_normal((9, 8)).astype(np.float32)
+    x = rng.standard_normal((5, 8)).astype(np.float32)
+    x[1, 3] = np.nan
+    x[2, 0] = np.inf
+    x[3, :] = -np.inf
+    with np.errstate(invalid="ignore"):
+        ids, d1, d2 = assign(x, c)
+    assert list(ids[1:4]) == [0, 0, 0]
+    assert ids[0] == _brute_assign(x[:1], c)[0] and ids[4] == _brute_assign(x[4:], c)[0]
+    assert all(0 <= i < len(c) for i in ids)
+
+
 # ----------------------------------------------------------------------------- fitting
 def test_fit_objective_never_increases():
     cfg = synth.get_config("self_forcing_layer")
