@@ -9,6 +9,7 @@ Entry points (names follow the C ABI):
   fit_assign(x, centroids, n_iter)          -> ids            (centroids fitted in place)
   encode(x, centroids, bits, group, ...)    -> (codes, meta, ids)
   attend(q, segments)                       -> (out, lse)
+  attend_noalloc(q, segments, out, lse)     -> (out, lse)     (no allocation: static scratch)
   attend_lowdim(q, basis_k, basis_v, segs)  -> (out, lse)
   lse_merge(outs, lses)                     -> (out, lse)
   assign_qsac(x, centroids, w, n_cand, group) -> ids          (query-aware key assignment)
@@ -30,7 +31,7 @@ import torch
 from . import _lib
 from ._lib import KvcSegment
 
-__all__ = ["KvcError", "Segment", "fit_assign", "encode", "attend", "attend_lowdim", "lse_merge",
+__all__ = ["KvcError", "Segment", "fit_assign", "encode", "attend", "attend_noalloc", "attend_lowdim", "lse_merge",
            "assign_qsac", "query_stats", "route_frames", "anchor_bits", "query_moments", "psac_basis",
            "psac_coeffs", "attend_psac", "library", "version"]
 
@@ -273,6 +274,20 @@ def attend(q: torch.Tensor, segments: Sequence[Segment], out: Optional[torch.Ten
     ws = _workspace(wsb, q.device)
     _check(lib.kvc_attend(H, n_q, d, _dtype_code(q), _ptr(q), arr, len(segments), _ptr(out), _ptr(lse),
                           _ptr(ws), wsb, _stream(q.device)))
+    return out, lse
+
+
+def attend_noalloc(q: torch.Tensor, segments: Sequence[Segment], out: torch.Tensor, lse: torch.Tensor):
+    """attend() through kvc_attend_noalloc: the workspace is the library's static
+    per-GPU scratch array, so the call allocates nothing (the caller passes the
+    outputs).  Calls that overlap on one GPU race on that array."""
+    _need(q, "q")
+    H, n_q, d = q.shape
+    _need(out, "out", q.device, torch.float32, (H, n_q, d))
+    _need(lse, "lse", q.device, torch.float32, (H, n_q))
+    arr = _seg_array(segments)
+    _check(library().kvc_attend_noalloc(H, n_q, d, _dtype_code(q), _ptr(q), arr, len(segments), _ptr(out),
+                                        _ptr(lse), _stream(q.device)))
     return out, lse
 
 

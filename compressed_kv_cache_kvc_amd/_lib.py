@@ -9,13 +9,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvc.so")
 
 KVC_OK, KVC_ERR_INVALID_ARG, KVC_ERR_UNSUPPORTED, KVC_ERR_WORKSPACE, KVC_ERR_HIP = range(5)
+NOALLOC_SCRATCH_BYTES = 64 << 20   # KVC_NOALLOC_SCRATCH_BYTES of include/kvc.h
 KVC_F32, KVC_BF16 = 0, 1
 
 # every symbol include/kvc.h declares
 EXPORTS = [
     "kvc_fit_assign", "kvc_fit_assign_workspace_bytes",
     "kvc_encode", "kvc_encode_workspace_bytes",
-    "kvc_attend", "kvc_attend_workspace_bytes",
+    "kvc_attend", "kvc_attend_workspace_bytes", "kvc_attend_noalloc",
     "kvc_attend_lowdim", "kvc_attend_lowdim_workspace_bytes",
     "kvc_lse_merge", "kvc_assign_qsac", "kvc_query_stats", "kvc_route_frames", "kvc_anchor_bits",
     "kvc_query_moments", "kvc_psac_basis", "kvc_psac_coeffs", "kvc_attend_psac", "kvc_attend_psac_workspace_bytes",
@@ -53,6 +54,8 @@ _SIGS = {
     "kvc_attend": (ctypes.c_int, [_i32, _i64, _i32, ctypes.c_int, _vp, ctypes.POINTER(KvcSegment), _i32, _vp, _vp,
                                   _vp, _sz, _vp]),
     "kvc_attend_workspace_bytes": (_sz, [_i32, _i64, _i32, ctypes.c_int, ctypes.POINTER(KvcSegment), _i32]),
+    "kvc_attend_noalloc": (ctypes.c_int, [_i32, _i64, _i32, ctypes.c_int, _vp, ctypes.POINTER(KvcSegment), _i32,
+                                          _vp, _vp, _vp]),
     "kvc_attend_lowdim": (ctypes.c_int, [_i32, _i64, _i32, ctypes.c_int, _vp, _vp, _vp, _i32,
                                          ctypes.POINTER(KvcSegment), _i32, _vp, _vp, _vp, _sz, _vp]),
     "kvc_attend_lowdim_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, ctypes.POINTER(KvcSegment), _i32]),

@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "kvc_internal.h"
@@ -527,6 +528,75 @@ kvc_status kvc_attend(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype
                       const kvc_segment* segs, int32_t n_segs, float* out, float* lse, void* ws,
                       size_t ws_bytes, hipStream_t stream) {
   return attend_impl(heads, n_q, dim, q_dtype, q, segs, n_segs, out, lse, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------------ attention without allocation
+// Workspace of kvc_attend_noalloc: one array per GPU, resident from the load of
+// the library's code object until the process ends.  Host code never passes the
+// array's own name to a kernel or a copy (on the host it names a host-side
+// stand-in); it uses the device address that hipGetSymbolAddress returns for the
+// current device, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[KVC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first call
+// on that device); nullptr with the message set on failure.
+void* scratch_on_current_device(kvc_status* st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *st = hip_status(e, "hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *st = fail(KVC_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      *st = hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *st = KVC_OK;
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+kvc_status kvc_attend_noalloc(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype, const void* q,
+                              const kvc_segment* segs, int32_t n_segs, float* out, float* lse,
+                              hipStream_t stream) {
+  try {
+    // the same validation and plan as kvc_attend; only the workspace differs
+    const size_t need = kvc_attend_workspace_bytes(heads, n_q, dim, q_dtype, segs, n_segs);
+    KVC_REQUIRE(need <= size_t(KVC_NOALLOC_SCRATCH_BYTES), KVC_ERR_WORKSPACE,
+                "kvc_attend_noalloc: this call needs %zu bytes of workspace, above the %zu-byte static scratch "
+                "array (use kvc_attend with a caller workspace)",
+                need, size_t(KVC_NOALLOC_SCRATCH_BYTES));
+    void* ws = nullptr;
+    if (need > 0) {
+      kvc_status st = KVC_OK;
+      ws = scratch_on_current_device(&st);
+      if (ws == nullptr) return st;
+    }
+    return attend_impl(heads, n_q, dim, q_dtype, q, segs, n_segs, out, lse, ws, need, stream, nullptr, nullptr);
+  } catch (...) {
+    return fail(KVC_ERR_HIP, "unexpected exception in kvc_attend_noalloc");
+  }
 }
 
 // ------------------------------------------------------------------------------ logit compensation

@@ -237,6 +237,23 @@ kvc_status kvc_attend(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype
 size_t kvc_attend_workspace_bytes(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype,
                                   const kvc_segment* segs, int32_t n_segs);
 
+/* kvc_attend for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * workspace kvc_attend would take (kvc_attend_workspace_bytes) is instead a
+ * static device array of KVC_NOALLOC_SCRATCH_BYTES inside the library, one per
+ * GPU, held from the first use on that GPU until the process ends; the call
+ * itself allocates and frees nothing.  Same arguments (minus the workspace),
+ * validation, kernels and results as kvc_attend.  A call whose workspace would
+ * exceed the array returns KVC_ERR_WORKSPACE before any launch (e.g. 24 heads
+ * over ten 256-centre segments need 31 MiB and fit; 720 heads over ten do not).
+ * Every call on one GPU shares that GPU's array and leaves its contents behind
+ * (nothing in it needs to start at zero), so calls that overlap on one GPU, on
+ * different streams or from different threads, race: serialize them. */
+#define KVC_NOALLOC_SCRATCH_BYTES (64u << 20)
+kvc_status kvc_attend_noalloc(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype, const void* q,
+                              const kvc_segment* segs, int32_t n_segs, float* out, float* lse,
+                              hipStream_t stream);
+
 /* Low-dimensional attention over coefficient-coded segments (NanoKV, Figure 4a
  * and 4d): q' = U_K^T q; k' = U_K^T c_K[id] + a_hat_K; S = q'.k' / sqrt(dim);
  * O' = softmax(S) (U_V^T c_V[id] + a_hat_V); out = U_V O'.  Returns lse as
