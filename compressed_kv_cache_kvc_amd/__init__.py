@@ -147,7 +147,11 @@ def query_stats(q: torch.Tensor, w: Optional[torch.Tensor] = None, n_prev: int =
             raise ValueError("n_prev > 0 needs the previous statistics w")
         w = torch.empty(H, d, dtype=torch.float32, device=q.device)
     _need(w, "w", q.device, torch.float32, (H, d))
-    _check(library().kvc_query_stats(H, n_q, d, _dtype_code(q), _ptr(q), n_prev, _ptr(w), _stream(q.device)))
+    lib = library()
+    wsb = lib.kvc_query_stats_workspace_bytes(H, n_q, d)
+    ws = _workspace(wsb, q.device)
+    _check(lib.kvc_query_stats(H, n_q, d, _dtype_code(q), _ptr(q), n_prev, _ptr(w), _ptr(ws), wsb,
+                               _stream(q.device)))
     return w
 
 

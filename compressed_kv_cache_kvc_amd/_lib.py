@@ -18,7 +18,8 @@ EXPORTS = [
     "kvc_encode", "kvc_encode_workspace_bytes",
     "kvc_attend", "kvc_attend_workspace_bytes", "kvc_attend_noalloc",
     "kvc_attend_lowdim", "kvc_attend_lowdim_workspace_bytes",
-    "kvc_lse_merge", "kvc_assign_qsac", "kvc_query_stats", "kvc_route_frames", "kvc_anchor_bits",
+    "kvc_lse_merge", "kvc_assign_qsac", "kvc_query_stats", "kvc_query_stats_workspace_bytes",
+    "kvc_route_frames", "kvc_anchor_bits",
     "kvc_query_moments", "kvc_psac_basis", "kvc_psac_coeffs", "kvc_attend_psac", "kvc_attend_psac_workspace_bytes",
     "kvc_status_string", "kvc_last_error", "kvc_version",
 ]
@@ -62,7 +63,8 @@ _SIGS = {
     "kvc_lse_merge": (ctypes.c_int, [_i32, _i64, _i32, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp, _vp,
                                      _vp]),
     "kvc_assign_qsac": (ctypes.c_int, [_i32, _i64, _i32, ctypes.c_int, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp]),
-    "kvc_query_stats": (ctypes.c_int, [_i32, _i64, _i32, ctypes.c_int, _vp, _i64, _vp, _vp]),
+    "kvc_query_stats": (ctypes.c_int, [_i32, _i64, _i32, ctypes.c_int, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "kvc_query_stats_workspace_bytes": (_sz, [_i32, _i64, _i32]),
     "kvc_route_frames": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _vp]),
     "kvc_query_moments": (ctypes.c_int, [_i32, _i64, _i32, ctypes.c_int, _vp, _i64, _vp, _vp]),
     "kvc_psac_basis": (ctypes.c_int, [_i32, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp]),

@@ -316,8 +316,13 @@ kvc_status kvc_assign_qsac(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dty
   }
 }
 
+size_t kvc_query_stats_workspace_bytes(int32_t heads, int64_t n_q, int32_t dim) {
+  if (heads <= 0 || n_q <= 0 || (dim != 64 && dim != 128)) return 0;
+  return align_up(kvc::query_stats_workspace(heads, n_q, dim));
+}
+
 kvc_status kvc_query_stats(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype, const void* q,
-                           int64_t n_prev, float* w, hipStream_t stream) {
+                           int64_t n_prev, float* w, void* ws, size_t ws_bytes, hipStream_t stream) {
   try {
     KVC_REQUIRE(heads >= 0 && n_q >= 0 && n_prev >= 0, KVC_ERR_INVALID_ARG, "heads, n_q and n_prev must be >= 0");
     KVC_REQUIRE(heads <= 65535, KVC_ERR_UNSUPPORTED, "at most 65535 heads per call");
@@ -327,7 +332,10 @@ kvc_status kvc_query_stats(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_
     KVC_PTR(q, work, "q");
     KVC_PTR(w, work, "w");
     if (!work) return ok();
-    return hip_status(kvc::launch_query_stats(heads, n_q, dim, q_dtype, q, n_prev, w, stream), "query stats");
+    const size_t need = kvc_query_stats_workspace_bytes(heads, n_q, dim);
+    KVC_REQUIRE(ws_bytes >= need, KVC_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    KVC_PTR(ws, true, "ws");
+    return hip_status(kvc::launch_query_stats(heads, n_q, dim, q_dtype, q, n_prev, w, ws, stream), "query stats");
   } catch (...) {
     return fail(KVC_ERR_HIP, "unexpected exception in kvc_query_stats");
   }

@@ -83,9 +83,13 @@ __global__ __launch_bounds__(256) void assign_exact_kernel(const T* __restrict__
 }
 
 
+// A workgroup stages its head's centre table once and then scores `rounds`
+// consecutive blocks of 256 tokens against it (the launch picks the number of
+// rounds so that the table staging is amortized while the grid still fills the
+// chip).
 template <int D>
 __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ cent,
-                                                          int C, int64_t n, uint8_t* __restrict__ ids) {
+                                                          int C, int64_t n, int rounds, uint8_t* __restrict__ ids) {
   constexpr int ROWP = D + 8;          // padded LDS row (bf16 elements): conflict-free fragment reads
   constexpr int KC = D / 16;
   __shared__ __attribute__((aligned(16))) uint16_t sC[256 * ROWP];
@@ -149,9 +153,9 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, off, 64));
 
-  for (int round = 0; round < kAssignRounds; ++round) {
+  for (int round = 0; round < rounds; ++round) {
   // token fragments (B operand) and ||x||^2
-  const int64_t tok0 = (int64_t(blockIdx.x) * kAssignRounds + round) * 256 + wave * 64;
+  const int64_t tok0 = (int64_t(blockIdx.x) * rounds + round) * 256 + wave * 64;
   if (tok0 >= n) break;                // wave-uniform; no barrier follows
   bf16x8 xb[2][KC];
   float xx[2];
@@ -489,19 +493,256 @@ __global__ __launch_bounds__(256) void kmeans_update_kernel(const T* __restrict_
   }
 }
 
+// Centre update from member lists sorted in LDS.  One workgroup of 8
+// wavefronts per (head, group of CG consecutive centres); the head's ids (at
+// most kSortedUpdateMaxTokens) are staged in LDS once.
+//   1. count: wavefront w takes the w-th eighth of the tokens and counts, per
+//      centre of the group, its members (the lanes of one 64-token step that hold
+//      the same centre are found with one ballot per bit of the centre's index;
+//      the last of them adds the count, so no atomics are needed);
+//   2. prefix: start[u] = members of the group's centres before u; every
+//      wavefront's write offset per centre follows in wavefront order;
+//   3. scatter: the same walk writes each member's token index at its offset
+//      plus its rank among the step's lanes of that centre -- a stable counting
+//      sort, so every centre's members end up in token order;
+//   4. sums: the sorted list is cut into eight equal runs, one per wavefront,
+//      whose rows are loaded BATCH at a time and added in fp64 in list order;
+//      a centre whose members all lie in the run gets its mean written at once,
+//      a centre cut by a run boundary leaves a partial sum (at most two per
+//      wavefront);
+//   5. the partial sums are added in run order and those centres written.
+// Every addition happens in a fixed order, so the result is deterministic; a
+// centre's sum is its members' rows in token order, grouped by run.  The mean is
+// one fp64 division rounded to nearest even in the storage type; a centre without
+// members keeps its value.
+template <typename T, int D>
+__global__ __launch_bounds__(512) void kmeans_update_sorted_kernel(const T* __restrict__ x, T* __restrict__ cent,
+                                                                   const uint8_t* __restrict__ ids, int C, int CG,
+                                                                   int n) {
+  constexpr int PER = D / 64;                 // channels per lane
+  constexpr int WPR = PER * int(sizeof(T)) / 4 > 0 ? PER * int(sizeof(T)) / 4 : 1;   // 32-bit words per lane and row
+  constexpr int BATCH = 32;                   // rows in flight per wavefront
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int h = blockIdx.y;
+  const int c0 = blockIdx.x * CG;
+  const int cg = min(CG, C - c0);
+  const int npad = (n + 15) & ~15;
+  uint8_t* sid = lds;
+  uint16_t* list = reinterpret_cast<uint16_t*>(lds + npad);
+  uint32_t* off = reinterpret_cast<uint32_t*>(lds + npad + ((2 * n + 15) & ~15));   // [8][CG]
+  uint32_t* start = off + 8 * CG;                                                       // [CG + 1]
+  int* pc = reinterpret_cast<int*>(start + CG + 1);                                     // [16] centre of a partial
+  uint32_t* wsum = reinterpret_cast<uint32_t*>(pc + 16);                                // [8]
+  double* part = reinterpret_cast<double*>(
+      lds + ((npad + ((2 * n + 15) & ~15) + 4 * (8 * CG + CG + 1 + 16 + 8) + 15) & ~15));   // [16][D]
+
+  const uint8_t* idh = ids + int64_t(h) * n;
+  if ((reinterpret_cast<uintptr_t>(idh) & 3) == 0) {
+    const int n4 = n / 4;
+    for (int i = threadIdx.x; i < n4; i += 512) reinterpret_cast<uint32_t*>(sid)[i] = reinterpret_cast<const uint32_t*>(idh)[i];
+    for (int i = 4 * n4 + threadIdx.x; i < n; i += 512) sid[i] = idh[i];
+  } else {
+    for (int i = threadIdx.x; i < n; i += 512) sid[i] = idh[i];
+  }
+  for (int i = threadIdx.x; i < 8 * CG; i += 512) off[i] = 0u;
+  if (threadIdx.x < 16) pc[threadIdx.x] = -1;
+  __syncthreads();
+
+  auto rank_of = [](uint64_t m) {
+    return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+  };
+  // lanes of this step holding the same centre as this lane (valid for matching lanes)
+  auto same_centre = [&](bool m, int u) {
+    uint64_t same = __ballot(m);
+    for (int b = 0; (1 << b) < CG; ++b) {
+      const bool bit = ((u >> b) & 1) != 0;
+      const uint64_t bb = __ballot(m && bit);
+      same &= bit ? bb : ~bb;
+    }
+    return same;
+  };
+  const int s0 = int(int64_t(n) * wave / 8), s1 = int(int64_t(n) * (wave + 1) / 8);
+  // 1. counts per (wavefront, centre)
+  for (int p0 = s0; p0 < s1; p0 += 64) {
+    const int p = p0 + lane;
+    const int u = p < s1 ? int(sid[p]) - c0 : -1;
+    const bool m = u >= 0 && u < cg;
+    const uint64_t same = same_centre(m, u);
+    const int cnt = __popcll(same), rk = rank_of(same);
+    if (m && rk == cnt - 1) off[wave * CG + u] += uint32_t(cnt);
+  }
+  __syncthreads();
+  // 2. prefix over the group's centres (thread t for centre t < cg <= 256), then
+  // the per-wavefront write offsets in wavefront order
+  {
+    const int t = threadIdx.x;
+    uint32_t tot = 0u;
+    if (t < cg)
+      for (int w = 0; w < 8; ++w) tot += off[w * CG + t];
+    uint32_t inc = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t v = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += v;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    uint32_t base = 0u;
+    for (int w = 0; w < wave; ++w) base += wsum[w];
+    const uint32_t excl = base + inc - tot;
+    if (t < cg) {
+      start[t] = excl;
+      uint32_t run = excl;
+      for (int w = 0; w < 8; ++w) {
+        const uint32_t c = off[w * CG + t];
+        off[w * CG + t] = run;
+        run += c;
+      }
+    }
+    if (t == cg - 1) start[cg] = excl + tot;
+  }
+  __syncthreads();
+  // 3. stable scatter of the members' token indices
+  for (int p0 = s0; p0 < s1; p0 += 64) {
+    const int p = p0 + lane;
+    const int u = p < s1 ? int(sid[p]) - c0 : -1;
+    const bool m = u >= 0 && u < cg;
+    const uint64_t same = same_centre(m, u);
+    const int cnt = __popcll(same), below = rank_of(same);
+    if (m) list[off[wave * CG + u] + below] = static_cast<uint16_t>(p);
+    if (m && below == cnt - 1) off[wave * CG + u] += uint32_t(cnt);
+  }
+  __syncthreads();
+
+  // 4. sums over this wavefront's run of the sorted list
+  const T* xh = x + int64_t(h) * n * D + lane * PER;
+  auto load_raw = [&](int j, uint32_t (&w)[WPR]) {
+    const T* row = xh + int64_t(j) * D;
+    if constexpr (sizeof(T) == 2 && PER == 1) w[0] = reinterpret_cast<const uint16_t*>(row)[0];
+    else {
+#pragma unroll
+      for (int q = 0; q < WPR; ++q) w[q] = reinterpret_cast<const uint32_t*>(row)[q];
+    }
+  };
+  auto value = [&](const uint32_t (&w)[WPR], int i) -> float {
+    if constexpr (sizeof(T) == 2) {
+      if constexpr (PER == 1) return __uint_as_float(w[0] << 16);
+      else return (i & 1) ? bf16_hi(w[i / 2]) : bf16_lo(w[i / 2]);
+    } else {
+      return __uint_as_float(w[i]);
+    }
+  };
+  auto write_mean = [&](int u, const double (&acc)[PER]) {
+    const double cnt = double(start[u + 1] - start[u]);
+    T* dst = cent + (int64_t(h) * C + c0 + u) * D + lane * PER;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const double mean = __ddiv_rn(acc[i], cnt);
+      if constexpr (sizeof(T) == 2)
+        reinterpret_cast<uint16_t*>(dst)[i] = static_cast<uint16_t>(f64_to_bits_rne<8>(mean));
+      else
+        reinterpret_cast<uint32_t*>(dst)[i] = f64_to_bits_rne<24>(mean);
+    }
+  };
+  const int M = int(start[cg]);
+  const int r0 = int(int64_t(M) * wave / 8), r1 = int(int64_t(M) * (wave + 1) / 8);
+  if (r0 < r1) {
+    // the centre of list position r0: the largest u with start[u] <= r0
+    int u = 0;
+    {
+      int lo = 0, hi = cg - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (int(start[mid]) <= r0) lo = mid; else hi = mid - 1;
+      }
+      u = lo;
+    }
+    int u_begin = int(start[u]), u_end = int(start[u + 1]);
+    int seg = 0;
+    double acc[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] = 0.0;
+    for (int i0 = r0; i0 < r1; i0 += BATCH) {
+      uint32_t w[BATCH][WPR];
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        const int j = int(list[i0 + b < r1 ? i0 + b : r1 - 1]);
+        load_raw(j < n ? j : n - 1, w[b]);   // always in range (the list holds token indices < n)
+      }
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        const int i = i0 + b;
+        if (i >= r1) break;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) acc[k] = __dadd_rn(acc[k], double(value(w[b], k)));
+        if (i + 1 == u_end || i + 1 == r1) {
+          if (u_begin >= r0 && u_end <= r1) {
+            write_mean(u, acc);
+          } else {
+            const int slot = wave * 2 + (seg == 0 ? 0 : 1);
+#pragma unroll
+            for (int k = 0; k < PER; ++k) part[slot * D + lane * PER + k] = acc[k];
+            if (lane == 0) pc[slot] = u;
+          }
+          ++seg;
+#pragma unroll
+          for (int k = 0; k < PER; ++k) acc[k] = 0.0;
+          if (i + 1 < r1) {             // next centre with members
+            ++u;
+            while (u + 1 < cg && int(start[u + 1]) == int(start[u])) ++u;
+            u_begin = int(start[u]);
+            u_end = int(start[u + 1]);
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // 5. centres cut by a run boundary: partial sums added in run order
+  if (wave == 0) {
+    int cur = -1;
+    double acc[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = 0.0;
+    for (int slot = 0; slot < 16; ++slot) {
+      const int u = pc[slot];
+      if (u < 0) continue;
+      if (u != cur) {
+        if (cur >= 0) write_mean(cur, acc);
+        cur = u;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) acc[k] = part[slot * D + lane * PER + k];
+      } else {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) acc[k] = __dadd_rn(acc[k], part[slot * D + lane * PER + k]);
+      }
+    }
+    if (cur >= 0) write_mean(cur, acc);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_assign(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C, const void* cent,
                          uint8_t* ids, hipStream_t st) {
   if (heads == 0 || n == 0) return hipSuccess;
   if (dt == KVC_BF16) {
-    const dim3 grid(unsigned((n + 256 * kAssignRounds - 1) / (256 * kAssignRounds)), unsigned(heads));
+    // blocks of 256 tokens per head, shared out over enough workgroups per head
+    // for about kAssignMinGroups workgroups in all (two fit a compute unit), each
+    // taking the same number of consecutive blocks
+    const int64_t blocks = (n + 255) / 256;
+    const int64_t want = (kAssignMinGroups + heads - 1) / heads;
+    const int64_t groups0 = blocks < want ? blocks : want;
+    const int rounds = int((blocks + groups0 - 1) / groups0);
+    const dim3 grid(unsigned((blocks + rounds - 1) / rounds), unsigned(heads));
     if (dim == 128)
       hipLaunchKernelGGL((assign_mfma_kernel<128>), grid, dim3(256), 0, st, static_cast<const bf16_t*>(x),
-                         static_cast<const bf16_t*>(cent), C, n, ids);
+                         static_cast<const bf16_t*>(cent), C, n, rounds, ids);
     else if (dim == 64)
       hipLaunchKernelGGL((assign_mfma_kernel<64>), grid, dim3(256), 0, st, static_cast<const bf16_t*>(x),
-                         static_cast<const bf16_t*>(cent), C, n, ids);
+                         static_cast<const bf16_t*>(cent), C, n, rounds, ids);
     else
       return hipErrorInvalidValue;
   } else {
@@ -533,11 +774,43 @@ size_t kmeans_update_workspace(int heads, int64_t n, int C) {
   return 256;                                 // reserved; the update keeps its lists in LDS
 }
 
+size_t sorted_update_lds(int64_t n, int CG, int dim) {
+  const size_t npad = (size_t(n) + 15) & ~size_t(15);
+  const size_t lpad = (2 * size_t(n) + 15) & ~size_t(15);
+  return ((npad + lpad + 4 * (8 * size_t(CG) + CG + 1 + 16 + 8) + 15) & ~size_t(15)) + 16 * size_t(dim) * 8;
+}
+
+template <typename T, int D>
+hipError_t run_kmeans_update_sorted(int heads, int64_t n, const void* x, int C, void* cent, const uint8_t* ids,
+                                    hipStream_t st) {
+  // workgroups per head: enough for about kUpdateMinGroups in all, at most 16
+  // (groups of at least 16 centres)
+  int S = int((kUpdateMinGroups + heads - 1) / heads);
+  S = S < 1 ? 1 : (S > 16 ? 16 : S);
+  const int CG = (C + S - 1) / S;
+  const size_t lds = sorted_update_lds(n, CG, D);
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kmeans_update_sorted_kernel<T, D>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((kmeans_update_sorted_kernel<T, D>), dim3(unsigned((C + CG - 1) / CG), unsigned(heads)),
+                     dim3(512), lds, st, static_cast<const T*>(x), static_cast<T*>(cent), ids, C, CG, int(n));
+  return hipGetLastError();
+}
+
 hipError_t launch_kmeans_update(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C, void* cent,
                                 const uint8_t* ids, void* ws, hipStream_t st) {
   (void)ws;
   if (heads == 0 || n == 0) return hipSuccess;
   if (n >= (int64_t(1) << 31)) return hipErrorInvalidValue;   // token indices are 32-bit in the lists
+  if (n <= kSortedUpdateMaxTokens) {
+    if (dt == KVC_BF16 && dim == 128) return run_kmeans_update_sorted<bf16_t, 128>(heads, n, x, C, cent, ids, st);
+    if (dt == KVC_BF16 && dim == 64) return run_kmeans_update_sorted<bf16_t, 64>(heads, n, x, C, cent, ids, st);
+    if (dt == KVC_F32 && dim == 128) return run_kmeans_update_sorted<float, 128>(heads, n, x, C, cent, ids, st);
+    if (dt == KVC_F32 && dim == 64) return run_kmeans_update_sorted<float, 64>(heads, n, x, C, cent, ids, st);
+    return hipErrorInvalidValue;
+  }
   if (dt == KVC_BF16 && dim == 128) return run_kmeans_update<bf16_t, 128>(heads, n, x, C, cent, ids, st);
   if (dt == KVC_BF16 && dim == 64) return run_kmeans_update<bf16_t, 64>(heads, n, x, C, cent, ids, st);
   if (dt == KVC_F32 && dim == 128) return run_kmeans_update<float, 128>(heads, n, x, C, cent, ids, st);

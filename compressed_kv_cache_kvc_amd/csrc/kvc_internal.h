@@ -48,13 +48,15 @@ hipError_t launch_encode(int heads, int64_t n, int dim, kvc_dtype dt, const void
 // Nearest-centre ids; the centre norms are computed inside the kernel.
 hipError_t launch_assign(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C,
                          const void* cent, uint8_t* ids, hipStream_t st);
-constexpr int kAssignRounds = 1;       // 256-token rounds per assignment workgroup
+constexpr int kAssignMinGroups = 1024;  // assignment workgroups a launch aims for (2 per compute unit, 2 rounds)
 // k-means update (per-centre means over the members in token order); ws of
 // kmeans_update_workspace(heads, n, C) bytes is reserved (the lists live in LDS).
 hipError_t launch_kmeans_update(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C,
                                 void* cent, const uint8_t* ids, void* ws, hipStream_t st);
 size_t kmeans_update_workspace(int heads, int64_t n, int C);
-constexpr int kScanChunk = 32768;      // ids per LDS chunk of the k-means update
+constexpr int kScanChunk = 32768;      // ids per LDS chunk of the k-means update (long heads)
+constexpr int kSortedUpdateMaxTokens = 32768;   // heads up to this length: member lists sorted in LDS
+constexpr int kUpdateMinGroups = 1024;          // centre-update workgroups a launch aims for
 
 // Query-aware assignment (QSAC) of key tokens; n_cand in {1, 2, 4, 8}, group 16 or 32;
 // w [heads][dim] fp32 or NULL (all ones).
@@ -71,9 +73,11 @@ hipError_t launch_psac_basis(int heads, int dim, const float* m, int n_iter, con
 hipError_t launch_psac_coeffs(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C, const void* cent,
                               const uint8_t* ids, const uint8_t* codes, const uint16_t* meta, int bits, int group,
                               const float* u, uint16_t* coef, hipStream_t st);
-// Running per-channel second moments of the queries (w updated in place).
+// Running per-channel second moments of the queries (w updated in place); ws holds
+// query_stats_workspace(heads, n_q, dim) bytes of per-block fp64 partial sums.
 hipError_t launch_query_stats(int heads, int64_t n_q, int dim, kvc_dtype dt, const void* q, int64_t n_prev,
-                              float* w, hipStream_t st);
+                              float* w, void* ws, hipStream_t st);
+size_t query_stats_workspace(int heads, int64_t n_q, int dim);
 
 hipError_t launch_lse_merge(int heads, int64_t n_q, int dim, int n_parts, const float* const* outs,
                             const float* const* lses, float* out, float* lse, hipStream_t st);

@@ -417,37 +417,54 @@ __global__ __launch_bounds__(256) void qsac_mfma_kernel(const bf16_t* __restrict
 
 // Second moments of the queries per head and channel (QuantWM, section 4.1,
 // Eqs. 6-8, diagonal): w <- (n_prev * w + sum_i q_ic^2) / (n_prev + n_q), sums in
-// fp64.  One workgroup per head: 1024 / D row groups, group r summing the rows
-// i = r mod groups in increasing order; the groups' sums are then added in
-// group order (a fixed reduction order).
+// fp64, in two launches with a fixed reduction order:
+//   1. grid (row blocks, heads): a workgroup reads its block of rows whole (each
+//      row by consecutive threads, 16 bytes each), every thread summing its
+//      channels over the rows i = lane row + k * RL in increasing order; the RL
+//      row lanes are then added in order, giving the block's partial sums;
+//   2. one thread per (head, channel) adds the blocks' partial sums in block
+//      order and folds in the previous statistics.
 template <typename T, int D>
-__global__ __launch_bounds__(1024) void query_stats_kernel(const T* __restrict__ q, int64_t n_q, int64_t n_prev,
-                                                           float* __restrict__ w) {
-  constexpr int RG = 1024 / D;
-  __shared__ double part[RG][D];
-  const int h = blockIdx.x;
-  const int c = threadIdx.x % D, r = threadIdx.x / D;
-  const T* qh = q + int64_t(h) * n_q * D;
-  double s0 = 0.0, s1 = 0.0;
-  int64_t i = r;
-  for (; i + RG < n_q; i += 2 * RG) {
-    const double a = elem64<T>(qh + i * D, c), b = elem64<T>(qh + (i + RG) * D, c);
-    s0 = __dadd_rn(s0, __dmul_rn(a, a));
-    s1 = __dadd_rn(s1, __dmul_rn(b, b));
+__global__ __launch_bounds__(256) void query_stats_partial_kernel(const T* __restrict__ q, int64_t n_q, int64_t rows,
+                                                                  double* __restrict__ part) {
+  constexpr int CPT = 16 / int(sizeof(T));     // channels per thread (one 16-byte load)
+  constexpr int NG = D / CPT;                  // channel groups of a row
+  constexpr int RL = 256 / NG;                 // row lanes
+  __shared__ double sp[RL][D];
+  const int h = blockIdx.y, b = blockIdx.x;
+  const int g = threadIdx.x % NG, rl = threadIdx.x / NG;
+  const int64_t r0 = int64_t(b) * rows;
+  const int64_t r1 = r0 + rows < n_q ? r0 + rows : n_q;
+  const T* qh = q + int64_t(h) * n_q * D + g * CPT;
+  double s[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) s[k] = 0.0;
+  for (int64_t i = r0 + rl; i < r1; i += RL) {
+    float v[CPT];
+    load_row<CPT>(qh + i * D, v);
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) s[k] = __dadd_rn(s[k], __dmul_rn(double(v[k]), double(v[k])));
   }
-  if (i < n_q) {
-    const double a = elem64<T>(qh + i * D, c);
-    s0 = __dadd_rn(s0, __dmul_rn(a, a));
-  }
-  part[r][c] = s0 + s1;
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) sp[rl][g * CPT + k] = s[k];
   __syncthreads();
-  if (r == 0) {
-    double tot = part[0][c];
-    for (int k = 1; k < RG; ++k) tot += part[k][c];
-    float* wc = w + int64_t(h) * D + c;
-    if (n_prev > 0) tot = __dadd_rn(tot, __dmul_rn(double(*wc), double(n_prev)));
-    *wc = float(tot / double(n_prev + n_q));
+  if (threadIdx.x < D) {
+    double tot = sp[0][threadIdx.x];
+    for (int k = 1; k < RL; ++k) tot = __dadd_rn(tot, sp[k][threadIdx.x]);
+    part[(int64_t(h) * gridDim.x + b) * D + threadIdx.x] = tot;
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void query_stats_finish_kernel(const double* __restrict__ part, int nb, int64_t n_q,
+                                                               int64_t n_prev, float* __restrict__ w) {
+  const int h = blockIdx.x, c = threadIdx.x;
+  const double* ph = part + int64_t(h) * nb * D + c;
+  double tot = 0.0;
+  for (int b = 0; b < nb; ++b) tot = __dadd_rn(tot, ph[int64_t(b) * D]);
+  float* wc = w + int64_t(h) * D + c;
+  if (n_prev > 0) tot = __dadd_rn(tot, __dmul_rn(double(*wc), double(n_prev)));
+  *wc = float(tot / double(n_prev + n_q));
 }
 
 template <int D, int M>
@@ -487,19 +504,39 @@ hipError_t launch_assign_qsac(int heads, int64_t n, int dim, kvc_dtype dt, const
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_query_stats(int heads, int64_t n_q, int dim, kvc_dtype dt, const void* q, int64_t n_prev,
-                              float* w, hipStream_t st) {
-  if (heads == 0 || n_q == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(heads), 1, 1);
-#define KVC_STATS(T, D) \
-  hipLaunchKernelGGL((query_stats_kernel<T, D>), grid, dim3(1024), 0, st, static_cast<const T*>(q), n_q, n_prev, w)
-  if (dt == KVC_BF16) {
-    if (dim == 128) KVC_STATS(bf16_t, 128); else KVC_STATS(bf16_t, 64);
-  } else {
-    if (dim == 128) KVC_STATS(float, 128); else KVC_STATS(float, 64);
-  }
-#undef KVC_STATS
+int query_stats_blocks(int heads, int64_t n_q) {
+  // about 1024 workgroups in all, at most one per 256 rows
+  const int64_t want = (1024 + heads - 1) / heads;
+  const int64_t most = (n_q + 255) / 256;
+  const int64_t nb = want < most ? want : most;
+  return int(nb > 0 ? nb : 1);
+}
+
+size_t query_stats_workspace(int heads, int64_t n_q, int dim) {
+  return size_t(heads) * size_t(query_stats_blocks(heads, n_q)) * size_t(dim) * sizeof(double);
+}
+
+template <typename T, int D>
+hipError_t run_query_stats(int heads, int64_t n_q, const void* q, int64_t n_prev, float* w, double* part,
+                           hipStream_t st) {
+  const int nb = query_stats_blocks(heads, n_q);
+  const int64_t rows = (n_q + nb - 1) / nb;
+  hipLaunchKernelGGL((query_stats_partial_kernel<T, D>), dim3(unsigned(nb), unsigned(heads)), dim3(256), 0, st,
+                     static_cast<const T*>(q), n_q, rows, part);
+  hipLaunchKernelGGL((query_stats_finish_kernel<D>), dim3(unsigned(heads)), dim3(D), 0, st, part, nb, n_q, n_prev, w);
   return hipGetLastError();
+}
+
+hipError_t launch_query_stats(int heads, int64_t n_q, int dim, kvc_dtype dt, const void* q, int64_t n_prev,
+                              float* w, void* ws, hipStream_t st) {
+  if (heads == 0 || n_q == 0) return hipSuccess;
+  double* part = static_cast<double*>(ws);
+  if (dt == KVC_BF16) {
+    if (dim == 128) return run_query_stats<bf16_t, 128>(heads, n_q, q, n_prev, w, part, st);
+    return run_query_stats<bf16_t, 64>(heads, n_q, q, n_prev, w, part, st);
+  }
+  if (dim == 128) return run_query_stats<float, 128>(heads, n_q, q, n_prev, w, part, st);
+  return run_query_stats<float, 64>(heads, n_q, q, n_prev, w, part, st);
 }
 
 }  // namespace kvc

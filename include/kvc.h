@@ -132,10 +132,15 @@ kvc_status kvc_assign_qsac(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dty
 
 /* Running second moments of the queries per head and channel (QuantWM, section
  * 4.1, Eqs. 6-8, diagonal): w <- (n_prev * w + sum_i q_ic^2) / (n_prev + n_q),
- * summed in fp64.  With n_prev = 0 the previous contents of w are ignored.
- *   q   [heads][n_q][dim], dtype q_dtype;  w  [heads][dim] fp32, in/out. */
+ * summed in fp64 in a fixed order.  With n_prev = 0 the previous contents of w
+ * are ignored.
+ *   q   [heads][n_q][dim], dtype q_dtype;  w  [heads][dim] fp32, in/out.
+ *   ws  at least kvc_query_stats_workspace_bytes(...) bytes (fp64 partial sums of
+ *       blocks of queries, added in block order). */
 kvc_status kvc_query_stats(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype,
-                           const void* q, int64_t n_prev, float* w, hipStream_t stream);
+                           const void* q, int64_t n_prev, float* w, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+size_t kvc_query_stats_workspace_bytes(int32_t heads, int64_t n_q, int32_t dim);
 
 /* Principal-subspace logit compensation, PSAC (QuantWM, section 4.2, Eqs. 13-17;
  * r = 8 kept directions).

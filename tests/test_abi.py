@@ -188,12 +188,18 @@ def test_qsac_validation(lib):
 
 def test_query_stats_validation(lib):
     f = lib.kvc_query_stats
-    # (heads, n_q, dim, dt, q, n_prev, w, stream)
-    assert f(1, 10, 100, 1, P, 0, P, None) == INV
-    assert f(1, 10, 128, 9, P, 0, P, None) == INV
-    assert f(1, 10, 128, 1, P, -1, P, None) == INV
-    assert f(1, 10, 128, 1, P, 0, None, None) == INV
-    assert f(1, 0, 128, 1, None, 0, None, None) == OK
+    # (heads, n_q, dim, dt, q, n_prev, w, ws, ws_bytes, stream)
+    big = 1 << 30
+    assert f(1, 10, 100, 1, P, 0, P, P, big, None) == INV
+    assert f(1, 10, 128, 9, P, 0, P, P, big, None) == INV
+    assert f(1, 10, 128, 1, P, -1, P, P, big, None) == INV
+    assert f(1, 10, 128, 1, P, 0, None, P, big, None) == INV
+    assert f(1, 0, 128, 1, None, 0, None, None, 0, None) == OK
+    # fp64 partial sums per block of queries: 720 heads x 2 blocks, 12 heads x 19 blocks
+    assert lib.kvc_query_stats_workspace_bytes(720, 4680, 128) == 720 * 2 * 128 * 8
+    assert lib.kvc_query_stats_workspace_bytes(12, 4680, 128) == 12 * 19 * 128 * 8
+    need = lib.kvc_query_stats_workspace_bytes(12, 4680, 128)
+    assert f(12, 4680, 128, 1, P, 0, P, P, need - 1, None) == WS
 
 
 def test_route_frames_matches_oracle(lib, golden_dir):
