@@ -21,6 +21,9 @@ video generation):
   choice among the nearest centres, Eqs. 6-12, and its cold start in the
   appendix; section 4.2, PSAC, the compensation of the remaining key error
   along the principal query directions);
+* TempoKV, section 3.3 Eqs. 2-4 and "Anchor frames" (keys predicted from their
+  reconstructed history, values from the aligned reconstructed key and their
+  own history, only the residual stored) and Eq. 5 (ridge calibration): tempo.py;
 * NanoKV (2611.06377), Table 4 (256 centres each for K and V, two k-means
   iterations, one residual stage), Table 5 caption (centres fitted separately
   for K and V) and Figure 4 (mixed-dimensional attention: reduce the queries,
@@ -53,3 +56,4 @@ from .codec import (  # noqa: F401
 from .attention import attend, attend_lowdim, lse_merge, Segment  # noqa: F401
 from .qsac import assign_qsac, query_stats  # noqa: F401
 from .psac import attend_psac, psac_basis, psac_coeffs, query_moments  # noqa: F401
+from . import tempo  # noqa: F401  (predictive residual coding over frames, TempoKV)
