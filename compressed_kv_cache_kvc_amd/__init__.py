@@ -18,6 +18,8 @@ Entry points (names follow the C ABI):
   anchor_bits(k_bits, v_bits)               -> int            (anchor precision)
   query_moments(q, m, n_prev) / psac_basis(m) / psac_coeffs(...) / attend_psac(q, u, segs, coefs)
                                             (principal-subspace logit compensation)
+  tempo_encode / tempo_decode               (predictive residual coding over latent frames)
+  reconstructed_segment(k_hat, v_hat)       -> Segment        (decoded history as a 16-bit segment)
   streaming.StreamingCache                  (chunk-by-chunk composition: fit, encode, append, attend)
 """
 from __future__ import annotations
@@ -33,6 +35,7 @@ from ._lib import KvcSegment
 
 __all__ = ["KvcError", "Segment", "fit_assign", "encode", "attend", "attend_noalloc", "attend_lowdim", "lse_merge",
            "assign_qsac", "query_stats", "route_frames", "anchor_bits", "query_moments", "psac_basis",
+           "tempo_param_count", "tempo_encode", "tempo_decode", "reconstructed_segment",
            "psac_coeffs", "attend_psac", "library", "version"]
 
 
@@ -166,6 +169,85 @@ def route_frames(n_frames: int, n_recent: int, period: int = 0, n_sink: int = 0,
 
 def anchor_bits(k_bits: int, v_bits: int) -> int:
     return int(library().kvc_anchor_bits(k_bits, v_bits))
+
+
+# ------------------------------------------------------------------------------ predictive residual codec
+def tempo_param_count(dim: int) -> int:
+    return int(library().kvc_tempo_param_count(dim))
+
+
+def _tempo_state(H: int, S: int, d: int, state: Optional[torch.Tensor], first_frame: int, device):
+    if state is None:
+        if first_frame > 0:
+            raise ValueError("frames after the anchor need the state the previous call left")
+        state = torch.zeros(H, S, 3, d, dtype=torch.float32, device=device)
+    _need(state, "state", device, torch.float32, (H, S, 3, d))
+    return state
+
+
+def tempo_encode(k: torch.Tensor, v: torch.Tensor, params: torch.Tensor, first_frame: int, frame_tokens: int,
+                 k_bits: int, v_bits: int, group: int, state: Optional[torch.Tensor] = None):
+    """Predictive residual coding of the frames first_frame, ... of k, v [H, n*S, d]
+    (params [H, P] fp32).  Returns (k_codes, k_meta, v_codes, v_meta, state); the
+    state [H, S, 3, d] fp32 is updated in place (allocated for the anchor call)."""
+    _need(k, "k")
+    H, N, d = k.shape
+    _need(v, "v", k.device, k.dtype, (H, N, d))
+    _need(params, "params", k.device, torch.float32, (H, tempo_param_count(d)))
+    S = frame_tokens
+    if S <= 0 or N % S:
+        raise ValueError("tokens must be whole frames of frame_tokens tokens")
+    state = _tempo_state(H, S, d, state, first_frame, k.device)
+    dev = k.device
+    kc = torch.empty(H, N, d * k_bits // 8, dtype=torch.uint8, device=dev)
+    vc = torch.empty(H, N, d * v_bits // 8, dtype=torch.uint8, device=dev)
+    km = torch.empty(H, N, d // group, 2, dtype=torch.uint16, device=dev)
+    vm = torch.empty(H, N, d // group, 2, dtype=torch.uint16, device=dev)
+    _check(library().kvc_tempo_encode(H, S, first_frame, N // S, d, _dtype_code(k), _ptr(k), _ptr(v), _ptr(params),
+                                      k_bits, v_bits, group, _ptr(kc), _ptr(km), _ptr(vc), _ptr(vm), _ptr(state),
+                                      _stream(dev)))
+    return kc, km, vc, vm, state
+
+
+def tempo_decode(k_codes: torch.Tensor, k_meta: torch.Tensor, v_codes: torch.Tensor, v_meta: torch.Tensor,
+                 params: torch.Tensor, first_frame: int, frame_tokens: int, k_bits: int, v_bits: int, group: int,
+                 state: Optional[torch.Tensor] = None, k_hat: Optional[torch.Tensor] = None,
+                 v_hat: Optional[torch.Tensor] = None):
+    """Reconstruct the frames a tempo_encode call coded.  Returns (k_hat, v_hat,
+    state): fp16 [H, n*S, d] reconstructions and the state (updated in place)."""
+    _need(k_codes, "k_codes")
+    H, N, _ = k_codes.shape
+    dev = k_codes.device
+    d = k_codes.shape[2] * 8 // k_bits
+    _need(params, "params", dev, torch.float32, (H, tempo_param_count(d)))
+    _need(k_codes, "k_codes", dev, torch.uint8, (H, N, d * k_bits // 8))
+    _need(v_codes, "v_codes", dev, torch.uint8, (H, N, d * v_bits // 8))
+    _need(k_meta, "k_meta", dev, torch.uint16, (H, N, d // group, 2))
+    _need(v_meta, "v_meta", dev, torch.uint16, (H, N, d // group, 2))
+    S = frame_tokens
+    if S <= 0 or N % S:
+        raise ValueError("tokens must be whole frames of frame_tokens tokens")
+    state = _tempo_state(H, S, d, state, first_frame, dev)
+    k_hat = k_hat if k_hat is not None else torch.empty(H, N, d, dtype=torch.float16, device=dev)
+    v_hat = v_hat if v_hat is not None else torch.empty(H, N, d, dtype=torch.float16, device=dev)
+    _need(k_hat, "k_hat", dev, torch.float16, (H, N, d))
+    _need(v_hat, "v_hat", dev, torch.float16, (H, N, d))
+    _check(library().kvc_tempo_decode(H, S, first_frame, N // S, d, _ptr(params), k_bits, v_bits, group,
+                                      _ptr(k_codes), _ptr(k_meta), _ptr(v_codes), _ptr(v_meta), _ptr(state),
+                                      _ptr(k_hat), _ptr(v_hat), _stream(dev)))
+    return k_hat, v_hat, state
+
+
+def reconstructed_segment(k_hat: torch.Tensor, v_hat: torch.Tensor) -> "Segment":
+    """A history segment holding reconstructed K and V (fp16 [H, n, d]) as 16-bit
+    residuals over a zero centre table (one centre, all ids 0), which attend()
+    reads unchanged."""
+    H, N, d = k_hat.shape
+    dev = k_hat.device
+    ids = torch.zeros(H, N, dtype=torch.uint8, device=dev)
+    zero = torch.zeros(H, 1, d, dtype=torch.bfloat16, device=dev)
+    return Segment(k_hat.view(torch.uint8).view(H, N, 2 * d), None, ids, zero,
+                   v_hat.view(torch.uint8).view(H, N, 2 * d), None, ids, zero, 16, 16, 16)
 
 
 # ------------------------------------------------------------------------------ encode

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvc.so")
 
-SOURCES = ["api.cpp", "encode.hip", "assign.hip", "attend.hip", "merge.hip", "qsac.hip", "psac.hip"]
+SOURCES = ["api.cpp", "encode.hip", "assign.hip", "attend.hip", "merge.hip", "qsac.hip", "psac.hip", "tempo.hip"]
 
 COMMON = [
     "-x", "hip", "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
@@ -29,7 +29,7 @@ COMMON = [
 # rounded fp32 operations
 # the assignment kernel reads every score with vector instructions: its matrix
 # products accumulate in ordinary VGPRs (no accumulation-register copies)
-PER_FILE = {"encode.hip": ["-ffp-contract=off"], "api.cpp": ["-ffp-contract=off"],
+PER_FILE = {"encode.hip": ["-ffp-contract=off"], "api.cpp": ["-ffp-contract=off"], "tempo.hip": ["-ffp-contract=off"],
             "assign.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 

@@ -418,6 +418,83 @@ kvc_status kvc_encode(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt
   }
 }
 
+// ------------------------------------------------------------------------------ predictive residual codec
+int32_t kvc_tempo_param_count(int32_t dim) { return dim > 0 ? 7 * dim + dim * dim : 0; }
+
+namespace {
+kvc_status tempo_check(int32_t heads, int32_t frame_tokens, int32_t first_frame, int32_t n_frames, int32_t dim,
+                       int32_t k_bits, int32_t v_bits, int32_t group, const float* params, const void* k_codes,
+                       const void* k_meta, const void* v_codes, const void* v_meta, const float* state) {
+  KVC_REQUIRE(heads >= 0 && frame_tokens >= 0 && n_frames >= 0 && first_frame >= 0, KVC_ERR_INVALID_ARG,
+              "heads, frame_tokens, n_frames and first_frame must be >= 0");
+  KVC_REQUIRE(dim == 64 || dim == 128, KVC_ERR_INVALID_ARG, "dim must be 64 or 128");
+  KVC_REQUIRE((k_bits == 2 || k_bits == 4) && (v_bits == 2 || v_bits == 4), KVC_ERR_INVALID_ARG,
+              "k_bits and v_bits must be 2 or 4");
+  KVC_REQUIRE(group > 0 && dim % group == 0, KVC_ERR_INVALID_ARG, "group must divide dim");
+  KVC_REQUIRE(group == 16 || group == 32, KVC_ERR_UNSUPPORTED, "group must be 16 or 32");
+  KVC_REQUIRE(first_frame > 0 || n_frames <= 1, KVC_ERR_INVALID_ARG,
+              "the anchor frame (first_frame = 0) is coded alone: n_frames must be 1");
+  KVC_REQUIRE(first_frame > 0 || (k_bits == 4 && v_bits == 4), KVC_ERR_INVALID_ARG,
+              "the anchor frame is coded at max(4, b_K, b_V) = 4 bits");
+  KVC_REQUIRE(heads <= 65535, KVC_ERR_UNSUPPORTED, "at most 65535 heads per call");
+  KVC_REQUIRE(int64_t(n_frames) * frame_tokens <= (int64_t(1) << 26), KVC_ERR_UNSUPPORTED,
+              "at most 2^26 tokens per head and call");
+  const bool work = heads > 0 && frame_tokens > 0 && n_frames > 0;
+  KVC_PTR(params, work, "params");
+  KVC_PTR(k_codes, work, "k_codes");
+  KVC_PTR(k_meta, work, "k_meta");
+  KVC_PTR(v_codes, work, "v_codes");
+  KVC_PTR(v_meta, work, "v_meta");
+  KVC_PTR(state, work, "state");
+  return ok();
+}
+}  // namespace
+
+kvc_status kvc_tempo_encode(int32_t heads, int32_t frame_tokens, int32_t first_frame, int32_t n_frames, int32_t dim,
+                            kvc_dtype dt, const void* k, const void* v, const float* params, int32_t k_bits,
+                            int32_t v_bits, int32_t group, uint8_t* k_codes, uint16_t* k_meta, uint8_t* v_codes,
+                            uint16_t* v_meta, float* state, hipStream_t stream) {
+  try {
+    kvc_status st = tempo_check(heads, frame_tokens, first_frame, n_frames, dim, k_bits, v_bits, group, params,
+                                k_codes, k_meta, v_codes, v_meta, state);
+    if (st != KVC_OK) return st;
+    KVC_REQUIRE(valid_dtype(dt), KVC_ERR_INVALID_ARG, "bad dtype");
+    const bool work = heads > 0 && frame_tokens > 0 && n_frames > 0;
+    KVC_PTR(k, work, "k");
+    KVC_PTR(v, work, "v");
+    if (!work) return ok();
+    return hip_status(kvc::launch_tempo(false, heads, frame_tokens, first_frame, n_frames, dim, dt, k, v, params,
+                                        k_bits, v_bits, group, k_codes, k_meta, v_codes, v_meta, state, nullptr,
+                                        nullptr, stream),
+                      "tempo encode");
+  } catch (...) {
+    return fail(KVC_ERR_HIP, "unexpected exception in kvc_tempo_encode");
+  }
+}
+
+kvc_status kvc_tempo_decode(int32_t heads, int32_t frame_tokens, int32_t first_frame, int32_t n_frames, int32_t dim,
+                            const float* params, int32_t k_bits, int32_t v_bits, int32_t group,
+                            const uint8_t* k_codes, const uint16_t* k_meta, const uint8_t* v_codes,
+                            const uint16_t* v_meta, float* state, uint16_t* k_hat, uint16_t* v_hat,
+                            hipStream_t stream) {
+  try {
+    kvc_status st = tempo_check(heads, frame_tokens, first_frame, n_frames, dim, k_bits, v_bits, group, params,
+                                k_codes, k_meta, v_codes, v_meta, state);
+    if (st != KVC_OK) return st;
+    const bool work = heads > 0 && frame_tokens > 0 && n_frames > 0;
+    KVC_PTR(k_hat, work, "k_hat");
+    KVC_PTR(v_hat, work, "v_hat");
+    if (!work) return ok();
+    return hip_status(kvc::launch_tempo(true, heads, frame_tokens, first_frame, n_frames, dim, KVC_BF16, nullptr,
+                                        nullptr, params, k_bits, v_bits, group, const_cast<uint8_t*>(k_codes),
+                                        const_cast<uint16_t*>(k_meta), const_cast<uint8_t*>(v_codes),
+                                        const_cast<uint16_t*>(v_meta), state, k_hat, v_hat, stream),
+                      "tempo decode");
+  } catch (...) {
+    return fail(KVC_ERR_HIP, "unexpected exception in kvc_tempo_decode");
+  }
+}
+
 // ------------------------------------------------------------------------------ attention
 size_t kvc_attend_workspace_bytes(int32_t heads, int64_t n_q, int32_t dim, kvc_dtype q_dtype,
                                   const kvc_segment* segs, int32_t n_segs) {

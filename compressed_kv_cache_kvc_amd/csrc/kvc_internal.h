@@ -110,6 +110,15 @@ hipError_t launch_attend_lowdim(int heads, int64_t n_q, int dim, int rank,
                                 const SegList& segs, int k_bits, int v_bits, int group,
                                 int n_split, float* out, float* lse, hipStream_t st);
 
+// Predictive residual codec over latent frames (encode, or decode to fp16
+// reconstructions); k/v are read only when encoding, k_hat/v_hat written only
+// when decoding; the state [heads][S][3][dim] fp32 is read when first_frame > 0
+// and written at the end.
+hipError_t launch_tempo(bool decode, int heads, int S, int first_frame, int n_frames, int dim, kvc_dtype dt,
+                        const void* k, const void* v, const float* prm, int kb, int vb, int g, uint8_t* k_codes,
+                        uint16_t* k_meta, uint8_t* v_codes, uint16_t* v_meta, float* state, uint16_t* k_hat,
+                        uint16_t* v_hat, hipStream_t st);
+
 // Split plan shared by the dispatcher and the workspace-size queries.
 int attend_split_plan(int heads, int64_t n_q, int64_t total_tiles, int rows_per_block);
 

@@ -185,6 +185,47 @@ kvc_status kvc_route_frames(int32_t n_frames, int32_t n_recent, int32_t period, 
 /* Anchor precision (TempoKV, section 3.3 and Table 7): b_a = max(4, b_K, b_V). */
 int32_t kvc_anchor_bits(int32_t k_bits, int32_t v_bits);
 
+/* Predictive residual coding over latent frames (TempoKV, section 3.3, Eqs. 2-4
+ * and "Anchor frames").  A head's tokens are frames of frame_tokens = S spatial
+ * tokens, token f*S + s being spatial token s of frame f of the call; a call
+ * codes frames first_frame .. first_frame + n_frames - 1.  Per token and frame t:
+ *   keys (Eq. 3):    K~ = beta_K + A1 (.) K^[t-1] + A2 (.) K^[t-2]; frame 1 uses its
+ *                    own (beta_K1, A_K1) and no A2 term; the anchor frame 0 has K~ = 0;
+ *   values (Eq. 4):  V~ = beta_V + W K^[t] + A_V (.) V^[t-1]; frame 0 has V~ = 0;
+ *   both (Eq. 2):    r = x - x~ quantized by the group quantizer of kvc_encode
+ *                    (fp16 scale rounded up, fp16 zero-point rounded down, codes
+ *                    and metadata laid out as for kvc_encode), x^ = x~ + (q*s + z).
+ * fp32 arithmetic in one fixed order, no fused multiply-add: x~ of a key is
+ * ((beta + A1*k1) + A2*k2); the W term adds W[c][j]*K^[j] for j ascending to beta_V,
+ * then A_V*v1 is added; r = x - x~; x^ = x~ + (q*s + z).
+ *   params   [heads][kvc_tempo_param_count(dim)] fp32 per head: beta_K1, A_K1,
+ *            beta_K2, A_K21, A_K22, beta_V, A_V (dim values each), then W row-major
+ *            (W[c][j] multiplies K^[j] into channel c), e.g. fitted offline by ridge
+ *            regression (TempoKV, Eq. 5).
+ *   state    [heads][S][3][dim] fp32: K^[f-1], K^[f-2], V^[f-1] before the call's
+ *            first frame f (read when first_frame > 0, ignored for the anchor);
+ *            overwritten with the same three rows after its last frame, so
+ *            consecutive calls continue the sequence.
+ *   The anchor frame is coded alone (first_frame = 0 needs n_frames = 1) at
+ *   b_a = max(4, b_K, b_V) = 4 bits: k_bits = v_bits = 4 in that call.
+ * kvc_tempo_encode: k, v [heads][n_frames*S][dim] (dtype dt) -> k_codes/v_codes
+ *   [heads][n_frames*S][dim*bits/8], k_meta/v_meta [heads][n_frames*S][dim/group][2].
+ * kvc_tempo_decode: the same codes (and the same state before the call) ->
+ *   k_hat, v_hat [heads][n_frames*S][dim] as fp16 bit patterns (x^ rounded to
+ *   nearest), bit for bit the encoder's reconstruction; the result reads through
+ *   kvc_attend as a 16-bit residual segment over a zero centre table.
+ * dim 64 or 128; bits 2 or 4; group 16 or 32.  No workspace. */
+int32_t kvc_tempo_param_count(int32_t dim);
+kvc_status kvc_tempo_encode(int32_t heads, int32_t frame_tokens, int32_t first_frame, int32_t n_frames,
+                            int32_t dim, kvc_dtype dt, const void* k, const void* v, const float* params,
+                            int32_t k_bits, int32_t v_bits, int32_t group, uint8_t* k_codes, uint16_t* k_meta,
+                            uint8_t* v_codes, uint16_t* v_meta, float* state, hipStream_t stream);
+kvc_status kvc_tempo_decode(int32_t heads, int32_t frame_tokens, int32_t first_frame, int32_t n_frames,
+                            int32_t dim, const float* params, int32_t k_bits, int32_t v_bits, int32_t group,
+                            const uint8_t* k_codes, const uint16_t* k_meta, const uint8_t* v_codes,
+                            const uint16_t* v_meta, float* state, uint16_t* k_hat, uint16_t* v_hat,
+                            hipStream_t stream);
+
 /* Encode tokens against their centres (TempoKV, section 3.1 Eq. 1 and section
  * 3.3 Eq. 2).  Per token: r = fl32(x - c[id]); with a basis, r is replaced by
  * its coefficients a_k = sum_i fl32(U[i][k] * r[i]) accumulated in fp32 over

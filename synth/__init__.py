@@ -14,6 +14,7 @@ from .configs import CONFIGS, Config, get_config  # noqa: F401
 from .gen import (  # noqa: F401
     AR1Stream,
     bf16_bits_to_f32,
+    coupled_values,
     forgy_init,
     one_per_label_init,
     orthonormal_basis,

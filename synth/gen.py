@@ -140,3 +140,15 @@ def orthonormal_basis(heads: int, dim: int, rank: int, seed: int) -> torch.Tenso
     sign = torch.sign(torch.diagonal(R, dim1=-2, dim2=-1))
     sign[sign == 0] = 1.0
     return (Q * sign[:, None, :]).float().contiguous()
+
+
+def coupled_values(k: torch.Tensor, v_chain: torch.Tensor, seed: int, mix: float = 0.6) -> torch.Tensor:
+    """Values that depend on the aligned key: V = mix * K M^T + sqrt(1 - mix^2) * V_chain,
+    rounded to bf16, with M a seeded orthogonal d x d matrix per head and V_chain an
+    independent value chain (e.g. AR1Stream(cfg, "v")).  Stands in for the
+    key-to-value dependence TempoKV measures (section 3.2: the aligned key is a
+    strong predictor of the value)."""
+    H, N, d = k.shape
+    M = orthonormal_basis(H, d, d, seed).to(k.device)
+    mixed = mix * torch.bmm(k.float(), M.transpose(1, 2).contiguous()) + math.sqrt(1.0 - mix * mix) * v_chain.float()
+    return mixed.to(torch.bfloat16).contiguous()
