@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--anchor", action="store_true",
                     help="larger_backbone: code the oldest frame, when read at full dimension, at "
                          "max(4, k_bits, v_bits) bits (TempoKV section 3.3)")
+    ap.add_argument("--tempo", action="store_true",
+                    help="self_forcing_layer coded by predictive residuals over its latent frames (TempoKV "
+                         "section 3.3): encode, decode and attention over the decoded history")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the warmup, run one plain fp32 negation of MIB MiB (reads and writes MIB MiB) so "
                          "that a hardware-counter run can scale its byte counters against a kernel of known traffic")
@@ -475,6 +478,61 @@ class Streaming(Workload):
         self.qsac = m
 
 
+class TempoLayer(Workload):
+    """self_forcing_layer coded by predictive residuals over its six latent frames
+    (TempoKV section 3.3): the anchor frame alone at 4 bits, then frames 1-5 at
+    the layer's k_bits / v_bits; the step encodes, decodes the fp16
+    reconstructions and attends over them (a 16-bit segment over a zero centre).
+    Values depend on the aligned key (synth.coupled_values).  The predictor
+    coefficients are seeded draws of plausible size (temporal gains below 1, a
+    dense key-to-value map); their fitted values would not change the work."""
+
+    def __init__(self, cfg, dev):
+        super().__init__(cfg, dev)
+        torch, synth = self.torch, self.synth
+        import compressed_kv_cache_kvc_amd as kvc
+        H, N, d = cfg.heads, cfg.hist, cfg.dim
+        self.S = cfg.frame_tokens
+        self.T = N // self.S
+        self.k = synth.AR1Stream(cfg, "k", device=dev).tokens(N)
+        self.v = synth.coupled_values(self.k, synth.AR1Stream(cfg, "v", device=dev).tokens(N),
+                                      synth.seed_for(cfg.seed, 0, 1, 2))
+        self.q = synth.queries(cfg, device=dev)
+        g = torch.Generator(device="cpu").manual_seed(synth.seed_for(cfg.seed, 0, 0, 5))
+        u = lambda lo, hi: lo + (hi - lo) * torch.rand(H, d, generator=g)   # noqa: E731
+        z = lambda: 0.05 * torch.randn(H, d, generator=g)                   # noqa: E731
+        w = 0.6 * torch.randn(H, d, d, generator=g) / math.sqrt(d)
+        self.params = torch.cat([z(), u(0.6, 1.0), z(), u(0.4, 0.9), u(-0.2, 0.3), z(), u(0.0, 0.6),
+                                 w.reshape(H, d * d)], dim=1).float().contiguous().to(dev)
+        assert self.params.shape[1] == kvc.tempo_param_count(d)
+        self.k0, self.k1 = self.k[:, :self.S].contiguous(), self.k[:, self.S:].contiguous()
+        self.v0, self.v1 = self.v[:, :self.S].contiguous(), self.v[:, self.S:].contiguous()
+        self.anchor_bits = kvc.anchor_bits(cfg.k_bits, cfg.v_bits)
+        self.attn_flops = 4.0 * H * cfg.n_q * N * d
+        self.enc_tokens = H * N
+        self.enc_bytes = H * N * (d * 2 * 2) + H * self.S * 2 * (d * self.anchor_bits // 8 + 4 * d // cfg.group) + \
+            H * (N - self.S) * (d * (cfg.k_bits + cfg.v_bits) // 8 + 8 * d // cfg.group)
+
+    def step(self):
+        import compressed_kv_cache_kvc_amd as kvc
+        cfg, S, P = self.cfg, self.S, self.params
+        ba, g = self.anchor_bits, cfg.group
+        e0 = self.ev()
+        a = kvc.tempo_encode(self.k0, self.v0, P, 0, S, ba, ba, g)
+        b = kvc.tempo_encode(self.k1, self.v1, P, 1, S, cfg.k_bits, cfg.v_bits, g, a[4])
+        e1 = self.ev()
+        kh0, vh0, st = kvc.tempo_decode(a[0], a[1], a[2], a[3], P, 0, S, ba, ba, g)
+        kh1, vh1, _ = kvc.tempo_decode(b[0], b[1], b[2], b[3], P, 1, S, cfg.k_bits, cfg.v_bits, g, st)
+        e2 = self.ev()
+        # the anchor frame and the predicted frames: two 16-bit segments, one launch
+        out, lse = kvc.attend(self.q, [kvc.reconstructed_segment(kh0, vh0), kvc.reconstructed_segment(kh1, vh1)])
+        e3 = self.ev()
+        self.mark("tempo_encode", e0, e1)
+        self.mark("tempo_decode", e1, e2)
+        self.mark("attend", e2, e3)
+        return out
+
+
 def make_workload(cfg, dev, route=None, anchor=False):
     if cfg.name == "larger_backbone":
         if route is not None or anchor:
@@ -486,6 +544,30 @@ def make_workload(cfg, dev, route=None, anchor=False):
 
 
 # ------------------------------------------------------------------------------ CPU oracle baseline
+def cpu_baseline_tempo(cfg):
+    """The oracle's predictive residual codec (oracle/tempo.py) on one head of the
+    layer: encode of its six frames (anchor, then five), timed as tokens/s."""
+    import numpy as np
+    import oracle
+    import synth
+    S = cfg.frame_tokens
+    k = synth.AR1Stream(cfg, "k", heads=1).tokens(cfg.hist)
+    v = synth.coupled_values(k, synth.AR1Stream(cfg, "v", heads=1).tokens(cfg.hist), synth.seed_for(cfg.seed, 0, 1, 2))
+    kn, vn = k[0].float().numpy(), v[0].float().numpy()
+    rng = np.random.default_rng(cfg.seed)
+    d = cfg.dim
+    P = oracle.tempo.join_params(0.05 * rng.standard_normal(d), rng.uniform(0.6, 1.0, d), 0.05 * rng.standard_normal(d),
+                                 rng.uniform(0.4, 0.9, d), rng.uniform(-0.2, 0.3, d), 0.05 * rng.standard_normal(d),
+                                 rng.uniform(0.0, 0.6, d), 0.6 * rng.standard_normal((d, d)) / np.sqrt(d))
+    ba = oracle.tempo.anchor_bits(cfg.k_bits, cfg.v_bits)
+    t0 = time.perf_counter()
+    a = oracle.tempo.encode_frames(kn[:S], vn[:S], P, 0, S, ba, ba, cfg.group)
+    oracle.tempo.encode_frames(kn[S:], vn[S:], P, 1, S, cfg.k_bits, cfg.v_bits, cfg.group, a[6])
+    dt = time.perf_counter() - t0
+    return {"tempo_encode_tokens_per_s": cfg.hist / dt,
+            "tempo_sample": f"oracle predictive encode of 1 head x {cfg.hist // S} frames x {S} tokens"}
+
+
 def cpu_baseline(cfg, budget_s):
     """Time the oracle (as it stands) on a bounded sample of the workload: the
     fp64 attention of all queries over the history the timed step attends, head
@@ -613,7 +695,12 @@ def main():
         raise SystemExit("--route takes RECENT,PERIOD,SINK,ALL_FULL_UNTIL")
     if (route is not None or args.anchor) and cfg.name != "larger_backbone":
         raise SystemExit("--route and --anchor apply to the larger_backbone workload")
-    w = make_workload(cfg, dev, route, args.anchor)
+    if args.tempo:
+        if cfg.name != "self_forcing_layer":
+            raise SystemExit("--tempo covers the self_forcing_layer workload")
+        w = TempoLayer(cfg, dev)
+    else:
+        w = make_workload(cfg, dev, route, args.anchor)
     if args.psac:
         if not hasattr(w, "enable_psac"):
             raise SystemExit("--psac covers the single-segment workloads (self_forcing_layer, streaming)")
@@ -710,6 +797,27 @@ def main():
                           "scores_per_s": round(scores / (lowdim_ms * 1e-3), 1),
                           "exp_peak_per_s": exp_peak,
                           "exp_bound_frac": round(scores / (lowdim_ms * 1e-3) / exp_peak, 4)}
+    if isinstance(w, TempoLayer):
+        # the predictions cost 2*d*d FLOP per value token (W K_hat, multiply and add
+        # rounded separately) plus 6*d for the key and the temporal terms; the
+        # reference rate of separately rounded fp32 operations is one per lane and
+        # clock: 256 CUs x 64 lanes x 2.4 GHz = 39.3 TFLOP/s
+        te = phases.get("tempo_encode", 0.0) / K * 1e-3
+        td = phases.get("tempo_decode", 0.0) / K * 1e-3
+        pred_tokens = cfg.heads * (cfg.hist - w.S)
+        pred_flop = pred_tokens * (2.0 * cfg.dim * cfg.dim + 6.0 * cfg.dim)
+        valu_peak = 256 * 64 * 2.4e9
+        line["config"]["codec"] = "tempo"
+        line["config"]["anchor_bits"] = w.anchor_bits
+        line["phase_ms"]["tempo_encode"] = round(te * 1e3, 4)
+        line["phase_ms"]["tempo_decode"] = round(td * 1e3, 4)
+        line["tempo"] = {"encode_tokens_per_s": round(w.enc_tokens / te, 1) if te else None,
+                         "decode_tokens_per_s": round(w.enc_tokens / td, 1) if td else None,
+                         "encode_GBps": round(w.enc_bytes / te / 1e9, 1) if te else None,
+                         "prediction_TFLOPs_encode": round(pred_flop / te / 1e12, 3) if te else None,
+                         "prediction_TFLOPs_decode": round(pred_flop / td / 1e12, 3) if td else None,
+                         "valu_peak_TFLOPs": valu_peak / 1e12,
+                         "encode_valu_frac": round(pred_flop / te / valu_peak, 4) if te else None}
     if w.psac:
         for name in ("psac_coeffs", "query_moments", "psac_basis"):
             line["phase_ms"][name] = round(phases.get(name, 0.0) / K, 4)
@@ -726,6 +834,8 @@ def main():
                         "read_GBps": round(qtok * cfg.dim * (4 if cfg.dtype == "f32" else 2) / qs / 1e9, 1) if qs else None}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        if isinstance(w, TempoLayer):
+            line["cpu_baseline"].update(cpu_baseline_tempo(cfg))
     print(json.dumps(line), flush=True)
 
 
