@@ -138,7 +138,7 @@ __device__ __forceinline__ void load_codes(const uint8_t* row, int lane, uint32_
 }
 
 template <typename T, int D, int KB, int VB, int G, bool DECODE>
-__global__ __launch_bounds__(64 * kTempoWaves) void tempo_kernel(TempoArgs a) {
+__global__ __launch_bounds__(64 * kTempoWaves, 8) void tempo_kernel(TempoArgs a) {
   constexpr int PER = D / 64;
   constexpr int NP = 7 * D + D * D;
   __shared__ float sWt[D * D];                       // sWt[j * D + c] = W[c][j]
