@@ -306,9 +306,11 @@ class LargerBackbone(Workload):
         vidf, vidr = vid[:, :F].contiguous(), vid[:, F:].contiguous()
         krc, krm, _ = kvc.encode(self.kr, kc, cfg.k_bits, cfg.group, ids=kidr)
         vrc, vrm, _ = kvc.encode(self.vr, vc, cfg.v_bits, cfg.group, ids=vidr)
+        e1b = self.ev()
         kfc, kfm, _ = kvc.encode(self.kf, kc, cfg.k_bits, cfg.group, ids=kidf, basis=self.Uk)
         vfc, vfm, _ = kvc.encode(self.vf, vc, cfg.v_bits, cfg.group, ids=vidf, basis=self.Uv)
         e2 = self.ev()
+        self.mark("encode_lowdim", e1b, e2)
         recent = kvc.Segment(krc, krm, kidr, kc, vrc, vrm, vidr, vc, cfg.k_bits, cfg.v_bits, cfg.group)
         far = kvc.Segment(kfc, kfm, kidf, kc, vfc, vfm, vidf, vc, cfg.k_bits, cfg.v_bits, cfg.group, rank=cfg.rank)
         o1, l1 = kvc.attend(self.q, [recent])
@@ -797,6 +799,20 @@ def main():
                           "scores_per_s": round(scores / (lowdim_ms * 1e-3), 1),
                           "exp_peak_per_s": exp_peak,
                           "exp_bound_frac": round(scores / (lowdim_ms * 1e-3) / exp_peak, 4)}
+        # the low-dim encode of the far part (K and V): a = U^T r with every
+        # multiply and add rounded separately (2*d*r vector operations per token,
+        # no fused multiply-add, so no packed or matrix unit applies); its bound is
+        # one fp32 operation per lane and clock: 256 CUs x 64 lanes x 2.4 GHz
+        el = phases.get("encode_lowdim", 0.0) / K * 1e-3
+        if el > 0:
+            ops = 2.0 * cfg.heads * w.low_tokens * 2.0 * cfg.dim * cfg.rank
+            valu_peak = 256 * 64 * 2.4e9
+            line["phase_ms"]["encode_lowdim"] = round(el * 1e3, 4)
+            line["encode_lowdim"] = {"ms": round(el * 1e3, 4),
+                                     "tokens_per_s": round(2.0 * cfg.heads * w.low_tokens / el, 1),
+                                     "valu_TOPs": round(ops / el / 1e12, 3),
+                                     "valu_peak_TOPs": valu_peak / 1e12,
+                                     "valu_frac": round(ops / el / valu_peak, 4)}
     if isinstance(w, TempoLayer):
         # the predictions cost 2*d*d FLOP per value token (W K_hat, multiply and add
         # rounded separately) plus 6*d for the key and the temporal terms; the
