@@ -9,8 +9,9 @@
 // exactly -1/2 of the one for ||c||^2 - 2 x.c and so is its rounding error).  Each
 // lane keeps the best score, its index and the second-best score.  When the top-2
 // gap is not larger than a bound on the fp32 rounding error of the scores, the
-// token is re-scored exactly: fp64 sums of (x_i - c_i)^2 over all centres, ties to
-// the lowest index.  fp32 tokens always take that fp64 path.
+// token is re-scored exactly: fp64 sums of (x_i - c_i)^2 over the centres whose
+// score lies within the bound of the best, ties to the lowest index.  fp32 tokens
+// always take an fp64 path over all centres.
 #include "kvc_internal.h"
 #include "dev_common.h"
 #include "mfma.h"
@@ -24,6 +25,16 @@ __device__ __forceinline__ float sq2_bf16(uint32_t w, float acc) {
   typedef __bf16 b2 __attribute__((ext_vector_type(2)));
   const b2 v = __builtin_bit_cast(b2, w);
   return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+}
+
+// max(a, b) as one v_max_f32: a key (a score with index bits in its low mantissa
+// bits) is built by integer operations, and fmaxf would first canonicalize it as
+// a possible signalling NaN, one more instruction per score.  NaN keys need no
+// care: a token with a non-finite value fails the gap test through its bound.
+__device__ __forceinline__ float key_max(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 // Exact fp64 squared distance between a token row (global) and a centre row.
@@ -83,18 +94,21 @@ __global__ __launch_bounds__(256) void assign_exact_kernel(const T* __restrict__
 }
 
 
+constexpr int kFlagCap = 128;          // flagged tokens a wavefront holds before resolving them
+
 // A workgroup stages its head's centre table once and then scores `rounds`
 // consecutive blocks of 256 tokens against it (the launch picks the number of
 // rounds so that the table staging is amortized while the grid still fills the
 // chip).
 template <int D>
-__global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ cent,
+__global__ __launch_bounds__(256, 2) void assign_mfma_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ cent,
                                                           int C, int64_t n, int rounds, uint8_t* __restrict__ ids) {
   constexpr int ROWP = D + 8;          // padded LDS row (bf16 elements): conflict-free fragment reads
   constexpr int KC = D / 16;
   __shared__ __attribute__((aligned(16))) uint16_t sC[256 * ROWP];
   __shared__ __attribute__((aligned(16))) float sN[256];
-  __shared__ __attribute__((aligned(16))) uint16_t sX[4][D];   // a flagged token's row, per wavefront
+  __shared__ int sFt[4][kFlagCap];     // per wavefront: flagged tokens waiting for the exact pass
+  __shared__ float sFl[4][kFlagCap];   // and their candidate limits (best score - bound)
 
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
@@ -129,9 +143,10 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
   }
   __syncthreads();
   // -||c||^2 / 2 with ||c||^2 in fp32, channel pairs in order (v_dot2_f32_bf16);
-  // padding rows score -inf
+  // padding rows score -FLT_MAX (finite: their keys, with index bits in the low
+  // mantissa bits, must not turn into NaNs as -inf would)
   {
-    float sn = -INFINITY;
+    float sn = -3.40282347e+38f;
     if (tid < C) {
       sn = 0.f;
 #pragma unroll
@@ -153,10 +168,110 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, off, 64));
 
-  for (int round = 0; round < rounds; ++round) {
-  // token fragments (B operand) and ||x||^2
+  // The flagged-token pass: tokens whose top-2 gap is within the rounding bound
+  // wait in a per-wavefront LDS list; when the list could not take another
+  // round's tokens, and after the last round, they are resolved 32 at a time: one
+  // more scoring pass over all centres (the same products, so the same fp32
+  // scores) marks each token's candidates, and every lane pair re-scores its
+  // token's candidates in fp64 (each lane over its 64 dimensions, the two halves
+  // added in a fixed order), ties to the lowest index.
+  auto flush = [&](int nfl) {
+    for (int base = 0; base < nfl; base += 32) {
+      const int k = base + col;
+      const bool has = k < nfl;
+      const int64_t t = sFt[wave][has ? k : base];
+      const float lim = has ? sFl[wave][k] : __builtin_nanf("");   // no candidates for idle lanes
+      bf16x8 xf[KC];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        xf[kc] = as_bf16x8(*reinterpret_cast<const uint4*>(x + (int64_t(h) * n + t) * D + kc * 16 + half * 8));
+      uint32_t cm[8];                 // candidate bits of block blk: 16 per lane (this lane's rows)
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) cm[blk] = 0;
+      // two blocks at a time (two independent accumulation chains); the second of
+      // a pair past the last block reads rows of the 256-row table that are never
+      // used and is discarded
+#pragma unroll
+      for (int bp = 0; bp < 4; ++bp) {
+        if (2 * bp >= nblk) break;
+        f32x16 acc[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const float4 tt = *reinterpret_cast<const float4*>(&sN[(2 * bp + u) * 32 + 8 * g4 + 4 * half]);
+            acc[u][4 * g4 + 0] = tt.x; acc[u][4 * g4 + 1] = tt.y; acc[u][4 * g4 + 2] = tt.z; acc[u][4 * g4 + 3] = tt.w;
+          }
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const bf16x8 a = as_bf16x8(
+                *reinterpret_cast<const uint4*>(&sC[((2 * bp + u) * 32 + col) * ROWP + kc * 16 + half * 8]));
+            acc[u] = mfma32(a, xf[kc], acc[u]);
+          }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          uint32_t bits = 0;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) bits |= (acc[u][v] >= lim ? 1u : 0u) << v;
+          if (2 * bp + u < nblk) cm[2 * bp + u] = bits;
+        }
+      }
+      // both lanes of a pair walk the union of their candidates in the same order
+      // (bit v of the low half: row 8*(v/4) + v%4, of the high half: the same + 4),
+      // so they run the loop in step and can exchange partial sums
+      double best = INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) {
+        if (blk >= nblk) break;
+        const uint32_t other = __shfl_xor(cm[blk], 32, 64);
+        uint32_t both = half ? (other | (cm[blk] << 16)) : (cm[blk] | (other << 16));
+        while (both) {
+          const int bit = __builtin_ctz(both);
+          both &= both - 1;
+          const int v = bit & 15, hh = bit >> 4;
+          const int ci = blk * 32 + 8 * (v / 4) + 4 * hh + (v % 4);
+          double part = 0.0;
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) {
+            const uint4 cw = *reinterpret_cast<const uint4*>(&sC[ci * ROWP + kc * 16 + half * 8]);
+            const uint4 xw = as_uint4(xf[kc]);
+            const uint32_t xa[4] = {xw.x, xw.y, xw.z, xw.w}, ca[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const double d0 = double(bf16_lo(xa[i])) - double(bf16_lo(ca[i]));
+              const double d1 = double(bf16_hi(xa[i])) - double(bf16_hi(ca[i]));
+              part = __dadd_rn(part, __dmul_rn(d0, d0));
+              part = __dadd_rn(part, __dmul_rn(d1, d1));
+            }
+          }
+          const double opart = __shfl_xor(part, 32, 64);
+          const double full = half ? __dadd_rn(opart, part) : __dadd_rn(part, opart);
+          if (full < best || (full == best && ci < bi)) { best = full; bi = ci; }
+        }
+      }
+      // no finite candidate (a token with a non-finite value): score every centre
+      // exactly, the whole wavefront per token
+      uint64_t lost = __ballot(has && half == 0 && bi == 0x7fffffff);
+      while (lost) {
+        const int b = __builtin_ctzll(lost);
+        lost &= lost - 1;
+        const int64_t tb = sFt[wave][base + b];
+        const int e = exact_assign_token<bf16_t, D>(x + (int64_t(h) * n + tb) * D, centh, C, lane);
+        if (lane == b) bi = e;       // 0 when no distance is finite
+      }
+      if (has && half == 0) ids[int64_t(h) * n + t] = static_cast<uint8_t>(bi);
+    }
+  };
+
+  int nfl = 0;                         // tokens in this wavefront's list (wave-uniform)
+  for (int round = 0;; ++round) {
   const int64_t tok0 = (int64_t(blockIdx.x) * rounds + round) * 256 + wave * 64;
-  if (tok0 >= n) break;                // wave-uniform; no barrier follows
+  const bool more = round < rounds && tok0 < n;   // wave-uniform; no barrier follows
+  if (more) {
+  // token fragments (B operand) and ||x||^2
   bf16x8 xb[2][KC];
   float xx[2];
 #pragma unroll
@@ -178,47 +293,84 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
     xx[cb] = s + __shfl_xor(s, 32, 64);
   }
 
-  // best and second-best score per token; the index of the best is kept without
-  // this lane's row offset 4*half (a wave-uniform code, added after the scan)
+  // Best and second-best score per token half.  A score is tracked as a key: its
+  // low 4 bits replaced by 15 - v, where v (0..15) is its register within the
+  // block, so that one maximum keeps both the best key and where it sits; the
+  // second best is the median of (best, second, new).  A key is within 15 ulp of
+  // its score (below 2^-19 of it), which the bound below takes into account.  The
+  // block of the best is recorded whenever a block raises it.
   float b1[2] = {-INFINITY, -INFINITY}, b2[2] = {-INFINITY, -INFINITY};
-  int i1[2] = {0, 0};
-  for (int blk = 0; blk < nblk; ++blk) {
-    f32x16 nc;
+  int blk1[2] = {0, 0};
+  // Software pipeline over the 32-centre blocks: the products of block blk + 1
+  // (into the other of two accumulator sets) are issued between the scan steps
+  // of block blk, so that the matrix cores and the vector unit work at the same
+  // time within a wavefront.
+  uint4 af[KC];
+  f32x16 nc;
+  auto read_block = [&](int blk) {
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      af[kc] = *reinterpret_cast<const uint4*>(&sC[(blk * 32 + col) * ROWP + kc * 16 + half * 8]);
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const float4 t = *reinterpret_cast<const float4*>(&sN[blk * 32 + 8 * g4 + 4 * half]);
       nc[4 * g4 + 0] = t.x; nc[4 * g4 + 1] = t.y; nc[4 * g4 + 2] = t.z; nc[4 * g4 + 3] = t.w;
     }
-    f32x16 acc0 = nc, acc1 = nc;
+  };
+  auto scan_v = [&](const f32x16& c0, const f32x16& c1, int v) {
+    const float k0 = __uint_as_float((__float_as_uint(c0[v]) & ~15u) | uint32_t(15 - v));
+    const float k1 = __uint_as_float((__float_as_uint(c1[v]) & ~15u) | uint32_t(15 - v));
+    b2[0] = __builtin_amdgcn_fmed3f(b1[0], b2[0], k0);
+    b1[0] = key_max(b1[0], k0);
+    b2[1] = __builtin_amdgcn_fmed3f(b1[1], b2[1], k1);
+    b1[1] = key_max(b1[1], k1);
+  };
+  // scan block blk (accumulators cur) and, when there is one, multiply block
+  // blk + 1 into nxt
+  auto step = [&](int blk, const f32x16& cur0, const f32x16& cur1, f32x16& nxt0, f32x16& nxt1, bool has_next) {
+    const float p0 = b1[0], p1 = b1[1];
+    if (has_next) {                    // wave-uniform
+      read_block(blk + 1);
+      nxt0 = nc;
+      nxt1 = nc;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&sC[(blk * 32 + col) * ROWP + kc * 16 + half * 8]));
-      acc0 = mfma32(a, xb[0][kc], acc0);
-      acc1 = mfma32(a, xb[1][kc], acc1);
-    }
-    // strictly greater: on equal scores the earlier (lower) centre stays; the
-    // second best is the median of (best, second, new)
+      for (int kc = 0; kc < KC; ++kc) {
+        scan_v(cur0, cur1, (2 * kc) % 16);
+        nxt0 = mfma32(as_bf16x8(af[kc]), xb[0][kc], nxt0);
+        scan_v(cur0, cur1, (2 * kc + 1) % 16);
+        nxt1 = mfma32(as_bf16x8(af[kc]), xb[1][kc], nxt1);
+      }
+      if constexpr (KC < 8) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int code = blk * 32 + 8 * (v / 4) + (v % 4);
-      {
-        const float sc = acc0[v];
-        const bool gt = sc > b1[0];
-        b2[0] = __builtin_amdgcn_fmed3f(b1[0], b2[0], sc);
-        b1[0] = gt ? sc : b1[0];
-        i1[0] = gt ? code : i1[0];
+        for (int v = 2 * KC; v < 16; ++v) scan_v(cur0, cur1, v);
       }
-      {
-        const float sc = acc1[v];
-        const bool gt = sc > b1[1];
-        b2[1] = __builtin_amdgcn_fmed3f(b1[1], b2[1], sc);
-        b1[1] = gt ? sc : b1[1];
-        i1[1] = gt ? code : i1[1];
-      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) scan_v(cur0, cur1, v);
     }
+    blk1[0] = b1[0] != p0 ? blk : blk1[0];
+    blk1[1] = b1[1] != p1 ? blk : blk1[1];
+  };
+  f32x16 cA0, cA1, cB0, cB1;
+  read_block(0);
+  cA0 = nc;
+  cA1 = nc;
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    cA0 = mfma32(as_bf16x8(af[kc]), xb[0][kc], cA0);
+    cA1 = mfma32(as_bf16x8(af[kc]), xb[1][kc], cA1);
   }
-  i1[0] += 4 * half;
-  i1[1] += 4 * half;
+  for (int blk = 0; blk < nblk; blk += 2) {
+    step(blk, cA0, cA1, cB0, cB1, blk + 1 < nblk);
+    if (blk + 1 >= nblk) break;
+    step(blk + 1, cB0, cB1, cA0, cA1, blk + 2 < nblk);
+  }
+  int i1[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int v = 15 - int(__float_as_uint(b1[cb]) & 15u);
+    i1[cb] = blk1[cb] * 32 + 8 * (v / 4) + 4 * half + (v % 4);
+  }
 
   // Bound on the difference of the rounding errors of two scores.  A score sums
   // D exact products and -n_c/2 in fp32 (in any order: at most D roundings), and
@@ -226,7 +378,13 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
   // |err(t_c)| <= g (n_c + ||x|| sqrt(n_c)) with g = D 2^-24 (1 + 2^-16), using
   // |x.c| <= ||x|| ||c||; a gap of two scores is then off by at most
   // 2 g (cmax + ||x|| sqrt(cmax)), below (2D + 4) 2^-24 (cmax + ||x|| sqrt(cmax)).
-  const float err_scale = float(2 * D + 4) * 5.9604645e-08f;   // (2D + 4) * 2^-24
+  // A key differs from its score by less than 2^-19 |t_c| <= 2^-19 (cmax/2 +
+  // ||x|| sqrt(cmax)), so a gap of two keys adds at most 2^-18 (cmax + ||x||
+  // sqrt(cmax)) = 64 * 2^-24 (...): a token whose key gap exceeds the sum has its
+  // best score more than the score bound above the second, and its best key is
+  // its best score.  The candidate limit (best key - bound) stays below the best
+  // score minus the score bound.
+  const float err_scale = float(2 * D + 68) * 5.9604645e-08f;   // (2D + 68) * 2^-24
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const float ob1 = __shfl_xor(b1[cb], 32, 64);
@@ -240,97 +398,28 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
     const bool valid = tok < n;
     const float thr = err_scale * (cmax + sqrtf(xx[cb] * cmax));
     const bool flag = valid && half == 0 && !(nb1 - nb2 > thr);  // also catches NaN
-    uint64_t mask = __ballot(flag);
+    if (valid && half == 0 && !flag) ids[int64_t(h) * n + tok] = static_cast<uint8_t>(id);
+    const uint64_t mask = __ballot(flag);
     if (mask) {
-      // The true nearest centre of a flagged token is among the centres whose
-      // computed score is within thr of the best one.  Those candidates are found
-      // by scoring this token half once more, then re-scored exactly (fp64,
-      // dimensions spread over the lanes, a fixed reduction order), ties to the
-      // lowest index.
-      const float lim = nb1 - thr;
-      uint32_t cm[8];                 // candidate bits of block blk: 16 per lane
-#pragma unroll
-      for (int blk = 0; blk < 8; ++blk) cm[blk] = 0;
-      // two blocks at a time (two independent accumulation chains); the second of
-      // a pair past the last block reads rows of the 256-row table that are never
-      // used and is discarded
-#pragma unroll
-      for (int bp = 0; bp < 4; ++bp) {
-        if (2 * bp >= nblk) break;
-        f32x16 acc[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const float4 t = *reinterpret_cast<const float4*>(&sN[(2 * bp + u) * 32 + 8 * g4 + 4 * half]);
-            acc[u][4 * g4 + 0] = t.x; acc[u][4 * g4 + 1] = t.y; acc[u][4 * g4 + 2] = t.z; acc[u][4 * g4 + 3] = t.w;
-          }
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const bf16x8 a = as_bf16x8(
-                *reinterpret_cast<const uint4*>(&sC[((2 * bp + u) * 32 + col) * ROWP + kc * 16 + half * 8]));
-            acc[u] = mfma32(a, xb[cb][kc], acc[u]);
-          }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          uint32_t bits = 0;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) bits |= (acc[u][v] >= lim ? 1u : 0u) << v;
-          if (2 * bp + u < nblk) cm[2 * bp + u] = bits;
-        }
+      const int slot = nfl + int(__builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u)));
+      if (flag) {
+        sFt[wave][slot] = int(tok);
+        sFl[wave][slot] = nb1 - thr;
       }
-      constexpr int PERL = D / 64;    // dimensions per lane in the exact re-scoring
-      while (mask) {
-        const int b = __builtin_ctzll(mask);
-        mask &= mask - 1;
-        const int64_t t = tok0 + cb * 32 + b;
-        const bf16_t* xr = x + (int64_t(h) * n + t) * D;
-        // the token's row from the two lanes that hold it (fragments of 8
-        // dimensions), through this wavefront's LDS row (LDS operations of one
-        // wavefront complete in order)
-        if (col == b) {
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc)
-            *reinterpret_cast<uint4*>(&sX[wave][kc * 16 + half * 8]) = as_uint4(xb[cb][kc]);
-        }
-        double xd[PERL];
-#pragma unroll
-        for (int i = 0; i < PERL; ++i) xd[i] = double(__uint_as_float(uint32_t(sX[wave][lane * PERL + i]) << 16));
-        double best = INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int blk = 0; blk < 8; ++blk) {
-          if (blk >= nblk) break;
-          const uint32_t w0 = __builtin_amdgcn_readlane(cm[blk], b);
-          const uint32_t w1 = __builtin_amdgcn_readlane(cm[blk], b + 32);
-          uint32_t both = w0 | (w1 << 16);   // bit v: row 8*(v/4) + v%4 (+4 for the high half)
-          while (both) {
-            const int bit = __builtin_ctz(both);
-            both &= both - 1;
-            const int v = bit & 15, hh = bit >> 4;
-            const int ci = blk * 32 + 8 * (v / 4) + 4 * hh + (v % 4);
-            double part = 0.0;
-#pragma unroll
-            for (int i = 0; i < PERL; ++i) {
-              const double cv = double(__uint_as_float(uint32_t(sC[ci * ROWP + lane * PERL + i]) << 16));
-              const double dlt = xd[i] - cv;
-              part = __dadd_rn(part, __dmul_rn(dlt, dlt));
-            }
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) part = __dadd_rn(part, __shfl_xor(part, o, 64));
-            if (part < best || (part == best && ci < bi)) { best = part; bi = ci; }
-          }
-        }
-        int e = bi;
-        if (bi == 0x7fffffff)           // no candidate (non-finite scores): score every centre exactly
-          e = exact_assign_token<bf16_t, D>(xr, centh, C, lane);   // 0 when no distance is finite
-        if (lane == b) id = e;
-      }
+      nfl += __popcll(mask);
     }
-    if (valid && half == 0) ids[int64_t(h) * n + tok] = static_cast<uint8_t>(id);
   }
+  }
+  // the list holds at most kFlagCap tokens and a round adds at most 64
+  if (nfl > kFlagCap - 64 || (!more && nfl > 0)) {
+    __builtin_amdgcn_wave_barrier();   // the list's LDS writes precede its reads (one wavefront: in order)
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    flush(nfl);
+    nfl = 0;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  }
+  if (!more) break;
   }
 }
 
