@@ -115,6 +115,28 @@ def test_assign_bf16(d, C, N):
     assert excl <= max(2, 0.001 * H * N)
 
 
+@pytest.mark.parametrize("d,N", [(128, 1000), (64, 600)])
+def test_assign_every_token_flagged_many_rounds(d, N):
+    """Centres 32..63 duplicate centres 0..31, so every token is an exact tie
+    between its nearest centre and that centre's copy and takes the exact pass.
+    1024 heads give each workgroup several consecutive rounds of 256 tokens (a
+    ragged last one), so the per-wavefront list of such tokens fills and is
+    resolved more than once.  Ties go to the lowest index, like the oracle's."""
+    H, C0 = 1024, 32
+    x = _bf16_tokens(H, N, d, 91)
+    base = synth.forgy_init(x, C0, 92)
+    cent = torch.cat([base, base], dim=1).contiguous()
+    ids = kvc().fit_assign(x.to(DEV), cent.to(DEV).clone(), n_iter=0).cpu().numpy().astype(np.int64)
+    assert ids.max() < C0, "a token took the copy of its centre (ties go to the lower index)"
+    xn, cn = np32(x), np32(cent)
+    for h in (0, 1, 2, 511, 512, 1022, 1023):
+        check_ids(ids[h], xn[h], cn[h], what=f"head {h}")
+    # identical centres: every token ties with all of them and takes id 0
+    same = cent[:, :1].expand(H, 8, d).contiguous()
+    ids0 = kvc().fit_assign(x.to(DEV), same.to(DEV).clone(), n_iter=0)
+    assert int(ids0.max().item()) == 0
+
+
 def test_assign_fp32_tiny():
     cfg = synth.get_config("tiny")
     x, _ = synth.tiny_kv(cfg, "k")
