@@ -680,9 +680,8 @@ def measured_traffic(workload):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported on this build "
-              "(the hot path has no multi-GPU sharding; see the design notes on how it would shard)",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the hot path runs on "
+              "one GPU; across GPUs it would be split by head, which needs no communication)", file=sys.stderr)
         sys.exit(2)
     import torch
     import compressed_kv_cache_kvc_amd as kvc
