@@ -378,6 +378,21 @@ def test_attend_fp32_tiny():
     _attend_check(q, [cache], cent_dtype=torch.float32, what="tiny fp32")
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_attend_fp32_many_ragged_segments(d):
+    # fp32 queries and centres over several segments of one codec (ragged sizes,
+    # a one-token segment), several heads, a query count that is not a multiple
+    # of the four wavefronts of a workgroup; then an empty history
+    H, n_q = 3, 203
+    caches = [_cache(H, n, d, min(16, n), 4, 2, 16, 70 + i, dtype=torch.float32)
+              for i, n in enumerate([130, 1, 517])]
+    q = torch.randn(H, n_q, d, generator=torch.Generator().manual_seed(79))
+    _attend_check(q, caches, cent_dtype=torch.float32, what=f"fp32 d{d}")
+    out, lse = kvc().attend(q.to(DEV), [])
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
 # ------------------------------------------------------------------------------ low-dim attention
 @pytest.mark.parametrize("rank,kb,vb,g", [(32, 2, 4, 16), (64, 4, 4, 32), (32, 4, 2, 32)])
 def test_attend_lowdim(rank, kb, vb, g):
