@@ -101,7 +101,7 @@ def _check_ids(ids_gpu, x, cent):
     return sum(check_ids(ids_gpu[h], x[h], cent[h], what=f"head {h}")[0] for h in range(x.shape[0]))
 
 
-@pytest.mark.parametrize("d,C,N", [(128, 256, 1300), (128, 100, 999), (64, 16, 700), (64, 256, 513)])
+@pytest.mark.parametrize("d,C,N", [(128, 256, 1300), (128, 100, 999), (128, 80, 777), (64, 16, 700), (64, 256, 513)])
 def test_assign_bf16(d, C, N):
     cfg = synth.get_config("self_forcing_layer")
     H = 2
