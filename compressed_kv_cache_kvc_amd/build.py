@@ -27,10 +27,10 @@ COMMON = [
 ]
 # the codec must not fuse multiply-adds: its codes are defined by separately
 # rounded fp32 operations
-# the assignment kernel reads every score with vector instructions: its matrix
+# the assignment kernels read every score with vector instructions: their matrix
 # products accumulate in ordinary VGPRs (no accumulation-register copies)
 PER_FILE = {"encode.hip": ["-ffp-contract=off"], "api.cpp": ["-ffp-contract=off"], "tempo.hip": ["-ffp-contract=off"],
-            "assign.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+            "assign.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"], "qsac.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:

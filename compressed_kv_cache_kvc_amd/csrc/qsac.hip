@@ -15,10 +15,13 @@
 // v_mfma_f32_32x32x16_bf16: w*x (fp32) is split into bf16 hi + lo parts, both
 // pre-scaled by -2 (exact), so that two products against the bf16 centre give
 // the dot product to about 2^-18 relative; the accumulator starts at ||mu_j||_w^2.
-// Each lane keeps its M+1 best (score, index) pairs.  When the gap between the
-// M-th and (M+1)-th score is not larger than twice a bound on the score error,
-// the candidate set is recomputed exactly: fp64 distances of the centres whose
-// computed score lies within that margin.  The candidates' QSAC scores are
+// Each lane keeps its M+1 smallest scores as packed keys (the score with its 8
+// low mantissa bits replaced by the centre index, so within 2^-15 of the score,
+// relative), in a sorted list that takes a new key with one min and M med3
+// operations.  When the gap between the M-th and (M+1)-th key is not larger than
+// twice a bound on the score error plus the packing error, the candidate set is
+// recomputed exactly: fp64 distances of the centres whose computed score lies
+// within that margin.  The candidates' QSAC scores are
 // computed in fp32.  fp32 tokens take the exact path
 // throughout, with fp64 scores.
 #include "kvc_internal.h"
@@ -189,9 +192,10 @@ __global__ __launch_bounds__(256) void qsac_mfma_kernel(const bf16_t* __restrict
     }
   }
   load_weights<D>(w, h, G, sW, sWg);   // ends with a barrier
-  // ||mu||_w^2 in fp32, channels in order; padding rows score +inf
+  // ||mu||_w^2 in fp32, channels in order; padding rows score the largest finite
+  // value (their packed keys stay finite and sort last)
   {
-    float sn = INFINITY;
+    float sn = 3.40282347e+38f;
     if (tid < C) {
       sn = 0.f;
       for (int c = 0; c < D; ++c) {
@@ -250,9 +254,23 @@ __global__ __launch_bounds__(256) void qsac_mfma_kernel(const bf16_t* __restrict
     }
     xxw += __shfl_xor(xxw, 32, 64);
 
-    // approximate weighted scores, M+1 best per lane (this half's 16 rows of each block)
-    TopList<float, M + 1> top;
-    top.init();
+    // approximate weighted scores: the M+1 smallest packed keys of this lane's
+    // rows (this half's 16 rows of each block), ascending
+    float key[M + 1];
+#pragma unroll
+    for (int k = 0; k <= M; ++k) key[k] = INFINITY;
+    // insertion into the sorted list from its old entries: entry k becomes the
+    // median of old entries k-1, k and the new key, entry 0 the smaller of old
+    // entry 0 and the new key
+    auto put = [&](float v) {
+      float nk[M + 1];
+      // written out: the compiler's min would first canonicalize the packed keys
+      asm("v_min_f32 %0, %1, %2" : "=v"(nk[0]) : "v"(key[0]), "v"(v));
+#pragma unroll
+      for (int k = 1; k <= M; ++k) nk[k] = __builtin_amdgcn_fmed3f(key[k - 1], key[k], v);
+#pragma unroll
+      for (int k = 0; k <= M; ++k) key[k] = nk[k];
+    };
     for (int blk = 0; blk < nblk; ++blk) {
       f32x16 acc;
 #pragma unroll
@@ -266,38 +284,39 @@ __global__ __launch_bounds__(256) void qsac_mfma_kernel(const bf16_t* __restrict
         acc = mfma32(a, bhi[kc], acc);
         acc = mfma32(a, blo[kc], acc);
       }
-      // most scores lose to the list's last entry: insert only when some lane's
-      // score beats it (a wave-uniform branch keeps each insertion small)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float sv = acc[v];
-        if (__ballot(sv <= top.s[M])) top.insert(sv, blk * 32 + 8 * (v / 4) + 4 * half + (v % 4));
+        const uint32_t row = uint32_t(blk * 32 + 8 * (v / 4) + 4 * half + (v % 4));
+        put(__uint_as_float((__float_as_uint(acc[v]) & ~0xFFu) | row));
       }
     }
     // merge with the other half of the rows (lane ^ 32): copy its list first
     {
-      float os[M + 1];
-      int oi[M + 1];
+      float ok[M + 1];
 #pragma unroll
-      for (int k = 0; k <= M; ++k) { os[k] = __shfl_xor(top.s[k], 32, 64); oi[k] = __shfl_xor(top.i[k], 32, 64); }
+      for (int k = 0; k <= M; ++k) ok[k] = __shfl_xor(key[k], 32, 64);
 #pragma unroll
-      for (int k = 0; k <= M; ++k) top.insert(os[k], oi[k]);
+      for (int k = 0; k <= M; ++k) put(ok[k]);
     }
     int cand[M];
 #pragma unroll
-    for (int k = 0; k < M; ++k) cand[k] = top.i[k];
-    // the set of the M nearest is certain when the (M+1)-th score is more than
-    // twice the error bound above the M-th one (or there are at most M centres)
+    for (int k = 0; k < M; ++k) cand[k] = key[k] < INFINITY ? int(__float_as_uint(key[k]) & 0xFFu) : 0x7fffffff;
+    // the set of the M nearest is certain when the (M+1)-th key is more than
+    // twice the score error bound, plus the packing error of the two keys (2^-15
+    // relative each, taken as 2^-14), above the M-th one (or there are at most M
+    // centres)
     const float thr = err_a * cmax + err_b * sqrtf(xxw * cmax);
-    const bool flag = valid && C > M && !(top.s[M] - top.s[M - 1] > 2.f * thr);   // also catches NaN
+    const float pack_err = 6.1035156e-05f * (fabsf(key[M]) + fabsf(key[M - 1]));
+    const bool flag = valid && C > M && !(key[M] - key[M - 1] > 2.f * thr + pack_err);   // also catches NaN
     uint64_t mask = __ballot(flag && half == 0);
     if (mask) {
       // Each computed score is within thr of its exact value, so every centre of
-      // the exact M nearest scores at most 2*thr above the M-th computed score:
+      // the exact M nearest scores at most 2*thr above the M-th computed score
+      // (itself within the packing error of the M-th key):
       // this pass's scores are formed once more to mark the centres under that
       // limit, and only those are re-scored exactly (fp64, dimensions spread over
       // the lanes, a fixed reduction order).
-      const float lim = top.s[M - 1] + 2.f * thr;
+      const float lim = key[M - 1] + 6.1035156e-05f * fabsf(key[M - 1]) + 2.f * thr;
       uint32_t cm[8];                 // marked rows of block blk: 16 bits per lane
 #pragma unroll
       for (int q = 0; q < 8; ++q) cm[q] = 0;
@@ -362,6 +381,7 @@ __global__ __launch_bounds__(256) void qsac_mfma_kernel(const bf16_t* __restrict
             both &= both - 1;
             const int v = bit & 15, hh = bit >> 4;
             const int ci = blk * 32 + 8 * (v / 4) + 4 * hh + (v % 4);
+            if (ci >= C) continue;     // a padding row (only under a non-finite limit)
             ex.insert(exact(ci), ci);
             ++seen;
           }
