@@ -67,6 +67,30 @@ __device__ __forceinline__ uint32_t f32_to_f16_directed(float f, bool up) {
   return (sign << 15) | bits;
 }
 
+// The same directed rounding by the conversion instruction: the round-mode
+// fields of the MODE register (bits 0-1 for fp32, 2-3 for fp16 and fp64; 1 =
+// toward +inf, 2 = toward -inf, 0 = nearest even) are set for the one
+// conversion and set back to nearest even in the same statement, with wait
+// states on both sides of the conversion.  The input is first clamped to
+// +-65504, so that results saturate there as above.
+__device__ __forceinline__ uint32_t f32_to_f16_directed_hw(float f, bool up) {
+  const float c = __builtin_amdgcn_fmed3f(f, -65504.0f, 65504.0f);
+  uint32_t r;
+  if (up)
+    asm volatile(
+        "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 4), 5\n\ts_nop 1\n\tv_cvt_f16_f32 %0, %1\n\ts_nop 4\n\t"
+        "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 4), 0"
+        : "=v"(r)
+        : "v"(c));
+  else
+    asm volatile(
+        "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 4), 10\n\ts_nop 1\n\tv_cvt_f16_f32 %0, %1\n\ts_nop 4\n\t"
+        "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 4), 0"
+        : "=v"(r)
+        : "v"(c));
+  return r & 0xffffu;
+}
+
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
   return __half2float(__ushort_as_half(static_cast<unsigned short>(h)));
 }

@@ -21,12 +21,12 @@ __device__ __forceinline__ uint32_t quantize_group(const float (&r)[G], uint32_t
   float mn = r[0], mx = r[0];
 #pragma unroll
   for (int i = 1; i < G; ++i) { mn = fminf(mn, r[i]); mx = fmaxf(mx, r[i]); }
-  uint32_t z16 = f32_to_f16_directed(mn, /*up=*/false);
+  uint32_t z16 = f32_to_f16_directed_hw(mn, /*up=*/false);
   if ((z16 & 0x7fffu) == 0) z16 = 0;                     // zero offset stored as +0
   const float z = f16_bits_to_f32(z16);
   constexpr float L = float((1 << BITS) - 1);
   const float s32 = __fdiv_rn(__fsub_rn(mx, z), L);
-  uint32_t s16 = f32_to_f16_directed(s32, /*up=*/true);
+  uint32_t s16 = f32_to_f16_directed_hw(s32, /*up=*/true);
   if ((s16 & 0x7fffu) == 0) s16 = 0;
   const float s = f16_bits_to_f32(s16);
   if (s16 == 0) {
@@ -44,20 +44,21 @@ __device__ __forceinline__ uint32_t quantize_group(const float (&r)[G], uint32_t
   return s16 | (z16 << 16);
 }
 
-// Full-dimensional encode: one thread per (token, channel group).
+// Full-dimensional encode: one thread per (token, channel group) of head
+// blockIdx.y (the arrays start at the launch's first head).
 template <typename T, int D, int G, int BITS>
 __global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, const T* __restrict__ cent,
                                                      const uint8_t* __restrict__ ids, int C, int64_t n,
-                                                     int64_t total_items, uint8_t* __restrict__ codes,
-                                                     uint32_t* __restrict__ meta) {
+                                                     uint8_t* __restrict__ codes, uint32_t* __restrict__ meta) {
   constexpr int NG = D / G;
   constexpr int ROW_BYTES = D * BITS / 8;
   constexpr int CHUNK_WORDS = G * BITS / 32;  // 32-bit words of codes per group
-  const int64_t item = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (item >= total_items) return;
-  const int g = int(item % NG);
-  const int64_t tok = item / NG;               // h * n + j
-  const int64_t h = tok / n;
+  static_assert((NG & (NG - 1)) == 0, "groups per row: a power of two");
+  const int64_t item = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;   // (token, group) within the head
+  if (item >= n * NG) return;
+  const int g = int(item) & (NG - 1);
+  const int64_t h = blockIdx.y;
+  const int64_t tok = h * n + (item >> __builtin_ctz(NG));   // h * n + j
   const int id = ids[tok];
 
   float xv[G], cv[G], r[G];
@@ -96,12 +97,13 @@ __global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, co
 template <typename T, int D>
 __global__ __launch_bounds__(256) void encode_raw_kernel(const T* __restrict__ x, const T* __restrict__ cent,
                                                          const uint8_t* __restrict__ ids, int C, int64_t n,
-                                                         int64_t total_items, uint8_t* __restrict__ codes) {
-  const int64_t item = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (item >= total_items) return;
-  const int g = int(item % (D / 8));
-  const int64_t tok = item / (D / 8);
-  const int64_t h = tok / n;
+                                                         uint8_t* __restrict__ codes) {
+  constexpr int NG = D / 8;
+  const int64_t item = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;   // (token, 8 channels) within the head
+  if (item >= n * NG) return;
+  const int g = int(item) & (NG - 1);
+  const int64_t h = blockIdx.y;
+  const int64_t tok = h * n + (item >> __builtin_ctz(NG));
   const int id = ids[tok];
   float xv[8], cv[8];
   load_row<8>(x + tok * D + g * 8, xv);
@@ -225,13 +227,19 @@ __global__ __launch_bounds__(256) void encode_lowdim_kernel(const T* __restrict_
 template <typename T, int D, int G, int BITS>
 hipError_t run_full(int heads, int64_t n, const void* x, int C, const void* cent, const uint8_t* ids,
                     uint8_t* codes, uint16_t* meta, hipStream_t st) {
-  const int64_t items = int64_t(heads) * n * (D / G);
-  if (items == 0) return hipSuccess;
-  const int64_t blocks = (items + 255) / 256;
-  hipLaunchKernelGGL((encode_kernel<T, D, G, BITS>), dim3(unsigned(blocks)), dim3(256), 0, st,
-                     static_cast<const T*>(x), static_cast<const T*>(cent), ids, C, n, items, codes,
-                     reinterpret_cast<uint32_t*>(meta));
-  return hipGetLastError();
+  if (heads == 0 || n == 0) return hipSuccess;
+  const int64_t blocks = (n * (D / G) + 255) / 256;
+  // the grid's second dimension takes the heads, at most 65535 per launch
+  for (int h0 = 0; h0 < heads; h0 += 65535) {
+    const int hc = heads - h0 < 65535 ? heads - h0 : 65535;
+    hipLaunchKernelGGL((encode_kernel<T, D, G, BITS>), dim3(unsigned(blocks), unsigned(hc)), dim3(256), 0, st,
+                       static_cast<const T*>(x) + int64_t(h0) * n * D, static_cast<const T*>(cent) + int64_t(h0) * C * D,
+                       ids + int64_t(h0) * n, C, n, codes + int64_t(h0) * n * (D * BITS / 8),
+                       reinterpret_cast<uint32_t*>(meta) + int64_t(h0) * n * (D / G));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <typename T, int D, int R, int G, int BITS>
@@ -250,11 +258,17 @@ template <typename T, int D>
 hipError_t dispatch_full(int heads, int64_t n, const void* x, int C, const void* cent, const uint8_t* ids,
                          int bits, int group, uint8_t* codes, uint16_t* meta, hipStream_t st) {
   if (bits == 16) {
-    const int64_t items = int64_t(heads) * n * (D / 8);
-    if (items == 0) return hipSuccess;
-    hipLaunchKernelGGL((encode_raw_kernel<T, D>), dim3(unsigned((items + 255) / 256)), dim3(256), 0, st,
-                       static_cast<const T*>(x), static_cast<const T*>(cent), ids, C, n, items, codes);
-    return hipGetLastError();
+    if (heads == 0 || n == 0) return hipSuccess;
+    const int64_t blocks = (n * (D / 8) + 255) / 256;
+    for (int h0 = 0; h0 < heads; h0 += 65535) {
+      const int hc = heads - h0 < 65535 ? heads - h0 : 65535;
+      hipLaunchKernelGGL((encode_raw_kernel<T, D>), dim3(unsigned(blocks), unsigned(hc)), dim3(256), 0, st,
+                         static_cast<const T*>(x) + int64_t(h0) * n * D, static_cast<const T*>(cent) + int64_t(h0) * C * D,
+                         ids + int64_t(h0) * n, C, n, codes + int64_t(h0) * n * (D * 2));
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
   if (group == 16 && bits == 2) return run_full<T, D, 16, 2>(heads, n, x, C, cent, ids, codes, meta, st);
   if (group == 16 && bits == 4) return run_full<T, D, 16, 4>(heads, n, x, C, cent, ids, codes, meta, st);
