@@ -37,43 +37,17 @@ __device__ __forceinline__ void load_row(const float* p, float (&v)[N]) {
   }
 }
 
-// fp32 -> fp16 bit pattern, rounding the magnitude up (toward +inf for positive
-// values) when `toward_pos_inf` matches the sign convention below.  Written from
-// the IEEE-754 binary16 definition: 11 significant bits, smallest normal 2^-14,
-// subnormal quantum 2^-24.  up = true rounds toward +inf, up = false toward -inf.
-// Results beyond the fp16 range saturate to +-65504 (out of the codec's contract).
+// fp32 -> fp16 bit pattern rounded toward +inf (up = true) or toward -inf
+// (up = false), with results beyond the fp16 range saturated to +-65504 (out of
+// the codec's contract): the exact value's nearest fp16 neighbour on that side
+// (11 significant bits, smallest normal 2^-14, subnormal quantum 2^-24; a tiny
+// nonzero input goes to +-2^-24 or to a signed zero).  Done by the conversion
+// instruction: the round-mode fields of the MODE register (bits 0-1 for fp32,
+// 2-3 for fp16 and fp64; 1 = toward +inf, 2 = toward -inf, 0 = nearest even)
+// are set for the one conversion and set back to nearest even in the same
+// statement, with wait states on both sides of the conversion.  The input is
+// first clamped to +-65504, which gives the saturation.
 __device__ __forceinline__ uint32_t f32_to_f16_directed(float f, bool up) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t sign = u >> 31;
-  const uint32_t a = u & 0x7fffffffu;
-  const bool mag_up = (up != (sign != 0));  // round the magnitude away from zero?
-  if (a == 0) return sign << 15;
-  uint32_t bits;
-  if (a < 0x00800000u) {                    // fp32 subnormal: far below half the fp16 quantum
-    bits = mag_up ? 1u : 0u;
-  } else {
-    const int e = int(a >> 23) - 127;       // value = m * 2^(e - 23), m in [2^23, 2^24)
-    const uint32_t m = (a & 0x007fffffu) | 0x00800000u;
-    const int qe = max(e - 10, -24);        // exponent of the fp16 quantum at this magnitude
-    const int sh = qe - (e - 23);           // >= 13
-    uint32_t R, rem;
-    if (sh >= 32) { R = 0; rem = m; }
-    else { R = m >> sh; rem = m & ((1u << sh) - 1u); }
-    if (rem != 0 && mag_up) R += 1;
-    // R * 2^qe with R <= 2048; the field layout absorbs a carry into the exponent
-    bits = (R < 1024u) ? R : (uint32_t(qe + 24) << 10) + R;
-    if (bits > 0x7bffu) bits = 0x7bffu;     // saturate at 65504
-  }
-  return (sign << 15) | bits;
-}
-
-// The same directed rounding by the conversion instruction: the round-mode
-// fields of the MODE register (bits 0-1 for fp32, 2-3 for fp16 and fp64; 1 =
-// toward +inf, 2 = toward -inf, 0 = nearest even) are set for the one
-// conversion and set back to nearest even in the same statement, with wait
-// states on both sides of the conversion.  The input is first clamped to
-// +-65504, so that results saturate there as above.
-__device__ __forceinline__ uint32_t f32_to_f16_directed_hw(float f, bool up) {
   const float c = __builtin_amdgcn_fmed3f(f, -65504.0f, 65504.0f);
   uint32_t r;
   if (up)

@@ -21,12 +21,12 @@ __device__ __forceinline__ uint32_t quantize_group(const float (&r)[G], uint32_t
   float mn = r[0], mx = r[0];
 #pragma unroll
   for (int i = 1; i < G; ++i) { mn = fminf(mn, r[i]); mx = fmaxf(mx, r[i]); }
-  uint32_t z16 = f32_to_f16_directed_hw(mn, /*up=*/false);
+  uint32_t z16 = f32_to_f16_directed(mn, /*up=*/false);
   if ((z16 & 0x7fffu) == 0) z16 = 0;                     // zero offset stored as +0
   const float z = f16_bits_to_f32(z16);
   constexpr float L = float((1 << BITS) - 1);
   const float s32 = __fdiv_rn(__fsub_rn(mx, z), L);
-  uint32_t s16 = f32_to_f16_directed_hw(s32, /*up=*/true);
+  uint32_t s16 = f32_to_f16_directed(s32, /*up=*/true);
   if ((s16 & 0x7fffu) == 0) s16 = 0;
   const float s = f16_bits_to_f32(s16);
   if (s16 == 0) {
