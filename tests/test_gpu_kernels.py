@@ -77,6 +77,28 @@ def test_encode_bit_exact(d, bits, group, dtype):
         assert np.array_equal(meta.cpu().numpy(), ref_meta)
 
 
+@pytest.mark.parametrize("bits,group", [(2, 16), (4, 32), (16, 16)])
+def test_encode_more_heads_than_one_launch_covers(bits, group):
+    """65537 heads of 3 tokens: the encoder's grid takes at most 65535 heads per
+    launch, so this call needs two; codes and metadata are checked bit-exactly on
+    heads at both ends of each launch and around the boundary."""
+    H, N, d, C = 65537, 3, 64, 4
+    g = torch.Generator().manual_seed(21)
+    x = (torch.randn(H, N, d, generator=g) * 2.0).to(torch.bfloat16)
+    cent = (torch.randn(H, C, d, generator=g) * 2.0).to(torch.bfloat16)
+    ids = torch.randint(0, C, (H, N), generator=g, dtype=torch.uint8)
+    codes, meta, _ = kvc().encode(x.to(DEV), cent.to(DEV), bits, group, ids=ids.to(DEV))
+    torch.cuda.synchronize()
+    sel = np.array([0, 1, 65533, 65534, 65535, 65536])
+    xs, cs, ids_s = np32(x[sel]), np32(cent[sel]), ids[sel].numpy().astype(np.int64)
+    ref_codes, ref_meta = encode_heads(xs, cs, ids_s, bits, group)
+    assert np.array_equal(codes.cpu().numpy()[sel], ref_codes)
+    if bits == 16:
+        assert meta is None
+    else:
+        assert np.array_equal(meta.cpu().numpy()[sel], ref_meta)
+
+
 @pytest.mark.parametrize("rank,bits,group", [(32, 2, 16), (32, 4, 16), (64, 4, 32), (64, 2, 32)])
 def test_encode_lowdim_bit_exact(rank, bits, group):
     H, N, C, d = 2, 777, 20, 128
