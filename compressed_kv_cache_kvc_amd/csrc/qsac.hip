@@ -12,8 +12,9 @@
 //      index).
 //
 // bf16 tokens.  d_w(x, mu_j) - ||x||_w^2 = ||mu_j||_w^2 - 2 (w*x).mu_j is formed on
-// v_mfma_f32_32x32x16_bf16: w*x (fp32) is split into bf16 hi + lo parts, both
-// pre-scaled by -2 (exact), so that two products against the bf16 centre give
+// v_mfma_f32_32x32x16_bf16: -2 w*x (fp32; the -2 is folded into the staged
+// weights, an exact scaling) is split into bf16 hi + lo parts, so that two
+// products against the bf16 centre give
 // the dot product to about 2^-18 relative; the accumulator starts at ||mu_j||_w^2.
 // Each lane keeps its M+1 smallest scores as packed keys (the score with its 8
 // low mantissa bits replaced by the centre index, so within 2^-15 of the score,
@@ -160,6 +161,7 @@ __global__ __launch_bounds__(256) void qsac_mfma_kernel(const bf16_t* __restrict
   __shared__ __attribute__((aligned(16))) uint16_t sC[256 * ROWP];
   __shared__ float sN[256];
   __shared__ float sW[D];
+  __shared__ float sWm2[D];            // -2 w: the token operand's factor (exact scaling)
   __shared__ float sWg[D / 16];
   __shared__ __attribute__((aligned(16))) uint16_t sX[4][D];   // a flagged token's row, per wavefront
 
@@ -204,6 +206,7 @@ __global__ __launch_bounds__(256) void qsac_mfma_kernel(const bf16_t* __restrict
       }
     }
     if (tid < rows) sN[tid] = sn;
+    if (tid < D) sWm2[tid] = -2.f * sW[tid];
   }
   __syncthreads();
   float cmax = 0.f;
@@ -239,20 +242,20 @@ __global__ __launch_bounds__(256) void qsac_mfma_kernel(const bf16_t* __restrict
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = kc * 16 + half * 8 + 2 * i;
+        // b = -2 w x: the factor -2 scales fl(w x), its bf16 parts and the norm
+        // terms exactly, so these are -2 times the parts of w x
         const float x0 = bf16_lo(ww[i]), x1 = bf16_hi(ww[i]);
-        const float b0 = sW[c] * x0, b1 = sW[c + 1] * x1;
+        const float b0 = sWm2[c] * x0, b1 = sWm2[c + 1] * x1;
         xxw = fmaf(b0, x0, xxw);
         xxw = fmaf(b1, x1, xxw);
         const uint32_t hp = pack_bf16x2(b0, b1);
-        const float h0 = bf16_lo(hp), h1 = bf16_hi(hp);
-        const uint32_t lp = pack_bf16x2(b0 - h0, b1 - h1);
-        hw[i] = pack_bf16x2(-2.f * h0, -2.f * h1);
-        lw[i] = pack_bf16x2(-2.f * bf16_lo(lp), -2.f * bf16_hi(lp));
+        hw[i] = hp;
+        lw[i] = pack_bf16x2(b0 - bf16_lo(hp), b1 - bf16_hi(hp));
       }
       bhi[kc] = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
       blo[kc] = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
     }
-    xxw += __shfl_xor(xxw, 32, 64);
+    xxw = -0.5f * (xxw + __shfl_xor(xxw, 32, 64));   // ||x||_w^2
 
     // approximate weighted scores: the M+1 smallest packed keys of this lane's
     // rows (this half's 16 rows of each block), ascending
