@@ -604,10 +604,15 @@ __global__ __launch_bounds__(256) void kmeans_update_kernel(const T* __restrict_
 // centre's sum is its members' rows in token order, grouped by run.  The mean is
 // one fp64 division rounded to nearest even in the storage type; a centre without
 // members keeps its value.
-template <typename T, int D>
+//
+// With GL (global lists), steps 1-3 are skipped: the member lists and the
+// centres' list starts of the whole head come from member_lists_kernel (in the
+// caller's workspace), so no workgroup scans the head's ids.
+template <typename T, int D, bool GL>
 __global__ __launch_bounds__(512) void kmeans_update_sorted_kernel(const T* __restrict__ x, T* __restrict__ cent,
                                                                    const uint8_t* __restrict__ ids, int C, int CG,
-                                                                   int n) {
+                                                                   int n, const uint32_t* __restrict__ glists,
+                                                                   const uint32_t* __restrict__ gstarts) {
   constexpr int PER = D / 64;                 // channels per lane
   constexpr int WPR = PER * int(sizeof(T)) / 4 > 0 ? PER * int(sizeof(T)) / 4 : 1;   // 32-bit words per lane and row
   constexpr int BATCH = 32;                   // rows in flight per wavefront
@@ -617,17 +622,33 @@ __global__ __launch_bounds__(512) void kmeans_update_sorted_kernel(const T* __re
   const int h = blockIdx.y;
   const int c0 = blockIdx.x * CG;
   const int cg = min(CG, C - c0);
-  const int npad = (n + 15) & ~15;
+  const int npad = GL ? 0 : (n + 15) & ~15;                  // staged ids
+  const int lpad = GL ? 0 : (2 * n + 15) & ~15;              // the group's list (uint16 token indices)
   uint8_t* sid = lds;
   uint16_t* list = reinterpret_cast<uint16_t*>(lds + npad);
-  uint32_t* off = reinterpret_cast<uint32_t*>(lds + npad + ((2 * n + 15) & ~15));   // [8][CG]
+  uint32_t* off = reinterpret_cast<uint32_t*>(lds + npad + lpad);                      // [8][CG]
   uint32_t* start = off + 8 * CG;                                                       // [CG + 1]
   int* pc = reinterpret_cast<int*>(start + CG + 1);                                     // [16] centre of a partial
   uint32_t* wsum = reinterpret_cast<uint32_t*>(pc + 16);                                // [8]
   double* part = reinterpret_cast<double*>(
-      lds + ((npad + ((2 * n + 15) & ~15) + 4 * (8 * CG + CG + 1 + 16 + 8) + 15) & ~15));   // [16][D]
+      lds + ((npad + lpad + 4 * (8 * CG + CG + 1 + 16 + 8) + 15) & ~15));   // [16][D]
+  // global lists: the group's segment of the head's list
+  const uint32_t* glist = nullptr;
+  if constexpr (GL) {
+    const uint32_t* st = gstarts + int64_t(h) * (C + 1) + c0;
+    const uint32_t base = st[0];
+    glist = glists + int64_t(h) * n + base;
+    for (int t = threadIdx.x; t <= cg; t += 512) start[t] = st[t] - base;
+    if (threadIdx.x < 16) pc[threadIdx.x] = -1;
+    __syncthreads();
+  }
+  auto list_at = [&](int i) -> int {
+    if constexpr (GL) return int(glist[i]);
+    else return int(list[i]);
+  };
 
   const uint8_t* idh = ids + int64_t(h) * n;
+  if constexpr (!GL) {
   if ((reinterpret_cast<uintptr_t>(idh) & 3) == 0) {
     const int n4 = n / 4;
     for (int i = threadIdx.x; i < n4; i += 512) reinterpret_cast<uint32_t*>(sid)[i] = reinterpret_cast<const uint32_t*>(idh)[i];
@@ -704,6 +725,7 @@ __global__ __launch_bounds__(512) void kmeans_update_sorted_kernel(const T* __re
     if (m && below == cnt - 1) off[wave * CG + u] += uint32_t(cnt);
   }
   __syncthreads();
+  }   // !GL
 
   // 4. sums over this wavefront's run of the sorted list
   const T* xh = x + int64_t(h) * n * D + lane * PER;
@@ -757,7 +779,7 @@ __global__ __launch_bounds__(512) void kmeans_update_sorted_kernel(const T* __re
       uint32_t w[BATCH][WPR];
 #pragma unroll
       for (int b = 0; b < BATCH; ++b) {
-        const int j = int(list[i0 + b < r1 ? i0 + b : r1 - 1]);
+        const int j = list_at(i0 + b < r1 ? i0 + b : r1 - 1);
         load_raw(j < n ? j : n - 1, w[b]);   // always in range (the list holds token indices < n)
       }
 #pragma unroll
@@ -812,6 +834,112 @@ __global__ __launch_bounds__(512) void kmeans_update_sorted_kernel(const T* __re
   }
 }
 
+// Member lists of a whole head for the centre update of long heads: a stable
+// counting sort of the head's tokens by centre id, written to the caller's
+// workspace as starts[u] (members of the centres before u; starts[C] = n) and
+// lists[starts[u] ..] (the token indices of centre u's members).  One workgroup
+// of NW wavefronts per head; wavefront w takes the w-th of NW equal token
+// ranges and walks it 256 tokens at a time, lane l holding tokens p + 4l .. p +
+// 4l + 3 and the four steps of 64 taking token p + 4l + k in step k.  Counting
+// and scattering walk in the same order, so the order inside a centre's list is
+// fixed (token order within a step, steps in walk order, ranges in wavefront
+// order) and the sums over it are deterministic.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void member_lists_kernel(const uint8_t* __restrict__ ids, int C, int n,
+                                                               uint32_t* __restrict__ lists,
+                                                               uint32_t* __restrict__ starts) {
+  __shared__ uint32_t off[NW][256];
+  __shared__ uint32_t wsum[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int h = blockIdx.x;
+  const uint8_t* idh = ids + int64_t(h) * n;
+  uint32_t* lh = lists + int64_t(h) * n;
+  for (int i = threadIdx.x; i < NW * 256; i += NW * 64) (&off[0][0])[i] = 0u;
+  __syncthreads();
+  auto rank_of = [](uint64_t m) {
+    return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+  };
+  // lanes of this step holding the same centre as this lane (valid for matching lanes)
+  auto same_centre = [&](bool m, int u) {
+    uint64_t same = __ballot(m);
+    for (int b = 0; (1 << b) < C; ++b) {
+      const bool bit = ((u >> b) & 1) != 0;
+      const uint64_t bb = __ballot(m && bit);
+      same &= bit ? bb : ~bb;
+    }
+    return same;
+  };
+  const int s0 = int(int64_t(n) * wave / NW), s1 = int(int64_t(n) * (wave + 1) / NW);
+  // 1. counts per (wavefront, centre)
+  for (int p0 = s0; p0 < s1; p0 += 256) {
+    int u4[4];
+    bool m4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int p = p0 + 4 * lane + k;
+      m4[k] = p < s1;
+      u4[k] = int(idh[m4[k] ? p : s1 - 1]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint64_t same = same_centre(m4[k], u4[k]);
+      const int cnt = __popcll(same), rk = rank_of(same);
+      if (m4[k] && rk == cnt - 1) off[wave][u4[k]] += uint32_t(cnt);
+    }
+  }
+  __syncthreads();
+  // 2. starts over the centres (thread t for centre t < C <= 256), then every
+  // wavefront's write offset per centre in wavefront order
+  {
+    const int t = threadIdx.x;
+    uint32_t tot = 0u;
+    if (t < C)
+      for (int w = 0; w < NW; ++w) tot += off[w][t];
+    uint32_t inc = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t v = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += v;
+    }
+    if (lane == 63 && wave < 4) wsum[wave] = inc;
+    __syncthreads();
+    uint32_t base = 0u;
+    for (int w = 0; w < wave && w < 4; ++w) base += wsum[w];
+    const uint32_t excl = base + inc - tot;
+    if (t < C) {
+      starts[int64_t(h) * (C + 1) + t] = excl;
+      uint32_t run = excl;
+      for (int w = 0; w < NW; ++w) {
+        const uint32_t c = off[w][t];
+        off[w][t] = run;
+        run += c;
+      }
+    }
+    if (t == C - 1) starts[int64_t(h) * (C + 1) + C] = excl + tot;
+  }
+  __syncthreads();
+  // 3. scatter of the token indices, in the order of step 1
+  for (int p0 = s0; p0 < s1; p0 += 256) {
+    int u4[4];
+    bool m4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int p = p0 + 4 * lane + k;
+      m4[k] = p < s1;
+      u4[k] = int(idh[m4[k] ? p : s1 - 1]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint64_t same = same_centre(m4[k], u4[k]);
+      const int cnt = __popcll(same), below = rank_of(same);
+      const uint32_t o = m4[k] ? off[wave][u4[k]] : 0u;
+      if (m4[k]) lh[o + uint32_t(below)] = uint32_t(p0 + 4 * lane + k);
+      if (m4[k] && below == cnt - 1) off[wave][u4[k]] = o + uint32_t(cnt);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_assign(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C, const void* cent,
@@ -856,48 +984,72 @@ hipError_t run_kmeans_update(int heads, int64_t n, const void* x, int C, void* c
   return hipGetLastError();
 }
 
+// Long heads, when there are enough of them to fill the chip with one sorting
+// workgroup each, have their member lists sorted once per head into the
+// workspace (member_lists_kernel) rather than by every workgroup of the head in
+// LDS (heads up to kSortedUpdateMaxTokens) or found by a scan per centre (longer
+// heads): 40 heads x 32760 tokens 291 -> 151-183 us; with 12 heads the
+// per-head sort leaves most of the chip idle and the other paths are faster.
+bool update_global_lists(int heads, int64_t n) { return n > kGlobalListTokens && heads >= kGlobalListHeads; }
+
 size_t kmeans_update_workspace(int heads, int64_t n, int C) {
-  (void)heads;
-  (void)n;
-  (void)C;
-  return 256;                                 // reserved; the update keeps its lists in LDS
+  if (!update_global_lists(heads, n)) return 256;     // reserved; the lists live in LDS
+  return size_t(heads) * size_t(n) * 4 + size_t(heads) * size_t(C + 1) * 4 + 256;
 }
 
-size_t sorted_update_lds(int64_t n, int CG, int dim) {
-  const size_t npad = (size_t(n) + 15) & ~size_t(15);
-  const size_t lpad = (2 * size_t(n) + 15) & ~size_t(15);
+size_t sorted_update_lds(int64_t n, int CG, int dim, bool gl) {
+  const size_t npad = gl ? 0 : (size_t(n) + 15) & ~size_t(15);
+  const size_t lpad = gl ? 0 : (2 * size_t(n) + 15) & ~size_t(15);
   return ((npad + lpad + 4 * (8 * size_t(CG) + CG + 1 + 16 + 8) + 15) & ~size_t(15)) + 16 * size_t(dim) * 8;
 }
 
 template <typename T, int D>
 hipError_t run_kmeans_update_sorted(int heads, int64_t n, const void* x, int C, void* cent, const uint8_t* ids,
-                                    hipStream_t st) {
+                                    void* ws, hipStream_t st) {
   // workgroups per head: enough for about kUpdateMinGroups in all, at most 16
   // (groups of at least 16 centres)
   int S = int((kUpdateMinGroups + heads - 1) / heads);
   S = S < 1 ? 1 : (S > 16 ? 16 : S);
   const int CG = (C + S - 1) / S;
-  const size_t lds = sorted_update_lds(n, CG, D);
-  if (lds > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kmeans_update_sorted_kernel<T, D>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  const bool gl = update_global_lists(heads, n);
+  uint32_t* glists = nullptr;
+  uint32_t* gstarts = nullptr;
+  if (gl) {
+    glists = static_cast<uint32_t*>(ws);
+    gstarts = glists + int64_t(heads) * n;
+    hipLaunchKernelGGL((member_lists_kernel<16>), dim3(unsigned(heads)), dim3(1024), 0, st, ids, C, int(n), glists,
+                       gstarts);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((kmeans_update_sorted_kernel<T, D>), dim3(unsigned((C + CG - 1) / CG), unsigned(heads)),
-                     dim3(512), lds, st, static_cast<const T*>(x), static_cast<T*>(cent), ids, C, CG, int(n));
+  const size_t lds = sorted_update_lds(n, CG, D, gl);
+  const void* fn = gl ? reinterpret_cast<const void*>(&kmeans_update_sorted_kernel<T, D, true>)
+                      : reinterpret_cast<const void*>(&kmeans_update_sorted_kernel<T, D, false>);
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid(unsigned((C + CG - 1) / CG), unsigned(heads));
+  if (gl)
+    hipLaunchKernelGGL((kmeans_update_sorted_kernel<T, D, true>), grid, dim3(512), lds, st, static_cast<const T*>(x),
+                       static_cast<T*>(cent), ids, C, CG, int(n), glists, gstarts);
+  else
+    hipLaunchKernelGGL((kmeans_update_sorted_kernel<T, D, false>), grid, dim3(512), lds, st, static_cast<const T*>(x),
+                       static_cast<T*>(cent), ids, C, CG, int(n), nullptr, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_kmeans_update(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C, void* cent,
                                 const uint8_t* ids, void* ws, hipStream_t st) {
-  (void)ws;
   if (heads == 0 || n == 0) return hipSuccess;
   if (n >= (int64_t(1) << 31)) return hipErrorInvalidValue;   // token indices are 32-bit in the lists
-  if (n <= kSortedUpdateMaxTokens) {
-    if (dt == KVC_BF16 && dim == 128) return run_kmeans_update_sorted<bf16_t, 128>(heads, n, x, C, cent, ids, st);
-    if (dt == KVC_BF16 && dim == 64) return run_kmeans_update_sorted<bf16_t, 64>(heads, n, x, C, cent, ids, st);
-    if (dt == KVC_F32 && dim == 128) return run_kmeans_update_sorted<float, 128>(heads, n, x, C, cent, ids, st);
-    if (dt == KVC_F32 && dim == 64) return run_kmeans_update_sorted<float, 64>(heads, n, x, C, cent, ids, st);
+  const bool gl = update_global_lists(heads, n);
+  if (gl && ws == nullptr) return hipErrorInvalidValue;
+  if (gl || n <= kSortedUpdateMaxTokens) {
+    if (dt == KVC_BF16 && dim == 128) return run_kmeans_update_sorted<bf16_t, 128>(heads, n, x, C, cent, ids, ws, st);
+    if (dt == KVC_BF16 && dim == 64) return run_kmeans_update_sorted<bf16_t, 64>(heads, n, x, C, cent, ids, ws, st);
+    if (dt == KVC_F32 && dim == 128) return run_kmeans_update_sorted<float, 128>(heads, n, x, C, cent, ids, ws, st);
+    if (dt == KVC_F32 && dim == 64) return run_kmeans_update_sorted<float, 64>(heads, n, x, C, cent, ids, ws, st);
     return hipErrorInvalidValue;
   }
   if (dt == KVC_BF16 && dim == 128) return run_kmeans_update<bf16_t, 128>(heads, n, x, C, cent, ids, st);

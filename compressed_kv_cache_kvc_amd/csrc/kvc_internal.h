@@ -49,13 +49,17 @@ hipError_t launch_encode(int heads, int64_t n, int dim, kvc_dtype dt, const void
 hipError_t launch_assign(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C,
                          const void* cent, uint8_t* ids, hipStream_t st);
 constexpr int kAssignMinGroups = 1024;  // assignment workgroups a launch aims for (2 per compute unit, 2 rounds)
-// k-means update (per-centre means over the members in token order); ws of
-// kmeans_update_workspace(heads, n, C) bytes is reserved (the lists live in LDS).
+// k-means update (per-centre means over the members in a fixed order); ws of
+// kmeans_update_workspace(heads, n, C) bytes holds the member lists of long
+// heads (update_global_lists) and is otherwise reserved.
 hipError_t launch_kmeans_update(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C,
                                 void* cent, const uint8_t* ids, void* ws, hipStream_t st);
 size_t kmeans_update_workspace(int heads, int64_t n, int C);
+bool update_global_lists(int heads, int64_t n);
 constexpr int kScanChunk = 32768;      // ids per LDS chunk of the k-means update (long heads)
 constexpr int kSortedUpdateMaxTokens = 32768;   // heads up to this length: member lists sorted in LDS
+constexpr int kGlobalListTokens = 16384;        // longer heads, at least kGlobalListHeads of them:
+constexpr int kGlobalListHeads = 32;            // member lists sorted once per head in the workspace
 constexpr int kUpdateMinGroups = 1024;          // centre-update workgroups a launch aims for
 
 // Query-aware assignment (QSAC) of key tokens; n_cand in {1, 2, 4, 8}, group 16 or 32;

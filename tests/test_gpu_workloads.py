@@ -140,6 +140,41 @@ def test_assign_and_update_full_size(name):
     assert updated >= 1
 
 
+def test_update_with_per_head_member_lists():
+    """34 heads x 17160 tokens (11 latent frames): long and numerous enough heads for the update to
+    sort each head's member lists once in the workspace; 100 centres (centre
+    groups of 7, the last one ragged) with one duplicated centre (no members:
+    it keeps its value).  Centres after one Lloyd iteration bit for bit against
+    the oracle on sampled heads whose ids equal the oracle's."""
+    from concurrent.futures import ThreadPoolExecutor
+    cfg = synth.get_config("larger_backbone")
+    H, N, C = 34, 17160, 100
+    x = synth.AR1Stream(cfg, "v", heads=H, device=DEV).tokens(N)
+    cent0 = synth.forgy_init(x, C, 29)
+    cent0[:, C - 1] = cent0[:, 5]
+    assert kvc().library().kvc_fit_assign_workspace_bytes(H, N, 128, C) > 4 * H * N
+    c1_g = cent0.clone()
+    ids_g = kvc().fit_assign(x, cent0.clone(), n_iter=0).cpu().numpy()
+    kvc().fit_assign(x, c1_g, n_iter=1)
+    torch.cuda.synchronize()
+    sample = [0, H // 2, H - 1]
+    xs, cs, c1s = np32(x[sample]), np32(cent0[sample]), np32(c1_g[sample])
+    assert np.array_equal(c1s[:, C - 1].view(np.uint32), cs[:, C - 1].view(np.uint32))
+
+    def one(i):
+        h = sample[i]
+        ref0 = oracle.assign(xs[i], cs[i])
+        _, differ = check_ids(ids_g[h].astype(np.int64), xs[i], cs[i], what=f"head {h}", ref=ref0)
+        if differ:
+            return False
+        c1, _ = oracle.fit(xs[i], cs[i], n_iter=1, storage="bf16")
+        assert np.array_equal(c1s[i].view(np.uint32), c1.view(np.uint32)), f"head {h}: centres"
+        return True
+
+    with ThreadPoolExecutor(max_workers=len(sample)) as ex:
+        assert sum(ex.map(one, range(len(sample)))) >= 1
+
+
 # ------------------------------------------------------------------------------ encode, full size
 @pytest.mark.parametrize("name", ["self_forcing_layer", "long_history", "larger_backbone", "streaming"])
 def test_encode_full_size(name):
