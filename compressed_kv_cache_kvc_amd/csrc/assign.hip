@@ -838,10 +838,11 @@ __global__ __launch_bounds__(512) void kmeans_update_sorted_kernel(const T* __re
 // counting sort of the head's tokens by centre id, written to the caller's
 // workspace as starts[u] (members of the centres before u; starts[C] = n) and
 // lists[starts[u] ..] (the token indices of centre u's members).  One workgroup
-// of NW wavefronts per head; wavefront w takes the w-th of NW equal token
-// ranges and walks it 256 tokens at a time, lane l holding tokens p + 4l .. p +
-// 4l + 3 and the four steps of 64 taking token p + 4l + k in step k.  Counting
-// and scattering walk in the same order, so the order inside a centre's list is
+// of NW wavefronts per head; wavefront w takes the w-th of NW token ranges (cut
+// at multiples of 4) and walks it 1024 tokens at a time, lane l holding tokens p
+// + 16l .. p + 16l + 15 (four 32-bit loads when the ids are 4-byte aligned) and
+// the 16 steps of 64 taking token p + 16l + k in step k.  Counting and
+// scattering walk in the same order, so the order inside a centre's list is
 // fixed (token order within a step, steps in walk order, ranges in wavefront
 // order) and the sums over it are deterministic.
 template <int NW>
@@ -870,24 +871,47 @@ __global__ __launch_bounds__(NW * 64) void member_lists_kernel(const uint8_t* __
     }
     return same;
   };
-  const int s0 = int(int64_t(n) * wave / NW), s1 = int(int64_t(n) * (wave + 1) / NW);
+  const int s0 = wave == 0 ? 0 : int((int64_t(n) * wave / NW) & ~int64_t(3));
+  const int s1 = wave == NW - 1 ? n : int((int64_t(n) * (wave + 1) / NW) & ~int64_t(3));
+  const bool words = ((reinterpret_cast<uintptr_t>(idh) | uintptr_t(n)) & 3) == 0;   // wave-uniform
+  // calls fn(valid, centre, token) for the steps of the walk, in walk order
+  auto walk = [&](auto&& fn) {
+    for (int p0 = s0; p0 < s1; p0 += 1024) {
+      const int q = p0 + 16 * lane;
+      uint32_t w[4];
+      if (words) {
+        // the word holding the last token of the range bounds every read
+        const int qmax = (s1 - 1) & ~3;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int a = q + 4 * j < qmax ? q + 4 * j : qmax;
+          w[j] = *reinterpret_cast<const uint32_t*>(idh + a);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t v = 0u;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int pe = q + 4 * j + e;
+            v |= uint32_t(idh[pe < s1 ? pe : s1 - 1]) << (8 * e);
+          }
+          w[j] = v;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int p = q + k;
+        fn(p < s1, int((w[k >> 2] >> (8 * (k & 3))) & 0xffu), p);
+      }
+    }
+  };
   // 1. counts per (wavefront, centre)
-  for (int p0 = s0; p0 < s1; p0 += 256) {
-    int u4[4];
-    bool m4[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int p = p0 + 4 * lane + k;
-      m4[k] = p < s1;
-      u4[k] = int(idh[m4[k] ? p : s1 - 1]);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint64_t same = same_centre(m4[k], u4[k]);
-      const int cnt = __popcll(same), rk = rank_of(same);
-      if (m4[k] && rk == cnt - 1) off[wave][u4[k]] += uint32_t(cnt);
-    }
-  }
+  walk([&](bool m, int u, int) {
+    const uint64_t same = same_centre(m, u);
+    const int cnt = __popcll(same), rk = rank_of(same);
+    if (m && rk == cnt - 1) off[wave][u] += uint32_t(cnt);
+  });
   __syncthreads();
   // 2. starts over the centres (thread t for centre t < C <= 256), then every
   // wavefront's write offset per centre in wavefront order
@@ -920,24 +944,13 @@ __global__ __launch_bounds__(NW * 64) void member_lists_kernel(const uint8_t* __
   }
   __syncthreads();
   // 3. scatter of the token indices, in the order of step 1
-  for (int p0 = s0; p0 < s1; p0 += 256) {
-    int u4[4];
-    bool m4[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int p = p0 + 4 * lane + k;
-      m4[k] = p < s1;
-      u4[k] = int(idh[m4[k] ? p : s1 - 1]);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint64_t same = same_centre(m4[k], u4[k]);
-      const int cnt = __popcll(same), below = rank_of(same);
-      const uint32_t o = m4[k] ? off[wave][u4[k]] : 0u;
-      if (m4[k]) lh[o + uint32_t(below)] = uint32_t(p0 + 4 * lane + k);
-      if (m4[k] && below == cnt - 1) off[wave][u4[k]] = o + uint32_t(cnt);
-    }
-  }
+  walk([&](bool m, int u, int p) {
+    const uint64_t same = same_centre(m, u);
+    const int cnt = __popcll(same), below = rank_of(same);
+    const uint32_t o = m ? off[wave][u] : 0u;
+    if (m) lh[o + uint32_t(below)] = uint32_t(p);
+    if (m && below == cnt - 1) off[wave][u] = o + uint32_t(cnt);
+  });
 }
 
 }  // namespace

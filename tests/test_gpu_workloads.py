@@ -140,16 +140,22 @@ def test_assign_and_update_full_size(name):
     assert updated >= 1
 
 
-def test_update_with_per_head_member_lists():
-    """34 heads x 17160 tokens (11 latent frames): long and numerous enough heads for the update to
-    sort each head's member lists once in the workspace; 100 centres (centre
+@pytest.mark.parametrize("H,N,stream", [(34, 17160, True), (32, 16390, False)])
+def test_update_with_per_head_member_lists(H, N, stream):
+    """Long and numerous enough heads for the update to sort each head's member
+    lists once in the workspace: 34 heads x 17160 tokens of the synthetic stream
+    (11 latent frames), and 32 heads x 16390 random tokens (a length that is not
+    a multiple of 4: the sort reads the ids byte by byte); 100 centres (centre
     groups of 7, the last one ragged) with one duplicated centre (no members:
     it keeps its value).  Centres after one Lloyd iteration bit for bit against
     the oracle on sampled heads whose ids equal the oracle's."""
     from concurrent.futures import ThreadPoolExecutor
-    cfg = synth.get_config("larger_backbone")
-    H, N, C = 34, 17160, 100
-    x = synth.AR1Stream(cfg, "v", heads=H, device=DEV).tokens(N)
+    C = 100
+    if stream:
+        x = synth.AR1Stream(synth.get_config("larger_backbone"), "v", heads=H, device=DEV).tokens(N)
+    else:
+        g = torch.Generator().manual_seed(31)
+        x = torch.randn(H, N, 128, generator=g).to(torch.bfloat16).to(DEV)
     cent0 = synth.forgy_init(x, C, 29)
     cent0[:, C - 1] = cent0[:, 5]
     assert kvc().library().kvc_fit_assign_workspace_bytes(H, N, 128, C) > 4 * H * N
