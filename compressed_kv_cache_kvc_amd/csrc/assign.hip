@@ -455,133 +455,6 @@ __device__ __forceinline__ uint32_t f64_to_bits_rne(double d) {
   return (sign << SIGN_SHIFT) | bits;
 }
 
-// One wavefront per (head, centre): the members' rows are added in fp64 in token
-// order.  The head's ids pass through LDS in chunks of kScanChunk tokens, shared
-// by the workgroup's four wavefronts; each wavefront finds its centre's members 64
-// ids at a time (a ballot; slots in token order by mbcnt), lists up to 64 of them
-// in LDS and then adds their rows in that order with BATCH row loads in flight.
-// The order of the additions is fixed, so the result is deterministic; the centre
-// becomes the mean (one fp64 division) rounded to nearest even in the storage
-// type, and a centre without members keeps its value.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void kmeans_update_kernel(const T* __restrict__ x, T* __restrict__ cent,
-                                                            const uint8_t* __restrict__ ids, int C, int64_t n) {
-  constexpr int PER = D / 64;                 // channels per lane
-  constexpr int WPR = PER * int(sizeof(T)) / 4 > 0 ? PER * int(sizeof(T)) / 4 : 1;   // 32-bit words per lane and row
-  constexpr int BATCH = 64 / WPR < 64 ? 64 / WPR : 64;   // rows in flight (64 registers of raw words)
-  __shared__ __attribute__((aligned(16))) uint8_t sid[kScanChunk];
-  __shared__ int slist[4][256];
-  const int lane = threadIdx.x % 64;
-  const int wave = threadIdx.x / 64;
-  const int c = blockIdx.x * 4 + wave;
-  const int h = blockIdx.y;
-  const bool active = c < C;                  // wave-uniform; every wavefront takes the barriers
-  const uint8_t* idh = ids + int64_t(h) * n;
-  const T* xh = x + int64_t(h) * n * D + lane * PER;
-  double acc[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.0;
-  int64_t cnt = 0;
-  int nl = 0;                                 // members listed, not yet added
-  // lane's channels of a row
-  auto load_raw = [&](const T* row, uint32_t (&w)[WPR]) {
-    if constexpr (sizeof(T) == 2 && PER == 1) w[0] = reinterpret_cast<const uint16_t*>(row)[0];
-    else {
-#pragma unroll
-      for (int q = 0; q < WPR; ++q) w[q] = reinterpret_cast<const uint32_t*>(row)[q];
-    }
-  };
-  auto value = [&](const uint32_t (&w)[WPR], int i) -> float {
-    if constexpr (sizeof(T) == 2) {
-      if constexpr (PER == 1) return __uint_as_float(w[0] << 16);
-      else return (i & 1) ? bf16_hi(w[i / 2]) : bf16_lo(w[i / 2]);
-    } else {
-      return __uint_as_float(w[i]);
-    }
-  };
-  auto flush = [&]() {                        // add the listed rows, in list order
-    for (int u0 = 0; u0 < nl; u0 += BATCH) {
-      uint32_t w[BATCH][WPR];
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const int j = slist[wave][u0 + u < nl ? u0 + u : nl - 1];
-        load_raw(xh + int64_t(j) * D, w[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u)
-        if (u0 + u < nl) {
-#pragma unroll
-          for (int i = 0; i < PER; ++i) acc[i] = __dadd_rn(acc[i], double(value(w[u], i)));
-        }
-    }
-    nl = 0;
-  };
-  for (int64_t c0 = 0; c0 < n; c0 += kScanChunk) {
-    const int len = int(n - c0 < kScanChunk ? n - c0 : kScanChunk);
-    __syncthreads();                          // the previous chunk is scanned
-    if (((reinterpret_cast<uintptr_t>(idh + c0)) & 3) == 0) {
-      const int len4 = len / 4;
-      for (int i = threadIdx.x; i < len4; i += 256)
-        reinterpret_cast<uint32_t*>(sid)[i] = reinterpret_cast<const uint32_t*>(idh + c0)[i];
-      for (int i = 4 * len4 + threadIdx.x; i < len; i += 256) sid[i] = idh[c0 + i];
-    } else {
-      for (int i = threadIdx.x; i < len; i += 256) sid[i] = idh[c0 + i];
-    }
-    __syncthreads();
-    if (active) {
-      // Windows of 256 ids, four ids (one 32-bit word) per lane, lane l holding
-      // ids 4l..4l+3; four windows read at once, then taken in token order.  A
-      // byte equal to c is flagged exactly: with x = word ^ (c in every byte),
-      // ((x & 0x7f..) + 0x7f..) | x has its top bit clear only in zero bytes
-      // (no carry crosses a byte).  Flags past the end of the chunk are dropped.
-      const uint32_t cc = uint32_t(c) * 0x01010101u;
-      auto rank_of = [](uint64_t m) {
-        return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
-      };
-      for (int p0 = 0; p0 < len; p0 += 1024) {
-        uint32_t wv[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int p = p0 + 256 * k + 4 * lane;
-          wv[k] = p < len ? reinterpret_cast<const uint32_t*>(sid)[p >> 2] : 0u;
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int p = p0 + 256 * k + 4 * lane;
-          const uint32_t x = wv[k] ^ cc;
-          uint32_t z = ~(((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x) & 0x80808080u;
-          const int rem = len - p;
-          if (rem < 4) z &= rem <= 0 ? 0u : (0x80808080u >> (8 * (4 - rem)));
-          if (__ballot(z != 0u)) {
-            // members of this window: lane prefix of the per-lane counts (0..4)
-            // from three ballots of the count's bits
-            const int k1 = __popc(z);
-            const uint64_t b0 = __ballot(k1 & 1), b1 = __ballot(k1 & 2), b2 = __ballot(k1 & 4);
-            const int tot = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
-            if (nl + tot > 64) flush();
-            int pos = nl + rank_of(b0) + 2 * rank_of(b1) + 4 * rank_of(b2);
-            for (uint32_t zz = z; zz != 0u; zz &= zz - 1u) slist[wave][pos++] = int(c0 + p + (__builtin_ctz(zz) >> 3));
-            nl += tot;
-            cnt += tot;
-          }
-        }
-      }
-    }
-  }
-  if (!active) return;
-  flush();
-  if (cnt == 0) return;                       // empty cluster keeps its centre
-  T* dst = cent + (int64_t(h) * C + c) * D + lane * PER;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const double mean = __ddiv_rn(acc[i], double(cnt));
-    if constexpr (sizeof(T) == 2)
-      reinterpret_cast<uint16_t*>(dst)[i] = static_cast<uint16_t>(f64_to_bits_rne<8>(mean));
-    else
-      reinterpret_cast<uint32_t*>(dst)[i] = f64_to_bits_rne<24>(mean);
-  }
-}
-
 // Centre update from member lists sorted in LDS.  One workgroup of 8
 // wavefronts per (head, group of CG consecutive centres); the head's ids (at
 // most kSortedUpdateMaxTokens) are staged in LDS once.
@@ -837,27 +710,34 @@ __global__ __launch_bounds__(512) void kmeans_update_sorted_kernel(const T* __re
 // Member lists of a whole head for the centre update of long heads: a stable
 // counting sort of the head's tokens by centre id, written to the caller's
 // workspace as starts[u] (members of the centres before u; starts[C] = n) and
-// lists[starts[u] ..] (the token indices of centre u's members).  One workgroup
-// of NW wavefronts per head; wavefront w takes the w-th of NW token ranges (cut
-// at multiples of 4) and walks it 1024 tokens at a time, lane l holding tokens p
-// + 16l .. p + 16l + 15 (four 32-bit loads when the ids are 4-byte aligned) and
-// the 16 steps of 64 taking token p + 16l + k in step k.  Counting and
-// scattering walk in the same order, so the order inside a centre's list is
-// fixed (token order within a step, steps in walk order, ranges in wavefront
-// order) and the sums over it are deterministic.
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void member_lists_kernel(const uint8_t* __restrict__ ids, int C, int n,
+// lists[starts[u] ..] (the token indices of centre u's members).  The head is cut
+// into P chunks (cut at multiples of 4) and each chunk into NW wavefront ranges
+// (also at multiples of 4); wavefront w walks its range 1024 tokens at a time,
+// lane l holding tokens p + 16l .. p + 16l + 15 (four 32-bit loads when the ids
+// are 4-byte aligned) and the 16 steps of 64 taking token p + 16l + k in step k.
+// Counting and scattering walk in the same order, so the order inside a centre's
+// list is fixed (token order within a step, steps in walk order, ranges in
+// wavefront order, chunks in token order) and the sums over it deterministic.
+//   PHASE 0: P = 1, one workgroup per head counts, takes the prefix and scatters;
+//   PHASE 1: workgroup (p, h) counts chunk p: wcnt[h][p][w][u] per wavefront and
+//            ctot[h][p][u] over the chunk;
+//   PHASE 2: workgroup (p, h) takes the prefix over the centres from ctot (chunk
+//            0 writes starts), its wavefronts' offsets from wcnt, and scatters.
+template <int NW, int PHASE>
+__global__ __launch_bounds__(NW * 64) void member_lists_kernel(const uint8_t* __restrict__ ids, int C, int n, int P,
                                                                uint32_t* __restrict__ lists,
-                                                               uint32_t* __restrict__ starts) {
+                                                               uint32_t* __restrict__ starts,
+                                                               uint32_t* __restrict__ wcnt,
+                                                               uint32_t* __restrict__ ctot) {
+  static_assert(NW * 64 >= 256, "one thread per centre in the prefix");
   __shared__ uint32_t off[NW][256];
   __shared__ uint32_t wsum[4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int h = blockIdx.x;
+  const int p = blockIdx.x;
+  const int h = blockIdx.y;
   const uint8_t* idh = ids + int64_t(h) * n;
   uint32_t* lh = lists + int64_t(h) * n;
-  for (int i = threadIdx.x; i < NW * 256; i += NW * 64) (&off[0][0])[i] = 0u;
-  __syncthreads();
   auto rank_of = [](uint64_t m) {
     return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
   };
@@ -871,8 +751,11 @@ __global__ __launch_bounds__(NW * 64) void member_lists_kernel(const uint8_t* __
     }
     return same;
   };
-  const int s0 = wave == 0 ? 0 : int((int64_t(n) * wave / NW) & ~int64_t(3));
-  const int s1 = wave == NW - 1 ? n : int((int64_t(n) * (wave + 1) / NW) & ~int64_t(3));
+  const int cs0 = p == 0 ? 0 : int((int64_t(n) * p / P) & ~int64_t(3));
+  const int cs1 = p == P - 1 ? n : int((int64_t(n) * (p + 1) / P) & ~int64_t(3));
+  const int len = cs1 - cs0;
+  const int s0 = cs0 + (wave == 0 ? 0 : int((int64_t(len) * wave / NW) & ~int64_t(3)));
+  const int s1 = wave == NW - 1 ? cs1 : cs0 + int((int64_t(len) * (wave + 1) / NW) & ~int64_t(3));
   const bool words = ((reinterpret_cast<uintptr_t>(idh) | uintptr_t(n)) & 3) == 0;   // wave-uniform
   // calls fn(valid, centre, token) for the steps of the walk, in walk order
   auto walk = [&](auto&& fn) {
@@ -901,54 +784,79 @@ __global__ __launch_bounds__(NW * 64) void member_lists_kernel(const uint8_t* __
       }
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        const int p = q + k;
-        fn(p < s1, int((w[k >> 2] >> (8 * (k & 3))) & 0xffu), p);
+        const int pk = q + k;
+        const int u = int((w[k >> 2] >> (8 * (k & 3))) & 0xffu);
+        fn(pk < s1 && u < C, u, pk);     // an id >= C belongs to no centre
       }
     }
   };
-  // 1. counts per (wavefront, centre)
-  walk([&](bool m, int u, int) {
-    const uint64_t same = same_centre(m, u);
-    const int cnt = __popcll(same), rk = rank_of(same);
-    if (m && rk == cnt - 1) off[wave][u] += uint32_t(cnt);
-  });
-  __syncthreads();
-  // 2. starts over the centres (thread t for centre t < C <= 256), then every
-  // wavefront's write offset per centre in wavefront order
-  {
-    const int t = threadIdx.x;
-    uint32_t tot = 0u;
-    if (t < C)
-      for (int w = 0; w < NW; ++w) tot += off[w][t];
-    uint32_t inc = tot;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t v = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += v;
-    }
-    if (lane == 63 && wave < 4) wsum[wave] = inc;
+  const int t = threadIdx.x;
+  const int64_t hp = int64_t(h) * P + p;
+  if constexpr (PHASE != 2) {
+    // 1. counts per (wavefront, centre)
+    for (int i = t; i < NW * 256; i += NW * 64) (&off[0][0])[i] = 0u;
     __syncthreads();
-    uint32_t base = 0u;
-    for (int w = 0; w < wave && w < 4; ++w) base += wsum[w];
-    const uint32_t excl = base + inc - tot;
-    if (t < C) {
-      starts[int64_t(h) * (C + 1) + t] = excl;
-      uint32_t run = excl;
-      for (int w = 0; w < NW; ++w) {
-        const uint32_t c = off[w][t];
-        off[w][t] = run;
-        run += c;
+    walk([&](bool m, int u, int) {
+      const uint64_t same = same_centre(m, u);
+      const int cnt = __popcll(same), rk = rank_of(same);
+      if (m && rk == cnt - 1) off[wave][u] += uint32_t(cnt);
+    });
+    __syncthreads();
+    if constexpr (PHASE == 1) {
+      if (t < C) {
+        uint32_t tot = 0u;
+        for (int w = 0; w < NW; ++w) {
+          wcnt[(hp * NW + w) * C + t] = off[w][t];
+          tot += off[w][t];
+        }
+        ctot[hp * C + t] = tot;
+      }
+      return;
+    }
+  }
+  // 2. starts over the centres (thread t for centre t < C <= 256), then every
+  // wavefront's write offset per centre: chunks before this one, then
+  // wavefronts before this one
+  uint32_t tot = 0u, before = 0u;
+  if (t < C) {
+    if constexpr (PHASE == 0) {
+      for (int w = 0; w < NW; ++w) tot += off[w][t];
+    } else {
+      for (int q = 0; q < P; ++q) {
+        const uint32_t c = ctot[(int64_t(h) * P + q) * C + t];
+        if (q < p) before += c;
+        tot += c;
       }
     }
-    if (t == C - 1) starts[int64_t(h) * (C + 1) + C] = excl + tot;
   }
+  uint32_t inc = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t v = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += v;
+  }
+  if (lane == 63 && wave < 4) wsum[wave] = inc;
+  __syncthreads();
+  uint32_t base = 0u;
+  for (int w = 0; w < wave && w < 4; ++w) base += wsum[w];
+  const uint32_t excl = base + inc - tot;
+  if (t < C) {
+    if (p == 0) starts[int64_t(h) * (C + 1) + t] = excl;
+    uint32_t run = excl + before;
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t c = PHASE == 0 ? off[w][t] : wcnt[(hp * NW + w) * C + t];
+      off[w][t] = run;
+      run += c;
+    }
+  }
+  if (p == 0 && t == C - 1) starts[int64_t(h) * (C + 1) + C] = excl + tot;
   __syncthreads();
   // 3. scatter of the token indices, in the order of step 1
-  walk([&](bool m, int u, int p) {
+  walk([&](bool m, int u, int pk) {
     const uint64_t same = same_centre(m, u);
     const int cnt = __popcll(same), below = rank_of(same);
     const uint32_t o = m ? off[wave][u] : 0u;
-    if (m) lh[o + uint32_t(below)] = uint32_t(p);
+    if (m) lh[o + uint32_t(below)] = uint32_t(pk);
     if (m && below == cnt - 1) off[wave][u] = o + uint32_t(cnt);
   });
 }
@@ -989,25 +897,31 @@ hipError_t launch_assign(int heads, int64_t n, int dim, kvc_dtype dt, const void
   return hipGetLastError();
 }
 
-template <typename T, int D>
-hipError_t run_kmeans_update(int heads, int64_t n, const void* x, int C, void* cent, const uint8_t* ids,
-                             hipStream_t st) {
-  hipLaunchKernelGGL((kmeans_update_kernel<T, D>), dim3(unsigned((C + 3) / 4), unsigned(heads)), dim3(256), 0, st,
-                     static_cast<const T*>(x), static_cast<T*>(cent), ids, C, n);
-  return hipGetLastError();
+// Heads longer than kSortedUpdateMaxTokens (whose ids do not fit in LDS), and
+// heads longer than kGlobalListTokens when there are at most
+// kGlobalListMaxHeads of them, have their member lists sorted once per head into
+// the workspace (member_lists_kernel) rather than by every workgroup of the head
+// in LDS: with few heads the update splits a head over many workgroups, each of
+// which would sort the whole head again (12 heads x 32760 tokens: 95 -> 50 us;
+// 40 x 32760: 312 -> 138 us; 720 x 4680 stays in LDS, 314 us against 356 us).
+// The sort is cut into chunks of at least kListChunkTokens tokens so that about
+// kListMinGroups workgroups share it when the heads are few.
+bool update_global_lists(int heads, int64_t n) {
+  return n > kSortedUpdateMaxTokens || (n > kGlobalListTokens && heads <= kGlobalListMaxHeads);
 }
 
-// Long heads, when there are enough of them to fill the chip with one sorting
-// workgroup each, have their member lists sorted once per head into the
-// workspace (member_lists_kernel) rather than by every workgroup of the head in
-// LDS (heads up to kSortedUpdateMaxTokens) or found by a scan per centre (longer
-// heads): 40 heads x 32760 tokens 291 -> 151-183 us; with 12 heads the
-// per-head sort leaves most of the chip idle and the other paths are faster.
-bool update_global_lists(int heads, int64_t n) { return n > kGlobalListTokens && heads >= kGlobalListHeads; }
+int member_list_chunks(int heads, int64_t n) {
+  const int64_t want = (kListMinGroups + heads - 1) / heads;
+  const int64_t most = (n + kListChunkTokens - 1) / kListChunkTokens;
+  const int64_t P = want < most ? want : most;
+  return P < 1 ? 1 : int(P);
+}
 
 size_t kmeans_update_workspace(int heads, int64_t n, int C) {
   if (!update_global_lists(heads, n)) return 256;     // reserved; the lists live in LDS
-  return size_t(heads) * size_t(n) * 4 + size_t(heads) * size_t(C + 1) * 4 + 256;
+  const int P = member_list_chunks(heads, n);
+  const size_t counts = P > 1 ? size_t(heads) * size_t(P) * size_t(kListChunkWaves + 1) * size_t(C) * 4 : 0;
+  return size_t(heads) * size_t(n) * 4 + size_t(heads) * size_t(C + 1) * 4 + counts + 256;
 }
 
 size_t sorted_update_lds(int64_t n, int CG, int dim, bool gl) {
@@ -1021,17 +935,31 @@ hipError_t run_kmeans_update_sorted(int heads, int64_t n, const void* x, int C, 
                                     void* ws, hipStream_t st) {
   // workgroups per head: enough for about kUpdateMinGroups in all, at most 16
   // (groups of at least 16 centres)
-  int S = int((kUpdateMinGroups + heads - 1) / heads);
-  S = S < 1 ? 1 : (S > 16 ? 16 : S);
-  const int CG = (C + S - 1) / S;
+  // (groups of at least 16 centres; with global lists, of at least
+  // 256 / kGlobalListMaxSplit, as no workgroup scans the ids)
   const bool gl = update_global_lists(heads, n);
+  const int smax = gl ? kGlobalListMaxSplit : 16;
+  int S = int((kUpdateMinGroups + heads - 1) / heads);
+  S = S < 1 ? 1 : (S > smax ? smax : S);
+  const int CG = (C + S - 1) / S;
   uint32_t* glists = nullptr;
   uint32_t* gstarts = nullptr;
   if (gl) {
     glists = static_cast<uint32_t*>(ws);
     gstarts = glists + int64_t(heads) * n;
-    hipLaunchKernelGGL((member_lists_kernel<16>), dim3(unsigned(heads)), dim3(1024), 0, st, ids, C, int(n), glists,
-                       gstarts);
+    const int P = member_list_chunks(heads, n);
+    if (P == 1) {     // heads enough to fill the chip: one workgroup of 16 wavefronts per head
+      hipLaunchKernelGGL((member_lists_kernel<16, 0>), dim3(1u, unsigned(heads)), dim3(1024), 0, st, ids, C, int(n),
+                         1, glists, gstarts, nullptr, nullptr);
+    } else {
+      uint32_t* wcnt = gstarts + int64_t(heads) * (C + 1);
+      uint32_t* ctot = wcnt + int64_t(heads) * P * kListChunkWaves * C;
+      const dim3 grid(static_cast<unsigned>(P), static_cast<unsigned>(heads));
+      hipLaunchKernelGGL((member_lists_kernel<kListChunkWaves, 1>), grid, dim3(kListChunkWaves * 64), 0, st, ids, C,
+                         int(n), P, glists, gstarts, wcnt, ctot);
+      hipLaunchKernelGGL((member_lists_kernel<kListChunkWaves, 2>), grid, dim3(kListChunkWaves * 64), 0, st, ids, C,
+                         int(n), P, glists, gstarts, wcnt, ctot);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1056,19 +984,11 @@ hipError_t launch_kmeans_update(int heads, int64_t n, int dim, kvc_dtype dt, con
                                 const uint8_t* ids, void* ws, hipStream_t st) {
   if (heads == 0 || n == 0) return hipSuccess;
   if (n >= (int64_t(1) << 31)) return hipErrorInvalidValue;   // token indices are 32-bit in the lists
-  const bool gl = update_global_lists(heads, n);
-  if (gl && ws == nullptr) return hipErrorInvalidValue;
-  if (gl || n <= kSortedUpdateMaxTokens) {
-    if (dt == KVC_BF16 && dim == 128) return run_kmeans_update_sorted<bf16_t, 128>(heads, n, x, C, cent, ids, ws, st);
-    if (dt == KVC_BF16 && dim == 64) return run_kmeans_update_sorted<bf16_t, 64>(heads, n, x, C, cent, ids, ws, st);
-    if (dt == KVC_F32 && dim == 128) return run_kmeans_update_sorted<float, 128>(heads, n, x, C, cent, ids, ws, st);
-    if (dt == KVC_F32 && dim == 64) return run_kmeans_update_sorted<float, 64>(heads, n, x, C, cent, ids, ws, st);
-    return hipErrorInvalidValue;
-  }
-  if (dt == KVC_BF16 && dim == 128) return run_kmeans_update<bf16_t, 128>(heads, n, x, C, cent, ids, st);
-  if (dt == KVC_BF16 && dim == 64) return run_kmeans_update<bf16_t, 64>(heads, n, x, C, cent, ids, st);
-  if (dt == KVC_F32 && dim == 128) return run_kmeans_update<float, 128>(heads, n, x, C, cent, ids, st);
-  if (dt == KVC_F32 && dim == 64) return run_kmeans_update<float, 64>(heads, n, x, C, cent, ids, st);
+  if (update_global_lists(heads, n) && ws == nullptr) return hipErrorInvalidValue;
+  if (dt == KVC_BF16 && dim == 128) return run_kmeans_update_sorted<bf16_t, 128>(heads, n, x, C, cent, ids, ws, st);
+  if (dt == KVC_BF16 && dim == 64) return run_kmeans_update_sorted<bf16_t, 64>(heads, n, x, C, cent, ids, ws, st);
+  if (dt == KVC_F32 && dim == 128) return run_kmeans_update_sorted<float, 128>(heads, n, x, C, cent, ids, ws, st);
+  if (dt == KVC_F32 && dim == 64) return run_kmeans_update_sorted<float, 64>(heads, n, x, C, cent, ids, ws, st);
   return hipErrorInvalidValue;
 }
 

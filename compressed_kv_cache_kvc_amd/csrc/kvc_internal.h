@@ -56,11 +56,14 @@ hipError_t launch_kmeans_update(int heads, int64_t n, int dim, kvc_dtype dt, con
                                 void* cent, const uint8_t* ids, void* ws, hipStream_t st);
 size_t kmeans_update_workspace(int heads, int64_t n, int C);
 bool update_global_lists(int heads, int64_t n);
-constexpr int kScanChunk = 32768;      // ids per LDS chunk of the k-means update (long heads)
-constexpr int kSortedUpdateMaxTokens = 32768;   // heads up to this length: member lists sorted in LDS
-constexpr int kGlobalListTokens = 16384;        // longer heads, at least kGlobalListHeads of them:
-constexpr int kGlobalListHeads = 32;            // member lists sorted once per head in the workspace
+constexpr int kSortedUpdateMaxTokens = 32768;   // heads up to this length: member lists sorted in LDS,
+constexpr int kGlobalListTokens = 8192;         // unless longer than this and at most kGlobalListMaxHeads
+constexpr int kGlobalListMaxHeads = 511;        // of them: then sorted once per head in the workspace
 constexpr int kUpdateMinGroups = 1024;          // centre-update workgroups a launch aims for
+constexpr int kGlobalListMaxSplit = 64;         // workgroups per head of the update over global lists, at most
+constexpr int kListMinGroups = 512;             // member-list sort: workgroups a launch aims for,
+constexpr int kListChunkTokens = 4096;          // chunks of at least this many tokens,
+constexpr int kListChunkWaves = 4;              // of this many wavefronts
 
 // Query-aware assignment (QSAC) of key tokens; n_cand in {1, 2, 4, 8}, group 16 or 32;
 // w [heads][dim] fp32 or NULL (all ones).

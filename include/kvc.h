@@ -97,10 +97,11 @@ typedef struct {
  *   ids_out    [heads][n_tokens]: argmin over centres of the squared L2 distance,
  *              ties to the lowest index.
  *   ws         workspace of at least kvc_fit_assign_workspace_bytes(...) bytes:
- *              with n_tokens > 16384 and heads >= 32 it holds every head's member
- *              lists, sorted once per head (4 * heads * (n_tokens + n_centroids +
- *              1) + 256 bytes); otherwise 256 bytes, reserved (the update keeps
- *              its member lists in LDS).
+ *              with n_tokens > 32768, or n_tokens > 8192 and heads <= 511, it
+ *              holds every head's member lists, sorted once per head (4 * heads
+ *              * (n_tokens + n_centroids + 1) bytes), the sort's per-chunk counts
+ *              when a head is sorted in several chunks, and 256 bytes; otherwise
+ *              256 bytes, reserved (the update keeps its member lists in LDS).
  * dim must be 64 or 128; n_centroids 1..256; n_tokens < 2^31 (token indices
  * are 32-bit); n_tokens >= n_centroids is not required.  Tokens must be finite: a token with a NaN or an infinite value has
  * no finite distance and is assigned id 0 (its codes and the centre update are

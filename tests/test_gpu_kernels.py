@@ -212,8 +212,9 @@ def test_fit_many_heads():
 
 
 def test_fit_long_history_member_list_chunks():
-    # 40000 tokens per head: the ids of the centre update pass through LDS in two
-    # chunks of 32768 tokens, and the sums must continue across them
+    # 40000 tokens in one head, more than the update's LDS takes: the member
+    # lists are sorted in the workspace in 10 chunks (16 centres), and a centre's
+    # list runs across chunk boundaries
     # (seed 16 with these centres has no near-tie token, before or after the update)
     H, N, C, d = 1, 40000, 16, 64
     x = _bf16_tokens(H, N, d, 16)

@@ -99,8 +99,9 @@ def test_tiny_whole_path():
 @pytest.mark.parametrize("name", ["self_forcing_layer", "long_history", "larger_backbone", "streaming"])
 def test_assign_and_update_full_size(name):
     """One assignment and one Lloyd iteration over every head at the workload's
-    full size (long_history: 70200 tokens a head, so the update walks three LDS
-    chunks of ids; larger_backbone: 40 heads x 32760), checked on sampled heads:
+    full size (long_history: 12 heads x 70200 tokens and larger_backbone: 40
+    heads x 32760, whose updates sort member lists in the workspace, 18 and 8
+    chunks a head), checked on sampled heads:
     ids against the oracle's assignment, and, wherever the GPU's ids equal the
     oracle's (a near-tie resolved the other way changes the update's input),
     the updated centres bit for bit and the ids after the update."""
@@ -140,22 +141,25 @@ def test_assign_and_update_full_size(name):
     assert updated >= 1
 
 
-@pytest.mark.parametrize("H,N,stream", [(34, 17160, True), (32, 16390, False)])
+@pytest.mark.parametrize("H,N,stream", [(34, 17160, True), (32, 16390, False), (12, 9362, False),
+                                        (512, 32772, False)])
 def test_update_with_per_head_member_lists(H, N, stream):
-    """Long and numerous enough heads for the update to sort each head's member
-    lists once in the workspace: 34 heads x 17160 tokens of the synthetic stream
-    (11 latent frames), and 32 heads x 16390 random tokens (a length that is not
-    a multiple of 4: the sort reads the ids byte by byte); 100 centres (centre
-    groups of 7, the last one ragged) with one duplicated centre (no members:
-    it keeps its value).  Centres after one Lloyd iteration bit for bit against
-    the oracle on sampled heads whose ids equal the oracle's."""
+    """Heads long enough for the update to sort each head's member lists once in
+    the workspace: 34 heads x 17160 tokens of the synthetic stream (11 latent
+    frames; the sort in 5 chunks a head), 32 heads x 16390 and 12 heads x 9362
+    random tokens (lengths that are not a multiple of 4: the sort reads the ids
+    byte by byte), and 512 heads x 32772 random tokens (longer than the LDS
+    path takes, and heads enough for one sorting workgroup a head); 100 centres
+    with one duplicated centre (no members: it keeps its value).  Centres after
+    one Lloyd iteration bit for bit against the oracle on sampled heads whose
+    ids equal the oracle's."""
     from concurrent.futures import ThreadPoolExecutor
     C = 100
     if stream:
         x = synth.AR1Stream(synth.get_config("larger_backbone"), "v", heads=H, device=DEV).tokens(N)
     else:
-        g = torch.Generator().manual_seed(31)
-        x = torch.randn(H, N, 128, generator=g).to(torch.bfloat16).to(DEV)
+        g = torch.Generator(device=DEV).manual_seed(31)
+        x = torch.randn(H, N, 128, generator=g, device=DEV).to(torch.bfloat16)
     cent0 = synth.forgy_init(x, C, 29)
     cent0[:, C - 1] = cent0[:, 5]
     assert kvc().library().kvc_fit_assign_workspace_bytes(H, N, 128, C) > 4 * H * N
