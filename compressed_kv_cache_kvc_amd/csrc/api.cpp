@@ -262,6 +262,7 @@ kvc_status kvc_fit_assign(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtyp
   try {
     KVC_REQUIRE(heads >= 0 && n_tokens >= 0, KVC_ERR_INVALID_ARG, "heads and n_tokens must be >= 0");
     KVC_REQUIRE(n_tokens < (int64_t(1) << 31), KVC_ERR_INVALID_ARG, "n_tokens must be < 2^31 (32-bit token indices)");
+    KVC_REQUIRE(heads <= 65535, KVC_ERR_UNSUPPORTED, "at most 65535 heads per call");
     KVC_REQUIRE(dim == 64 || dim == 128, KVC_ERR_INVALID_ARG, "dim must be 64 or 128");
     KVC_REQUIRE(valid_dtype(dt), KVC_ERR_INVALID_ARG, "bad dtype");
     KVC_REQUIRE(n_centroids >= 1 && n_centroids <= 256, KVC_ERR_INVALID_ARG, "n_centroids must be in [1, 256]");

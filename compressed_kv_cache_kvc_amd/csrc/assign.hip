@@ -866,35 +866,42 @@ __global__ __launch_bounds__(NW * 64) void member_lists_kernel(const uint8_t* __
 hipError_t launch_assign(int heads, int64_t n, int dim, kvc_dtype dt, const void* x, int C, const void* cent,
                          uint8_t* ids, hipStream_t st) {
   if (heads == 0 || n == 0) return hipSuccess;
-  if (dt == KVC_BF16) {
-    // blocks of 256 tokens per head, shared out over enough workgroups per head
-    // for about kAssignMinGroups workgroups in all (two fit a compute unit), each
-    // taking the same number of consecutive blocks
-    const int64_t blocks = (n + 255) / 256;
-    const int64_t want = (kAssignMinGroups + heads - 1) / heads;
-    const int64_t groups0 = blocks < want ? blocks : want;
-    const int rounds = int((blocks + groups0 - 1) / groups0);
-    const dim3 grid(unsigned((blocks + rounds - 1) / rounds), unsigned(heads));
-    if (dim == 128)
-      hipLaunchKernelGGL((assign_mfma_kernel<128>), grid, dim3(256), 0, st, static_cast<const bf16_t*>(x),
-                         static_cast<const bf16_t*>(cent), C, n, rounds, ids);
-    else if (dim == 64)
-      hipLaunchKernelGGL((assign_mfma_kernel<64>), grid, dim3(256), 0, st, static_cast<const bf16_t*>(x),
-                         static_cast<const bf16_t*>(cent), C, n, rounds, ids);
-    else
-      return hipErrorInvalidValue;
-  } else {
-    const dim3 grid(unsigned((n + 3) / 4), unsigned(heads));
-    if (dim == 128)
-      hipLaunchKernelGGL((assign_exact_kernel<float, 128>), grid, dim3(256), 0, st, static_cast<const float*>(x),
-                         static_cast<const float*>(cent), C, n, ids);
-    else if (dim == 64)
-      hipLaunchKernelGGL((assign_exact_kernel<float, 64>), grid, dim3(256), 0, st, static_cast<const float*>(x),
-                         static_cast<const float*>(cent), C, n, ids);
-    else
-      return hipErrorInvalidValue;
+  if (dim != 128 && dim != 64) return hipErrorInvalidValue;
+  // the grid's second dimension takes the heads, at most 65535 per launch
+  const size_t es = dt == KVC_BF16 ? 2 : 4;
+  for (int h0 = 0; h0 < heads; h0 += 65535) {
+    const int hc = heads - h0 < 65535 ? heads - h0 : 65535;
+    const void* xh = static_cast<const char*>(x) + size_t(h0) * size_t(n) * size_t(dim) * es;
+    const void* ch = static_cast<const char*>(cent) + size_t(h0) * size_t(C) * size_t(dim) * es;
+    uint8_t* ih = ids + size_t(h0) * size_t(n);
+    if (dt == KVC_BF16) {
+      // blocks of 256 tokens per head, shared out over enough workgroups per head
+      // for about kAssignMinGroups workgroups in all (two fit a compute unit), each
+      // taking the same number of consecutive blocks
+      const int64_t blocks = (n + 255) / 256;
+      const int64_t want = (kAssignMinGroups + hc - 1) / hc;
+      const int64_t groups0 = blocks < want ? blocks : want;
+      const int rounds = int((blocks + groups0 - 1) / groups0);
+      const dim3 grid(unsigned((blocks + rounds - 1) / rounds), unsigned(hc));
+      if (dim == 128)
+        hipLaunchKernelGGL((assign_mfma_kernel<128>), grid, dim3(256), 0, st, static_cast<const bf16_t*>(xh),
+                           static_cast<const bf16_t*>(ch), C, n, rounds, ih);
+      else
+        hipLaunchKernelGGL((assign_mfma_kernel<64>), grid, dim3(256), 0, st, static_cast<const bf16_t*>(xh),
+                           static_cast<const bf16_t*>(ch), C, n, rounds, ih);
+    } else {
+      const dim3 grid(unsigned((n + 3) / 4), unsigned(hc));
+      if (dim == 128)
+        hipLaunchKernelGGL((assign_exact_kernel<float, 128>), grid, dim3(256), 0, st, static_cast<const float*>(xh),
+                           static_cast<const float*>(ch), C, n, ih);
+      else
+        hipLaunchKernelGGL((assign_exact_kernel<float, 64>), grid, dim3(256), 0, st, static_cast<const float*>(xh),
+                           static_cast<const float*>(ch), C, n, ih);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 // Heads longer than kSortedUpdateMaxTokens (whose ids do not fit in LDS), and

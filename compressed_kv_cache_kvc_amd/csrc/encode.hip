@@ -248,10 +248,17 @@ hipError_t run_lowdim(int heads, int64_t n, const void* x, int C, const void* ce
   if (n == 0 || heads == 0) return hipSuccess;
   const int tpb = 128;
   const int64_t bx = (n + tpb - 1) / tpb;
-  hipLaunchKernelGGL((encode_lowdim_kernel<T, D, R, G, BITS>), dim3(unsigned(bx), unsigned(heads)), dim3(256),
-                     0, st, static_cast<const T*>(x), static_cast<const T*>(cent), ids, C, n, basis, tpb,
-                     codes, reinterpret_cast<uint32_t*>(meta));
-  return hipGetLastError();
+  // the grid's second dimension takes the heads, at most 65535 per launch
+  for (int h0 = 0; h0 < heads; h0 += 65535) {
+    const int hc = heads - h0 < 65535 ? heads - h0 : 65535;
+    hipLaunchKernelGGL((encode_lowdim_kernel<T, D, R, G, BITS>), dim3(unsigned(bx), unsigned(hc)), dim3(256),
+                       0, st, static_cast<const T*>(x) + int64_t(h0) * n * D, static_cast<const T*>(cent) + int64_t(h0) * C * D,
+                       ids + int64_t(h0) * n, C, n, basis + int64_t(h0) * D * R, tpb,
+                       codes + int64_t(h0) * n * (R * BITS / 8), reinterpret_cast<uint32_t*>(meta) + int64_t(h0) * n * (R / G));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <typename T, int D>

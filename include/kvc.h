@@ -103,7 +103,8 @@ typedef struct {
  *              when a head is sorted in several chunks, and 256 bytes; otherwise
  *              256 bytes, reserved (the update keeps its member lists in LDS).
  * dim must be 64 or 128; n_centroids 1..256; n_tokens < 2^31 (token indices
- * are 32-bit); n_tokens >= n_centroids is not required.  Tokens must be finite: a token with a NaN or an infinite value has
+ * are 32-bit); heads <= 65535 (KVC_ERR_UNSUPPORTED above); n_tokens >=
+ * n_centroids is not required.  Tokens must be finite: a token with a NaN or an infinite value has
  * no finite distance and is assigned id 0 (its codes and the centre update are
  * then meaningless, but every id stays a valid index). */
 kvc_status kvc_fit_assign(int32_t heads, int64_t n_tokens, int32_t dim, kvc_dtype dt,

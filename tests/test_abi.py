@@ -76,6 +76,7 @@ def test_fit_assign_validation(lib):
     assert f(1, 10, 128, 1, P, 300, P, 2, P, P, need, None) == INV
     assert f(1, 10, 128, 1, P, 4, P, -1, P, P, need, None) == INV
     assert f(1, 1 << 31, 128, 1, P, 4, P, 0, P, P, 1 << 40, None) == INV   # 32-bit token indices
+    assert f(65536, 10, 128, 1, P, 4, P, 2, P, P, 1 << 40, None) == UNS      # grid: at most 65535 heads
     assert f(0, 10, 128, 1, None, 4, None, 2, None, None, 0, None) == OK
 
 

@@ -99,6 +99,48 @@ def test_encode_more_heads_than_one_launch_covers(bits, group):
         assert np.array_equal(meta.cpu().numpy()[sel], ref_meta)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_encode_with_assignment_more_heads_than_one_launch_covers(dtype):
+    """65537 heads of 5 tokens, ids left to the call: the assignment inside it
+    also takes at most 65535 heads per launch (the matrix-core kernel for bf16,
+    the exact kernel for fp32).  Ids are checked against the oracle and codes
+    bit-exactly (given those ids) on heads at both ends of each launch."""
+    H, N, d, C, bits, group = 65537, 5, 64, 4, 4, 32
+    g = torch.Generator().manual_seed(23)
+    x = (torch.randn(H, N, d, generator=g) * 2.0).to(dtype)
+    cent = (torch.randn(H, C, d, generator=g) * 2.0).to(dtype)
+    codes, meta, ids = kvc().encode(x.to(DEV), cent.to(DEV), bits, group)
+    torch.cuda.synchronize()
+    sel = np.array([0, 1, 65533, 65534, 65535, 65536])
+    xs, cs = np32(x[sel]), np32(cent[sel])
+    ids_s = ids.cpu().numpy()[sel]
+    for i, h in enumerate(sel):
+        check_ids(ids_s[i], xs[i], cs[i], what=f"head {h}")
+    ref_codes, ref_meta = encode_heads(xs, cs, ids_s.astype(np.int64), bits, group)
+    assert np.array_equal(codes.cpu().numpy()[sel], ref_codes)
+    assert np.array_equal(meta.cpu().numpy()[sel], ref_meta)
+
+
+def test_encode_lowdim_more_heads_than_one_launch_covers():
+    """Coefficient codes over 65537 heads (two launches); seven distinct bases
+    repeat over the heads, so a basis read from the wrong head of the second
+    launch (65535 is not a multiple of 7) changes the codes."""
+    H, N, d, C, rank, bits, group = 65537, 3, 128, 4, 32, 2, 16
+    g = torch.Generator().manual_seed(24)
+    x = (torch.randn(H, N, d, generator=g) * 2.0).to(torch.bfloat16)
+    cent = (torch.randn(H, C, d, generator=g) * 2.0).to(torch.bfloat16)
+    ids = torch.randint(0, C, (H, N), generator=g, dtype=torch.uint8)
+    B = synth.orthonormal_basis(7, d, rank, 25)
+    U = B[torch.arange(H) % 7].contiguous()
+    codes, meta, _ = kvc().encode(x.to(DEV), cent.to(DEV), bits, group, ids=ids.to(DEV), basis=U.to(DEV))
+    torch.cuda.synchronize()
+    sel = np.array([0, 1, 65533, 65534, 65535, 65536])
+    ref_codes, ref_meta = encode_heads(np32(x[sel]), np32(cent[sel]), ids[sel].numpy().astype(np.int64), bits,
+                                       group, U[sel].numpy())
+    assert np.array_equal(codes.cpu().numpy()[sel], ref_codes)
+    assert np.array_equal(meta.cpu().numpy()[sel], ref_meta)
+
+
 @pytest.mark.parametrize("rank,bits,group", [(32, 2, 16), (32, 4, 16), (64, 4, 32), (64, 2, 32)])
 def test_encode_lowdim_bit_exact(rank, bits, group):
     H, N, C, d = 2, 777, 20, 128
