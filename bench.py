@@ -587,7 +587,7 @@ def cpu_baseline(cfg, budget_s):
 
     if cfg.name == "streaming":
         N, bounds, own_tables = cfg.hist, [cfg.chunk * i for i in range(cfg.steps + 1)], True
-        H = min(cfg.heads, 4)
+        H = min(cfg.heads, 16)
     elif cfg.name == "larger_backbone":
         N, bounds, own_tables = cfg.recent, [0, cfg.recent], False
         H = min(cfg.heads, 16)
