@@ -187,11 +187,6 @@ constexpr bool kSeqSchedule = LOWDIM && DQ == 32;
 template <int DQ, int KB, int VB, int G, bool LOWDIM, int DOUT, bool PSAC = false>
 __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void attend_kernel(AttendParams p, SegList segs) {
   constexpr bool SEQ = kSeqSchedule<DQ, LOWDIM>;
-  // Wavefronts whose 32 queries all lie past the last query (five of the eight
-  // in a block of 72) only dequantize their share of each tile, so the other
-  // wavefront on their SIMD runs alone.  Built where the register budget allows
-  // it without new spills in the tile loop: plain 2/4-bit full-dimensional keys.
-  constexpr bool kIdleWaves = !LOWDIM && !PSAC && KB != 16;
   static_assert(!PSAC || (!LOWDIM && !SEQ), "logit compensation: full-dimensional path only");
   constexpr int NK = SEQ ? 5 : 4;  // K tile buffers
   constexpr int KC = DQ / 16;     // k-chunks of the QK^T product
@@ -542,9 +537,8 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
     store_tile(2, 2);
   }
   __syncthreads();
-  const bool active = !kIdleWaves || int64_t(qb) * 256 + wave * 32 < p.n_q;   // wave-uniform
   if constexpr (!SEQ)
-    if (active && t_begin < t_end) qk(0, sa);
+    if (t_begin < t_end) qk(0, sa);
 
   int vbuf = 0;                     // V buffer of tile t; tile t+3 goes to (vbuf + 3) % 5
   int kbuf = 0;                     // K buffer of tile t; tile t+3 goes to (kbuf + 3) % NK
@@ -748,31 +742,15 @@ __global__ __launch_bounds__(512, (kSeqSchedule<DQ, LOWDIM> ? 4 : 1)) void atten
     vbuf = vbuf == 4 ? 0 : vbuf + 1;
     kbuf = kbuf == NK - 1 ? 0 : kbuf + 1;
   };
-  if (active) {
-    for (int t = t_begin; t < t_end; t += 2) {
-      if constexpr (SEQ) {
-        step(t, sa, sa);
-        if (t + 1 < t_end) step(t + 1, sa, sa);
-      } else {
-        step(t, sa, sb);
-        if (t + 1 < t_end) step(t + 1, sb, sa);
-      }
-      __syncthreads();
+  for (int t = t_begin; t < t_end; t += 2) {
+    if constexpr (SEQ) {
+      step(t, sa, sa);
+      if (t + 1 < t_end) step(t + 1, sa, sa);
+    } else {
+      step(t, sa, sb);
+      if (t + 1 < t_end) step(t + 1, sb, sa);
     }
-  } else if constexpr (kIdleWaves) {
-    // the same loads, the same tile t+3 into the same buffers at step t, and
-    // the same barriers (after every second step and after the last)
-    for (int t = t_begin; t < t_end; ++t) {
-      const int t3 = clamp_t(t + 3), t4 = clamp_t(t + 4);
-      data_seek(cur_data, t3);
-      load_data(cur_data, t3, kid_n, vid_n);
-      ids_seek(cur_ids, t4);
-      load_ids(cur_ids, t4, kid_n, vid_n);
-      store_tile(kbuf + 3 < NK ? kbuf + 3 : kbuf + 3 - NK, vbuf >= 2 ? vbuf - 2 : vbuf + 3);
-      vbuf = vbuf == 4 ? 0 : vbuf + 1;
-      kbuf = kbuf == NK - 1 ? 0 : kbuf + 1;
-      if (((t - t_begin) & 1) || t + 1 == t_end) __syncthreads();
-    }
+    __syncthreads();
   }
 
   // epilogue: normalise, write this split's (out, lse)
